@@ -1,0 +1,8 @@
+"""float64 CPU oracle for attention forward/backward.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the benchmark's CPU-baseline leg, never by the library.
+"""
+from .attention import (attention_backward, attention_forward,  # noqa: F401
+                        attention_forward_rows, attention_probs, loss)
+from .fdcheck import fd_full, fd_grad  # noqa: F401
