@@ -1,0 +1,174 @@
+"""MI355X (gfx950) fused attention forward/backward: Python binding.
+
+A thin ctypes layer over ``libattn_mi355x.so`` (the C ABI in
+``include/attn.h``).  The functions here have the C names and only marshal
+arguments: torch tensors supply device pointers and the current HIP stream;
+every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+__all__ = ["AttnError", "lib", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
+           "attn_bwd_workspace_size", "attn_status_string", "attn_version",
+           "ATTN_F32", "ATTN_BF16", "STATUS", "LIB_PATH", "HEADER_PATH"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "attn.h")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
+          3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, func: str, code: int):
+        self.code = code
+        super().__init__(f"{func} returned {STATUS.get(code, code)}")
+
+
+_lib = None
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "attn_fwd": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_bwd_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                      _I, _I, _I, _I, _I, _F, _P]),
+    "attn_bwd_dq": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                         _I, _I, _I, _I, _I, _F, _P]),
+    "attn_bwd_dkdv": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                           _I, _I, _I, _I, _I, _F, _P]),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_version": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m attention_forward_backward_amd.build` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list[str]:
+    """Function names declared in include/attn.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attn_\w+)\s*\(", text, re.M)))
+
+
+def attn_status_string(code: int) -> str:
+    return lib().attn_status_string(code).decode()
+
+
+def attn_version() -> str:
+    return lib().attn_version().decode()
+
+
+# ---------------------------------------------------------------- torch marshalling
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"attention tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check(tensors: dict, shape, dtype) -> None:
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _check_f32(tensors: dict, shape) -> None:
+    import torch
+    _check(tensors, shape, torch.float32)
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _raise(func: str, code: int) -> None:
+    if code != 0:
+        raise AttnError(func, code)
+
+
+def attn_bwd_workspace_size(dtype: int, batch: int, heads: int, seq: int, head_dim: int,
+                            causal: bool) -> int:
+    return int(lib().attn_bwd_workspace_size(dtype, batch, heads, seq, head_dim, int(causal)))
+
+
+def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """O, LSE <- attention(Q, K, V); tensors [B,H,S,D] (LSE [B,H,S] float32)."""
+    B, H, S, D = q.shape
+    _check({"q": q, "k": k, "v": v, "o": o}, (B, H, S, D), q.dtype)
+    _check_f32({"lse": lse}, (B, H, S))
+    code = lib().attn_fwd(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          o.data_ptr(), lse.data_ptr(), B, H, S, D, int(causal),
+                          float(scale), _stream(stream))
+    _raise("attn_fwd", code)
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
+             stream=None) -> None:
+    """dQ, dK, dV <- attention backward; workspace is a device tensor of at
+    least attn_bwd_workspace_size() bytes."""
+    B, H, S, D = q.shape
+    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout, "dq": dq, "dk": dk, "dv": dv},
+           (B, H, S, D), q.dtype)
+    _check_f32({"lse": lse}, (B, H, S))
+    code = lib().attn_bwd(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                          dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), B, H, S, D,
+                          int(causal), float(scale), _stream(stream))
+    _raise("attn_bwd", code)
+
+
+def attn_bwd_dq(q, k, v, o, dout, lse, dq, workspace, causal: bool, scale: float,
+                stream=None) -> None:
+    B, H, S, D = q.shape
+    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout, "dq": dq}, (B, H, S, D), q.dtype)
+    _check_f32({"lse": lse}, (B, H, S))
+    code = lib().attn_bwd_dq(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             B, H, S, D, int(causal), float(scale), _stream(stream))
+    _raise("attn_bwd_dq", code)
+
+
+def attn_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, causal: bool, scale: float,
+                  stream=None) -> None:
+    B, H, S, D = q.shape
+    _check({"q": q, "k": k, "v": v, "dout": dout, "dk": dk, "dv": dv}, (B, H, S, D), q.dtype)
+    _check_f32({"lse": lse}, (B, H, S))
+    code = lib().attn_bwd_dkdv(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               dout.data_ptr(), lse.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               B, H, S, D, int(causal), float(scale), _stream(stream))
+    _raise("attn_bwd_dkdv", code)

@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark: attention forward+backward throughput on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+attn_fwd (O, LSE) followed by attn_bwd (dQ, dK, dV), with every input already
+resident in device memory.  The workload is the decoder training-step
+attention, B=8 H=12 S=512 D=64 causal, scale 1/8, in both arithmetic
+contracts (strict f32 is the headline `value`; bf16 is reported alongside).
+
+Throughput counts credited FLOP = 14*D per visible (query, key) pair
+(forward 4*D: QK^T, PV; backward 10*D: QK^T, dO V^T, P^T dO, dS K, dS^T Q),
+with S(S+1)/2 visible pairs per head when causal.  Recomputation the kernels
+do on top of that is not credited.
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd+bwd TFLOP/s (f32 / bf16-MFMA) at B8 H12 S512 D64 causal, 1 GPU"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}  # MI355X dense MFMA: f32, bf16
+PEAK_HBM_GBS = 8000.0
+# MFMA FLOP per visible pair that each kernel executes (its own contractions)
+KERNEL_FLOP_PER_PAIR_D = {"attn_fwd": 4, "attn_bwd_dq": 6, "attn_bwd_dkdv": 8}
+KERNEL_SYMBOL = {"attn_fwd": "fwd_kernel", "attn_bwd_dq": "bwd_dq_kernel",
+                 "attn_bwd_dkdv": "bwd_dkdv_kernel"}
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="decoder_step")
+    p.add_argument("--dtypes", default="f32,bf16", help="first one is the headline value")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time for the oracle baseline sample")
+    p.add_argument("--only-step", action="store_true",
+                   help="time only the full step (used under a profiler)")
+    return p.parse_args()
+
+
+def kernel_sources_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "attention_forward_backward_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str, dtype: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    e = rec.get(f"{kernel}/{workload}/{dtype}")
+    if not e or e.get("sources") != src_hash:
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the attention "
+              "path here is single-GPU; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_forward_backward_amd as afb
+    from attention_forward_backward_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    afb.lib()  # fail loudly if the HIP library is missing
+
+    cfg = synth.CONFIGS[args.config]
+    B, H, S, D = cfg.shape
+    flops = cfg.flops
+    dtypes = [d.strip() for d in args.dtypes.split(",") if d.strip()]
+    stream = torch.cuda.current_stream()
+    src_hash = kernel_sources_hash()
+    workload = f"{cfg.name} B{B} H{H} S{S} D{D} {'causal' if cfg.causal else 'non-causal'}"
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    results = {}
+    for dt in dtypes:
+        log(f"[bench] {workload} dtype={dt}: generating inputs")
+        inp = synth.config_inputs(cfg, args.seed, dt)
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        code = afb.ATTN_BF16 if dt == "bf16" else afb.ATTN_F32
+
+        def dev(n):
+            if dt == "bf16":
+                return torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(inp[n]).cuda()
+
+        q, k, v, do = (dev(n) for n in ("q", "k", "v", "do"))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(afb.attn_bwd_workspace_size(code, B, H, S, D, cfg.causal),
+                         dtype=torch.uint8, device="cuda")
+        sc = cfg.scale
+
+        def fwd():
+            afb.attn_fwd(q, k, v, o, lse, cfg.causal, sc, stream)
+
+        def bwd_dq():
+            afb.attn_bwd_dq(q, k, v, o, do, lse, dq, ws, cfg.causal, sc, stream)
+
+        def bwd_dkdv():
+            afb.attn_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, cfg.causal, sc, stream)
+
+        def bwd():
+            afb.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, cfg.causal, sc, stream)
+
+        def step():
+            fwd()
+            bwd()
+
+        def timed(fn, steps, warmup):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(steps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / steps  # ms per call
+
+        log(f"[bench] {dt}: {args.warmup} warmup + {args.steps} timed steps (fwd+bwd)")
+        ms_step = timed(step, args.steps, args.warmup)
+        res = {"ms_per_step": ms_step,
+               "value": flops["fwd_bwd"] / (ms_step * 1e-3) / 1e12}
+        if not args.only_step:
+            ms = {"fwd": timed(fwd, args.steps, 3), "bwd": timed(bwd, args.steps, 3)}
+            kern = {"attn_fwd": ms["fwd"], "attn_bwd_dq": timed(bwd_dq, args.steps, 3),
+                    "attn_bwd_dkdv": timed(bwd_dkdv, args.steps, 3)}
+            res["phases"] = {
+                ph: {"ms": ms[ph], "tflops": flops[ph] / (ms[ph] * 1e-3) / 1e12}
+                for ph in ("fwd", "bwd")}
+            res["kernels"] = {}
+            for kname, kms in kern.items():
+                kf = KERNEL_FLOP_PER_PAIR_D[kname] * D * cfg.pairs
+                res["kernels"][kname] = {
+                    "symbol": KERNEL_SYMBOL[kname], "avg_us": kms * 1e3,
+                    "flop_per_launch": kf, "tflops": kf / (kms * 1e-3) / 1e12}
+            dom = max(kern, key=kern.get)
+            dk_ = res["kernels"][dom]
+            achieved = dk_["tflops"]
+            res["roofline"] = {
+                "kernel": dom, "bound": "mfma", "achieved": round(achieved, 3),
+                "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS[dt], 4),
+                "traffic": load_traffic(dom, cfg.name, dt, src_hash),
+                "flop_per_launch": dk_["flop_per_launch"],
+                "avg_launch_us": round(dk_["avg_us"], 3)}
+            res["step_frac_of_mfma_peak"] = round(res["value"] / PEAK_TFLOPS[dt], 4)
+        results[dt] = res
+        log(f"[bench] {dt}: {ms_step * 1e3:.1f} us/step, {res['value']:.2f} TFLOP/s")
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+
+    head = dtypes[0]
+    line = {
+        "metric": METRIC,
+        "value": round(results[head]["value"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(results[head]["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head,
+        "data": "synthetic (seeded SplitMix64 + Box-Muller normals, seed %d)" % args.seed,
+        "config": {"workload": workload, "batch": B, "heads": H, "seq_len": S,
+                   "head_dim": D, "causal": cfg.causal, "scale": cfg.scale,
+                   "credited_gflop_per_step": flops["fwd_bwd"] / 1e9,
+                   "flop_convention": "14*D per visible pair, causal pairs S(S+1)/2"},
+        "kernel_sources": src_hash,
+    }
+    for key in ("roofline", "phases", "kernels", "step_frac_of_mfma_peak"):
+        if key in results[head]:
+            line[key] = results[head][key]
+    for dt in dtypes[1:]:
+        line[dt] = {kk: (round(vv, 5) if isinstance(vv, float) else vv)
+                    for kk, vv in results[dt].items()}
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu_baseline: timing the float64 oracle on the host")
+        line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, seed: int, target_s: float) -> dict:
+    """The float64 oracle, as it stands, timed on this host's cores over whole
+    passes of the workload until about `target_s` seconds have passed."""
+    import oracle
+    from attention_forward_backward_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = None
+    inp = synth.config_inputs(cfg, seed, "f32")
+    q, k, v, do = (inp[n].astype(np.float64) for n in ("q", "k", "v", "do"))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.attention_forward(q, k, v, cfg.causal, cfg.scale)
+        oracle.attention_backward(q, k, v, do, cfg.causal, cfg.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or el / reps * (reps + 1) > 2.5 * target_s:
+            break
+    per = el / reps
+    return {"value": cfg.flops["fwd_bwd"] / per / 1e12, "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full pass(es) of the {cfg.name} workload (fwd+bwd, float64, "
+                      f"numpy), {per:.2f} s per pass, {os.cpu_count()} logical CPUs visible"}
+
+
+if __name__ == "__main__":
+    main()

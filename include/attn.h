@@ -1,0 +1,148 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) fused attention library.
+ *
+ * One operation: scaled-dot-product attention over [B, H, S, D] tensors,
+ *   S_ij  = scale * sum_d Q_id K_jd        (key j visible from query i;
+ *                                          causal: visible iff j <= i)
+ *   LSE_i = ln sum_{j visible} exp(S_ij)
+ *   O_i   = sum_j exp(S_ij - LSE_i) V_j
+ * forward (O and LSE saved) and backward (dQ, dK, dV for a loss whose
+ * gradient with respect to O is dO).  "Meganeura: Portable GPU Training and
+ * Inference through Vulkan and Metal" (arXiv 2608.01563) treats attention as
+ * one graph node with a local derivative rule (Section 3.1) and lowers it to
+ * tiled attention forward, dQ and fused dK+dV kernels (Section 3.3); this
+ * library provides those three kernels for one GPU.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers named q, k, v, o, dout, dq, dk, dv, lse, workspace are DEVICE
+ *    pointers owned by the caller.  The library never allocates, frees or
+ *    keeps a pointer after the call returns; it holds no state.
+ *  - Layout: [batch, heads, seq, head_dim] contiguous row-major for Q, K, V,
+ *    O, dO, dQ, dK, dV; LSE is [batch, heads, seq] float32.  Query and key
+ *    length are both `seq` (self-attention).
+ *  - Element type per `dtype` (attn_dtype_t): ATTN_F32 = IEEE float32 for
+ *    every tensor (strict f32: f32 MFMA operands, f32 accumulation); ATTN_BF16
+ *    = bfloat16 storage for Q, K, V, O, dO, dQ, dK, dV, with bf16 MFMA
+ *    operands (the softmax probabilities and dS rounded to nearest-even
+ *    bf16) and f32 accumulation, softmax statistics and LSE.  These are the
+ *    two arithmetic contracts of the pages' Section 4.2 (strict f32 versus a
+ *    reduced-input matrix path), here with bf16 in place of f16.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    and the call returns; outputs are valid once the caller synchronises
+ *    the stream.  Faults inside a kernel surface at that synchronisation.
+ *  - Outputs are overwritten (=, never +=), must not alias inputs or each
+ *    other, and inputs are never written.
+ *  - Validation happens before anything is enqueued: on any error nothing
+ *    is launched and the error code is returned.
+ *      ATTN_ERR_INVALID_ARG  null pointer, batch/heads/seq <= 0, causal not
+ *                            0 or 1, scale not finite, a pointer not 16-byte
+ *                            aligned, or sizes whose element count overflows
+ *                            a 32-bit signed index
+ *      ATTN_ERR_UNSUPPORTED  head_dim not in {32, 64, 128}, or unknown dtype
+ *      ATTN_ERR_WORKSPACE    workspace smaller than attn_bwd_workspace_size()
+ *      ATTN_ERR_HIP          the HIP runtime reported a launch error
+ */
+#ifndef ATTN_MI355X_ATTN_H
+#define ATTN_MI355X_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,
+  ATTN_ERR_UNSUPPORTED = 2,
+  ATTN_ERR_WORKSPACE = 3,
+  ATTN_ERR_HIP = 4
+} attn_status_t;
+
+typedef enum {
+  ATTN_F32 = 0,  /* strict float32 contract */
+  ATTN_BF16 = 1  /* bf16 storage and MFMA operands, f32 accumulation */
+} attn_dtype_t;
+
+/*
+ * Forward pass (tiled attention forward; pages' Section 3.3).
+ *   in : q, k, v   [B,H,S,D] dtype
+ *   out: o         [B,H,S,D] dtype   softmax(scale * Q K^T, masked) V
+ *        lse       [B,H,S]   float32 natural-log row normaliser, scale
+ *                                    included; the backward reads it
+ * One kernel launch.
+ */
+attn_status_t attn_fwd(attn_dtype_t dtype,
+                       const void* q, const void* k, const void* v,
+                       void* o, float* lse,
+                       int batch, int heads, int seq, int head_dim,
+                       int causal, float scale, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs: the row vector
+ * D_i = sum_d dO_id O_id, [B,H,S] float32, rounded up to 256 bytes.
+ * Returns 0 for arguments attn_bwd would reject.  Pure host function.
+ */
+size_t attn_bwd_workspace_size(attn_dtype_t dtype, int batch, int heads,
+                               int seq, int head_dim, int causal);
+
+/*
+ * Backward pass: attn_bwd_dq followed by attn_bwd_dkdv on `stream`
+ * (the pages' dQ kernel and fused dK+dV kernel, Section 3.3 and the
+ * attention-backward profile of Section 7.3).
+ *   in : q, k, v, o, dout  [B,H,S,D] dtype  (o = the forward's output)
+ *        lse               [B,H,S]   float32 (the forward's LSE)
+ *   out: dq, dk, dv        [B,H,S,D] dtype  gradients of the loss
+ *   workspace              >= attn_bwd_workspace_size() bytes of device
+ *                          memory, 16-byte aligned; contents on entry are
+ *                          ignored, contents on return are D.
+ * Deterministic: no atomics; every output element is written by exactly one
+ * thread, so repeated calls give bitwise identical results.
+ */
+attn_status_t attn_bwd(attn_dtype_t dtype,
+                       const void* q, const void* k, const void* v,
+                       const void* o, const void* dout, const float* lse,
+                       void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes,
+                       int batch, int heads, int seq, int head_dim,
+                       int causal, float scale, void* stream);
+
+/*
+ * First backward stage alone (the pages' dQ kernel): for each query row,
+ * D_i = sum_d dO_id O_id (written to workspace, [B,H,S] float32) and
+ * dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j with P recomputed from LSE.
+ * Same arguments and rules as attn_bwd minus dk/dv.
+ */
+attn_status_t attn_bwd_dq(attn_dtype_t dtype,
+                          const void* q, const void* k, const void* v,
+                          const void* o, const void* dout, const float* lse,
+                          void* dq, void* workspace, size_t workspace_bytes,
+                          int batch, int heads, int seq, int head_dim,
+                          int causal, float scale, void* stream);
+
+/*
+ * Second backward stage alone (the pages' fused dK+dV kernel): per key row,
+ * dV_j = sum_i P_ij dO_i and dK_j = scale * sum_i P_ij (dP_ij - D_i) Q_i.
+ * Reads D from `workspace`, so attn_bwd_dq must have run on the same
+ * inputs first (stream order).  Same arguments and rules as attn_bwd
+ * minus o and dq.
+ */
+attn_status_t attn_bwd_dkdv(attn_dtype_t dtype,
+                            const void* q, const void* k, const void* v,
+                            const void* dout, const float* lse,
+                            void* dk, void* dv,
+                            const void* workspace, size_t workspace_bytes,
+                            int batch, int heads, int seq, int head_dim,
+                            int causal, float scale, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* attn_status_string(attn_status_t status);
+
+/* Library version string ("<major>.<minor>.<patch>"). */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_ATTN_H */

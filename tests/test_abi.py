@@ -1,0 +1,88 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every
+function include/attn.h declares, and rejects bad arguments before anything
+is launched (every call here fails validation, so no kernel ever runs)."""
+import ctypes
+import math
+
+import pytest
+
+import attention_forward_backward_amd as afb
+
+FAKE = 0x10000          # aligned, non-null; never dereferenced (validation fails first)
+MIS = 0x10008           # 8-byte aligned only
+
+
+def test_library_loads_and_exports_header_symbols():
+    L = afb.lib()
+    declared = afb.declared_symbols()
+    assert set(declared) == {"attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
+                             "attn_bwd_workspace_size", "attn_status_string", "attn_version"}
+    for name in declared:
+        assert hasattr(L, name), name
+    assert afb.attn_version() == "0.1.0"
+    for code in range(5):
+        assert afb.attn_status_string(code) not in ("", "unknown status")
+    assert afb.attn_status_string(99) == "unknown status"
+
+
+def _fwd(dtype=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, S=8, D=64, causal=1,
+         scale=0.125):
+    return afb.lib().attn_fwd(dtype, q, k, v, o, lse, B, H, S, D, causal, scale, None)
+
+
+def _bwd(dtype=0, ptr=FAKE, ws=FAKE, wsb=1 << 20, B=1, H=1, S=8, D=64, causal=1, scale=0.125,
+         misalign=None):
+    p = [ptr] * 9
+    if misalign is not None:
+        p[misalign] = MIS
+    return afb.lib().attn_bwd(dtype, *p, ws, wsb, B, H, S, D, causal, scale, None)
+
+
+def test_fwd_validation():
+    assert _fwd(q=None) == 1
+    assert _fwd(lse=None) == 1
+    assert _fwd(v=MIS) == 1
+    assert _fwd(B=0) == 1 and _fwd(H=-1) == 1 and _fwd(S=0) == 1
+    assert _fwd(causal=2) == 1
+    assert _fwd(scale=math.inf) == 1 and _fwd(scale=math.nan) == 1
+    assert _fwd(D=48) == 2 and _fwd(D=256) == 2 and _fwd(D=16) == 2
+    assert _fwd(dtype=7) == 2
+    assert _fwd(B=1 << 16, H=1 << 16) == 1          # B*H beyond int
+    assert _fwd(S=1 << 26, D=64) == 1               # S*D beyond int
+
+
+def test_bwd_validation():
+    for i in range(9):
+        assert _bwd(misalign=i) == 1, i
+    assert _bwd(ptr=None) == 1
+    assert _bwd(ws=None) == 1
+    assert _bwd(D=96) == 2
+    assert _bwd(dtype=3) == 2
+    assert _bwd(wsb=8 * 4 - 1) == 3
+    L = afb.lib()
+    # split stages validate the same way
+    assert L.attn_bwd_dq(0, *[FAKE] * 7, FAKE, 16, 1, 1, 8, 64, 1, 0.1, None) == 3
+    assert L.attn_bwd_dkdv(0, *[FAKE] * 7, FAKE, 16, 1, 1, 8, 64, 1, 0.1, None) == 3
+    assert L.attn_bwd_dq(0, *[FAKE] * 7, None, 1 << 20, 1, 1, 8, 64, 1, 0.1, None) == 1
+    assert L.attn_bwd_dkdv(0, *[FAKE] * 6, None, FAKE, 1 << 20, 1, 1, 8, 64, 1, 0.1, None) == 1
+
+
+def test_workspace_size():
+    ws = afb.attn_bwd_workspace_size
+    assert ws(0, 8, 12, 512, 64, True) == 8 * 12 * 512 * 4
+    assert ws(1, 1, 1, 1, 64, False) == 256
+    assert ws(0, 32, 8, 197, 64, False) == ((32 * 8 * 197 * 4 + 255) // 256) * 256
+    assert ws(0, 1, 1, 8, 48, True) == 0 and ws(0, 0, 1, 8, 64, True) == 0
+    assert ws(5, 1, 1, 8, 64, True) == 0
+    prev = 0
+    for s in (1, 17, 64, 197, 512, 1024):
+        cur = ws(0, 2, 3, s, 64, True)
+        assert cur >= prev and cur >= 2 * 3 * s * 4 and cur % 256 == 0
+        prev = cur
+
+
+def test_no_cpu_fallback_when_library_missing(monkeypatch, tmp_path):
+    monkeypatch.setattr(afb, "_lib", None)
+    monkeypatch.setattr(afb, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        afb.lib()

@@ -1,0 +1,139 @@
+"""GPU parity: the HIP path against the float64 oracle, element by element, on
+the same seeded inputs.  Gate per output tensor X in {O, LSE, dQ, dK, dV}:
+max|X_gpu - X_ref| / max|X_ref| <= 1e-4 (strict f32) or 2e-2 (bf16).  The
+backward is fed the GPU forward's own O and LSE (the pipeline is gated)."""
+import numpy as np
+import pytest
+
+from attention_forward_backward_amd import synth
+from parity_util import TOL, compare, gpu_fwd_bwd, max_rel_err, note, run_case
+
+pytestmark = pytest.mark.gpu
+
+CFG_CASES = [(name, dt, seed) for name, cfg in synth.CONFIGS.items()
+             for dt in (("f32", "bf16") if name != "tiny" else ("f32", "bf16"))
+             for seed in (0, 1, 2)]
+
+
+@pytest.mark.parametrize("name,dtype,seed", CFG_CASES)
+def test_config_parity(name, dtype, seed):
+    """The five measured workloads at full size, three seeds, both contracts."""
+    cfg = synth.CONFIGS[name]
+    errs, host, ref, *_ = run_case(cfg.shape, seed, dtype, cfg.causal, cfg.scale,
+                                   cfg.sigma_qkv, cfg.sigma_do)
+    note(f"  errors {name} {dtype} seed {seed}: " +
+         ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL[dtype], (k, v)
+    # D written to the workspace by the dQ kernel
+    assert max_rel_err(host["delta"], ref["delta"]) <= TOL[dtype]
+
+
+MICRO = [(S, D, causal) for S in (1, 17, 33, 67, 130, 197) for D in (32, 64, 128)
+         for causal in (True, False)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("S,D,causal", MICRO)
+def test_ragged_micro_shapes(S, D, causal, dtype):
+    """Sequence lengths that end mid-tile, every head_dim, guard bands after
+    every output, NaN-prefilled outputs."""
+    shape = (2, 3, S, D)
+    scale = 1.0 / np.sqrt(D)
+    errs, host, ref, inp, *_ = run_case(shape, 7, dtype, causal, scale, guard=64)
+    if S == 1:
+        # One key: P = 1, so O = V and dV = dO, while dQ and dK are exactly 0
+        # (dS = P (dP - D) with dP = D); the oracle's float64 dQ, dK are
+        # rounding noise there, so the relative metric does not apply.
+        # Bound |dQ|, |dK| by the rounding of dP - D instead.
+        q, k, v, do = (inp[n].astype(np.float64) for n in ("q", "k", "v", "do"))
+        bound = TOL[dtype] * scale * D * np.abs(do).max() * np.abs(v).max() \
+            * max(np.abs(k).max(), np.abs(q).max())
+        assert np.abs(host["dq"]).max() <= bound and np.abs(host["dk"]).max() <= bound
+        errs = {n: errs[n] for n in ("o", "lse", "dv")}
+    for k_, v_ in errs.items():
+        assert v_ <= TOL[dtype], (k_, v_)
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        assert host[name + "_guard_ok"], name
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_deterministic_and_inputs_untouched(dtype):
+    import torch
+    shape = (2, 4, 197, 64)
+    inp = synth.make_inputs(shape, 3, dtype)
+    note(f"[gpu case] determinism shape={shape} dtype={dtype}")
+    h1, dev, _ = gpu_fwd_bwd(inp, shape, dtype, True, 0.125)
+    before = {k: v.clone() for k, v in dev.items()}
+    h2, dev2, _ = gpu_fwd_bwd(inp, shape, dtype, True, 0.125)
+    for n in ("o", "lse", "dq", "dk", "dv", "delta"):
+        assert np.array_equal(h1[n], h2[n]), n
+    for n, t in dev.items():
+        assert torch.equal(t, before[n]), n
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_gradient_invariants_on_gpu(dtype, causal):
+    """sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i hold for any inputs."""
+    shape = (2, 2, 256, 64)
+    inp = synth.make_inputs(shape, 5, dtype)
+    note(f"[gpu case] invariants shape={shape} dtype={dtype} causal={causal}")
+    h, *_ = gpu_fwd_bwd(inp, shape, dtype, causal, 0.125)
+    dk_sum = h["dk"].astype(np.float64).sum(axis=2)
+    scale_k = np.abs(h["dk"]).max() * np.sqrt(256)
+    assert np.abs(dk_sum).max() <= 10 * TOL[dtype] * scale_k
+    dv_sum = h["dv"].astype(np.float64).sum(axis=2)
+    do_sum = inp["do"].astype(np.float64).sum(axis=2)
+    assert max_rel_err(dv_sum, do_sum) <= 10 * TOL[dtype]
+
+
+def test_backward_alone_on_oracle_forward():
+    """Diagnostic split: the backward fed the oracle's O and LSE (rounded to
+    the storage type) must meet the gate on its own."""
+    import torch
+    import attention_forward_backward_amd as afb
+    from parity_util import oracle_all, to_host
+    for dtype in ("f32", "bf16"):
+        cfg = synth.CONFIGS["decoder_step"]
+        shape = (2, 12, 512, 64)
+        inp = synth.make_inputs(shape, 0, dtype)
+        ref = oracle_all(inp, True, cfg.scale)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        note(f"[gpu case] backward-only shape={shape} dtype={dtype}")
+        dev = {}
+        for n in ("q", "k", "v", "do"):
+            if dtype == "bf16":
+                dev[n] = torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+            else:
+                dev[n] = torch.from_numpy(inp[n]).cuda()
+        o = torch.from_numpy(ref["o"]).to(tdt).cuda()
+        lse = torch.from_numpy(ref["lse"]).float().cuda()
+        outs = [torch.full(shape, float("nan"), dtype=tdt, device="cuda") for _ in range(3)]
+        ws = torch.empty(afb.attn_bwd_workspace_size(int(dtype == "bf16"), *shape, True),
+                         dtype=torch.uint8, device="cuda")
+        afb.attn_bwd(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, *outs, ws, True, cfg.scale)
+        torch.cuda.synchronize()
+        for t, n in zip(outs, ("dq", "dk", "dv")):
+            assert max_rel_err(to_host(t), ref[n]) <= TOL[dtype], (dtype, n)
+
+
+def test_split_stages_match_fused_call():
+    """attn_bwd_dq then attn_bwd_dkdv gives bitwise the same as attn_bwd."""
+    import torch
+    import attention_forward_backward_amd as afb
+    shape = (1, 4, 130, 64)
+    inp = synth.make_inputs(shape, 2, "f32")
+    note(f"[gpu case] split stages shape={shape}")
+    h, dev, outs = gpu_fwd_bwd(inp, shape, "f32", True, 0.125)
+    dq = torch.empty_like(outs["dq"])
+    dk = torch.empty_like(outs["dk"])
+    dv = torch.empty_like(outs["dv"])
+    ws = torch.empty(afb.attn_bwd_workspace_size(0, *shape, True), dtype=torch.uint8,
+                     device="cuda")
+    afb.attn_bwd_dq(dev["q"], dev["k"], dev["v"], outs["o"], dev["do"], outs["lse"], dq, ws,
+                    True, 0.125)
+    afb.attn_bwd_dkdv(dev["q"], dev["k"], dev["v"], dev["do"], outs["lse"], dk, dv, ws,
+                      True, 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, outs["dq"]) and torch.equal(dk, outs["dk"]) and torch.equal(dv, outs["dv"])
