@@ -51,7 +51,20 @@ def parse():
                    help="target CPU time for the oracle baseline sample")
     p.add_argument("--only-step", action="store_true",
                    help="time only the full step (used under a profiler)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="instead of the benchmark, run 5 plain device-to-device copies of "
+                        "BYTES bytes (the reference kernel for scaling HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(nbytes: int) -> None:
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": x.numel() * 4, "launches": 5}), flush=True)
 
 
 def kernel_sources_hash() -> str:
@@ -88,6 +101,9 @@ def main():
     import attention_forward_backward_amd as afb
     from attention_forward_backward_amd import synth
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
