@@ -22,9 +22,12 @@ LIB = os.path.join(PKG, "libattn_mi355x.so")
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming packed f32 VALU ops.
+# -amdgpu-mfma-vgpr-form: MFMA results in ordinary VGPRs, so the softmax VALU
+# reads them without accumulator-register copies.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

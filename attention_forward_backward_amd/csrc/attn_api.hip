@@ -18,7 +18,7 @@ attn_status_t check_shape(attn_dtype_t dtype, int batch, int heads, int seq, int
   if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (batch <= 0 || heads <= 0 || seq <= 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
-  if (check_scale && !isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (check_scale && !(isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
   // Element counts must fit the kernels' index arithmetic: B*H within the
   // grid's x dimension, S*D within int, and the whole tensor within int64.

@@ -111,17 +111,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
       const int arow = (qb * 32 + pi32(n)) * STR + h * (D / 2);
       f32x16 s = dot_rows<E, D>(Qs + arow, kf, zero16());
       f32x16 dp = dot_rows<E, D>(dOs + arow, vf, zero16());
-      // LSE and D of this lane's 16 queries: two runs of 8 at rho(0, h), rho(8, h).
-      const float* lrow = lse2s + qb * 32;
-      const float* drow = Ds + qb * 32;
+      if (CAUSAL && qq0 < k0 + 31) {
+        // query(r) = qq0 + 8h + (16*(r/8) + r%8) sees key kj iff query >= kj
+        const int lim = kj - qq0 - 8 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (16 * (r >> 3) + (r & 7) < lim) s[r] = -INFINITY;
+      }
+      // LSE*log2(e) and D of this lane's 16 queries: two runs of 8 at rho(0, h)
+      // and rho(8, h).  Queries past S carry LSE = +inf, so their P is 0.
+      float lq[16], dq_[16];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int v4 = 0; v4 < 2; ++v4) {
+          const int off = qb * 32 + 16 * u + 8 * h + 4 * v4;
+          const f32x4 a = *reinterpret_cast<const f32x4*>(lse2s + off);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(Ds + off);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lq[8 * u + 4 * v4 + e] = a[e];
+            dq_[8 * u + 4 * v4 + e] = b[e];
+          }
+        }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ql = rho(r, h);
-        const int qi = qq0 + ql;
-        const bool vis = !CAUSAL || qi >= kj;
-        const float p = vis ? fast_exp2(s[r] * c - lrow[ql]) : 0.f;
+        const float p = fast_exp2(fmaf(s[r], c, -lq[r]));
         s[r] = p;
-        dp[r] = p * (dp[r] - drow[ql]);
+        dp[r] = p * (dp[r] - dq_[r]);
       }
       RegOperand<E> P, dS;
       P.set(s);

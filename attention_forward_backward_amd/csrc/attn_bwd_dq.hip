@@ -109,12 +109,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
       const int arow = (kb * 32 + pi32(n)) * STR + h * (D / 2);
       f32x16 st = dot_rows<E, D>(Ks + arow, qf, zero16());
       f32x16 dpt = dot_rows<E, D>(Vs + arow, dof, zero16());
+      if (kk0 + 32 > S || (CAUSAL && kk0 + 31 > q0)) {
+        // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < S and key <= qi
+        const int lim = min(S - 1, CAUSAL ? qi : S - 1) - kk0 - 8 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (16 * (r >> 3) + (r & 7) > lim) st[r] = -INFINITY;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = kk0 + rho(r, h);
-        const bool vis = key < S && (!CAUSAL || key <= qi);
-        const float p = vis ? fast_exp2(st[r] * c - lse2) : 0.f;
-        st[r] = p * (dpt[r] - di);  // dS^T
+        const float p = fast_exp2(fmaf(st[r], c, -lse2));  // 0 where masked
+        st[r] = p * (dpt[r] - di);                            // dS^T
       }
       RegOperand<E> dS;
       dS.set(st);

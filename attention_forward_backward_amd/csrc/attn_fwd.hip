@@ -81,44 +81,59 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     }
     if (!wave_active) continue;
 
+    // Scores of the tile's 32-key blocks.  A block is skipped when no key in
+    // it is visible from any of the wave's queries, and masked only when
+    // some but not all of it is (the causal diagonal, the ragged end).
     f32x16 sacc[NKB];
-    bool blk[NKB];
-    float mx = -INFINITY;
+    bool blk[NKB], part[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       const int kk0 = kt * BK + kb * 32;
       blk[kb] = kk0 < S && (!CAUSAL || kk0 <= q0 + 31);
-      if (blk[kb]) {
-        sacc[kb] = dot_rows<E, D>(Ks + (kb * 32 + pi32(n)) * STR + h * (D / 2), qf, zero16());
+      part[kb] = kk0 + 32 > S || (CAUSAL && kk0 + 31 > q0);
+      if (blk[kb]) sacc[kb] = dot_rows<E, D>(Ks + (kb * 32 + pi32(n)) * STR + h * (D / 2), qf, zero16());
+    }
+    float mx = -INFINITY;  // max of the raw (unscaled) visible scores
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kk0 + rho(r, h);
-          const bool vis = key < S && (!CAUSAL || key <= qi);
-          const float x = vis ? sacc[kb][r] * c : -INFINITY;
-          sacc[kb][r] = x;
-          mx = fmaxf(mx, x);
-        }
+    for (int kb = 0; kb < NKB; ++kb) {
+      if (!blk[kb]) continue;
+      if (part[kb]) {
+        const int kk0 = kt * BK + kb * 32;
+        // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < S and key <= qi
+        const int lim = min(S - 1, CAUSAL ? qi : S - 1) - kk0 - 8 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (16 * (r >> 3) + (r & 7) > lim) sacc[kb][r] = -INFINITY;
       }
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
     }
     mx = fmaxf(mx, xhalf(mx));
-    const float mnew = fmaxf(m, mx);  // finite: key 0 is visible from every query
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
+    // Lazy rescaling: exponents are taken against a reference m that may lag
+    // the running max by up to 2^8, so O and l are rescaled only when some
+    // row's max grows past that (and never on the first tile, where they are 0).
+    const float mc = mx * c;
+    if (__any(mc > m + 8.f)) {
+      const float mnew = fmaxf(m, mc);
+      const float alpha = fast_exp2(m - mnew);  // 0 on the first tile (m = -inf)
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    }
     float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       if (blk[kb]) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(sacc[kb][r] - mnew);
+          const float p = fast_exp2(fmaf(sacc[kb][r], c, -m));
           sacc[kb][r] = p;
           rs += p;
         }
       }
     }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    l += rs;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       if (blk[kb]) {

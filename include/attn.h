@@ -35,9 +35,10 @@
  *  - Validation happens before anything is enqueued: on any error nothing
  *    is launched and the error code is returned.
  *      ATTN_ERR_INVALID_ARG  null pointer, batch/heads/seq <= 0, causal not
- *                            0 or 1, scale not finite, a pointer not 16-byte
- *                            aligned, or sizes whose element count overflows
- *                            a 32-bit signed index
+ *                            0 or 1, scale not a finite positive number (the
+ *                            kernels take row maxima of unscaled scores), a
+ *                            pointer not 16-byte aligned, or sizes whose
+ *                            element count overflows a 32-bit signed index
  *      ATTN_ERR_UNSUPPORTED  head_dim not in {32, 64, 128}, or unknown dtype
  *      ATTN_ERR_WORKSPACE    workspace smaller than attn_bwd_workspace_size()
  *      ATTN_ERR_HIP          the HIP runtime reported a launch error

@@ -45,6 +45,7 @@ def test_fwd_validation():
     assert _fwd(B=0) == 1 and _fwd(H=-1) == 1 and _fwd(S=0) == 1
     assert _fwd(causal=2) == 1
     assert _fwd(scale=math.inf) == 1 and _fwd(scale=math.nan) == 1
+    assert _fwd(scale=0.0) == 1 and _fwd(scale=-0.125) == 1
     assert _fwd(D=48) == 2 and _fwd(D=256) == 2 and _fwd(D=16) == 2
     assert _fwd(dtype=7) == 2
     assert _fwd(B=1 << 16, H=1 << 16) == 1          # B*H beyond int
