@@ -37,7 +37,8 @@ attn_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
 }
 
 size_t delta_bytes(int batch, int heads, int seq) {
-  const size_t b = (size_t)batch * heads * seq * sizeof(float);
+  // D, then LSE * log2(e), one float each per query row
+  const size_t b = 2 * (size_t)batch * heads * seq * sizeof(float);
   return (b + 255) & ~(size_t)255;
 }
 

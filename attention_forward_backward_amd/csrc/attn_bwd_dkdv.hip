@@ -7,56 +7,55 @@
 //   P_ij  = exp(scale * Q_i.K_j - LSE_i)
 //   dV_j  = sum_i P_ij dO_i
 //   dK_j  = scale * sum_i P_ij (dO_i.V_j - D_i) Q_i
-// with D_i from the workspace (written by the dQ kernel).
+// with D_i and LSE_i*log2(e) read from the workspace the dQ kernel wrote.
 //
-// Work split: one workgroup per (key tile of 32*NW rows, batch*head), one
-// wave per 32 keys whose K and V rows stay in registers, and dK, dV
-// accumulated in registers over all query tiles (BQ queries each, staged in
-// LDS with their LSE and D and shared by the waves).  Per 32-query block a
-// wave forms S = Q K^T and dP = dO V^T (queries x keys; each lane holds one
-// key), then P^T and dS^T are the register A operands of
+// Work split: one workgroup per (key tile of 32*RB rows, batch*head).  Each
+// 32-key block is owned by NSPLIT waves that keep its K and V rows in
+// registers, split the query blocks between them, accumulate dK and dV in
+// registers and sum their partials through LDS at the end.  Query tiles (Q,
+// dO, and the queries' LSE and D) stream through an NST-stage ring of LDS
+// tiles filled by direct global->LDS loads issued NST-1 tiles ahead.  Per
+// 32-query block a wave forms S = Q K^T and dP = dO V^T (queries x keys; each
+// lane holds one key), then P^T and dS^T are the register A operands of
 // dV (keys x d) += P^T dO and dK += dS^T Q, with dO and Q read back from LDS.
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
 
 namespace attn {
 
-template <class E, int D, int NW, int BQ, bool CAUSAL>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Dws,
-    typename E::T* __restrict__ dK, typename E::T* __restrict__ dV, int S, float c,
-    float scale) {
+    const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
+    int S, int L, float c, float scale) {
   using T = typename E::T;
-  constexpr int NT = NW * 64;
-  constexpr int BKV = NW * 32;
+  using TL = Tile<E, D>;
+  constexpr int RB = NW / NSPLIT;        // 32-key blocks per workgroup
+  constexpr int BKV = 32 * RB;           // keys per workgroup
+  constexpr int BQ = 32 * NSPLIT * KPW;  // queries per staged tile
   constexpr int NDB = D / 32;
-  constexpr int NQB = BQ / 32;
-  constexpr int STR = row_stride<E, D>();
-  constexpr int STRT = tr_stride<BQ>();
-  constexpr int T_ELEMS = BQ * STR;
-  constexpr int TT_ELEMS = is_bf16<E>() ? D * STRT : 0;
-  __shared__ __attribute__((aligned(16))) T smem[2 * T_ELEMS + 2 * TT_ELEMS];
-  __shared__ __attribute__((aligned(16))) float stat[2 * BQ];
-  T* Qs = smem;                                // [query][d]
-  T* dOs = smem + T_ELEMS;                     // [query][d]
-  T* QsT = smem + 2 * T_ELEMS;                 // bf16 only: [d][query]
-  T* dOsT = smem + 2 * T_ELEMS + TT_ELEMS;     // bf16 only: [d][query]
-  float* lse2s = stat;                         // LSE * log2(e); +inf past S
-  float* Ds = stat + BQ;                       // D; 0 past S
+  using LD = StageLoader<E, D, BQ, NW>;
+  constexpr int TILEB = BQ * TL::ROWB;                            // dO follows Q in a stage
+  constexpr int STAGE = (LD::BYTES + 2 * BQ * 4 + 1023) / 1024 * 1024;  // + LSE*log2e, D
+  constexpr int NL = LD::NLOADS + 1;                              // loads per wave per tile
+  constexpr int COMB = RB * (NSPLIT - 1) * 32 * NDB * 64 * 4;
+  constexpr int SMEM = NST * STAGE > COMB ? NST * STAGE : COMB;
+  static_assert(NW % NSPLIT == 0 && NST >= 2 && NST <= 4, "launch shape");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int kbk = w / NSPLIT, sp = w % NSPLIT;
   const int bh = blockIdx.x;
   const int kt = blockIdx.y;  // causal: tile 0 has the most queries, dispatched first
   const size_t base = (size_t)bh * S * D;
   const T* q = Q + base;
   const T* dout = dO + base;
-  const float* lse = LSE + (size_t)bh * S;
-  const float* dws = Dws + (size_t)bh * S;
+  const float* dlt = Dws + (size_t)bh * S;
+  const float* lse2g = Dws + (size_t)L + (size_t)bh * S;
 
-  const int k0 = kt * BKV + w * 32;
+  const int k0 = kt * BKV + kbk * 32;
   const int kj = k0 + n;
   const bool wave_active = k0 < S;
   const size_t krow = base + (size_t)min(kj, S - 1) * D + h * (D / 2);
@@ -74,58 +73,51 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
 
   const int nqt = (S + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
-
-  TileRegs<T, BQ, D, NT> qr, dor;
-  float st_lse = 0.f, st_d = 0.f;
-  auto load_tile = [&](int qt) {
-    qr.load(q, qt * BQ, S, tid);
-    dor.load(dout, qt * BQ, S, tid);
-    if (tid < BQ) {
-      const int qi = qt * BQ + tid;
-      st_lse = qi < S ? lse[qi] * kLog2e : INFINITY;
-      st_d = qi < S ? dws[qi] : 0.f;
-    }
+  auto issue = [&](int qt) {
+    char* st = smem + ((qt - qt0) % NST) * STAGE;
+    LD::issue(st, q, dout, qt * BQ, S, w, lane);
+    issue_stats<BQ, NW>(reinterpret_cast<float*>(st + LD::BYTES), lse2g, dlt, qt * BQ, S, w, lane);
   };
-  if (qt0 < nqt) load_tile(qt0);
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (qt0 + s < nqt) issue(qt0 + s);
 
   for (int qt = qt0; qt < nqt; ++qt) {
-    __syncthreads();
-    qr.template store<STR>(Qs, tid);
-    dor.template store<STR>(dOs, tid);
-    if constexpr (is_bf16<E>()) {
-      qr.template store_t<STRT>(QsT, tid);
-      dor.template store_t<STRT>(dOsT, tid);
-    }
-    if (tid < BQ) {
-      lse2s[tid] = st_lse;
-      Ds[tid] = st_d;
-    }
-    __syncthreads();
-    if (qt + 1 < nqt) load_tile(qt + 1);
+    wait_tiles<NL>(min(NST - 2, nqt - 1 - qt));
+    lds_barrier();  // tile qt is in LDS; every wave is done with tile qt-1
+    if (qt + NST - 1 < nqt) issue(qt + NST - 1);
     if (!wave_active) continue;
+    const char* Qt = smem + ((qt - qt0) % NST) * STAGE;
+    const char* dOt = Qt + TILEB;
+    const float* lse2s = reinterpret_cast<const float*>(Qt + LD::BYTES);
+    const float* Ds = lse2s + BQ;
 
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int qq0 = qt * BQ + qb * 32;
+    for (int j = 0; j < KPW; ++j) {
+      const int qbl = sp + NSPLIT * j;  // query block within the tile
+      const int qq0 = qt * BQ + qbl * 32;
       if (!(qq0 < S && (!CAUSAL || qq0 + 31 >= k0))) continue;  // wave-uniform
-      const int arow = (qb * 32 + pi32(n)) * STR + h * (D / 2);
-      f32x16 s = dot_rows<E, D>(Qs + arow, kf, zero16());
-      f32x16 dp = dot_rows<E, D>(dOs + arow, vf, zero16());
-      if (CAUSAL && qq0 < k0 + 31) {
-        // query(r) = qq0 + 8h + (16*(r/8) + r%8) sees key kj iff query >= kj
-        const int lim = kj - qq0 - 8 * h;
+      const int arow = qbl * 32 + pi32(n);
+      f32x16 s = dot_tile<E, D>(Qt, arow, h, kf, zero16());
+      f32x16 dp = dot_tile<E, D>(dOt, arow, h, vf, zero16());
+      if ((CAUSAL && qq0 < k0 + 31) || qq0 + 32 > S) {
+        // query(r) = qq0 + 8h + (16*(r/8) + r%8) sees key kj iff kj <= query < S
+        const int lo = CAUSAL ? kj - qq0 - 8 * h : -64;
+        const int hi = S - 1 - qq0 - 8 * h;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (16 * (r >> 3) + (r & 7) < lim) s[r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int o = 16 * (r >> 3) + (r & 7);
+          if (o < lo || o > hi) s[r] = -INFINITY;
+        }
       }
       // LSE*log2(e) and D of this lane's 16 queries: two runs of 8 at rho(0, h)
-      // and rho(8, h).  Queries past S carry LSE = +inf, so their P is 0.
+      // and rho(8, h).
       float lq[16], dq_[16];
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int v4 = 0; v4 < 2; ++v4) {
-          const int off = qb * 32 + 16 * u + 8 * h + 4 * v4;
+          const int off = qbl * 32 + 16 * u + 8 * h + 4 * v4;
           const f32x4 a = *reinterpret_cast<const f32x4*>(lse2s + off);
           const f32x4 b = *reinterpret_cast<const f32x4*>(Ds + off);
 #pragma unroll
@@ -136,7 +128,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[r], c, -lq[r]));
+        const float p = fast_exp2(fmaf(s[r], c, -lq[r]));  // 0 where masked
         s[r] = p;
         dp[r] = p * (dp[r] - dq_[r]);
       }
@@ -145,12 +137,42 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
       dS.set(dp);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        dvacc[db] = second_product<E, STR, STRT, true>(P, dOs, dOsT, qb * 32, db * 32 + n, h, dvacc[db]);
-        dkacc[db] = second_product<E, STR, STRT, true>(dS, Qs, QsT, qb * 32, db * 32 + n, h, dkacc[db]);
+        dvacc[db] = second_tile<E, D, true>(P, dOt, qbl * 32, db * 32, lane, dvacc[db]);
+        dkacc[db] = second_tile<E, D, true>(dS, Qt, qbl * 32, db * 32, lane, dkacc[db]);
       }
     }
   }
 
+  // Sum the NSPLIT partial dK, dV of each key block through LDS.
+  if constexpr (NSPLIT > 1) {
+    float* cb = reinterpret_cast<float*>(smem);
+    lds_barrier();  // every wave is done with the tiles (no loads pending)
+    if (sp != 0 && wave_active) {
+      float* dst = cb + ((kbk * (NSPLIT - 1) + sp - 1) * 32 * NDB) * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dst[(db * 16 + r) * 64] = dkacc[db][r];
+          dst[((NDB + db) * 16 + r) * 64] = dvacc[db][r];
+        }
+    }
+    lds_barrier();
+    if (sp != 0) return;
+    if (wave_active) {
+#pragma unroll
+      for (int p = 0; p < NSPLIT - 1; ++p) {
+        const float* src = cb + ((kbk * (NSPLIT - 1) + p) * 32 * NDB) * 64 + lane;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            dkacc[db][r] += src[(db * 16 + r) * 64];
+            dvacc[db][r] += src[((NDB + db) * 16 + r) * 64];
+          }
+      }
+    }
+  }
   if (!wave_active) return;
   // element r of acc[db]: row k0 + out_row(r, h), column db*32 + n
   T* dk = dK + base;
@@ -170,14 +192,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
 
 template <class E, int D, bool CAUSAL>
 static hipError_t launch(const BwdArgs& a) {
-  constexpr int NW = 4;
-  constexpr int BQ = D == 128 ? 32 : 64;
+  constexpr int NW = is_bf16<E>() ? ATTN_DKDV_NW_BF16 : ATTN_DKDV_NW_F32;
+  constexpr int NSPLIT = is_bf16<E>() ? ATTN_DKDV_NSPLIT_BF16 : ATTN_DKDV_NSPLIT_F32;
+  constexpr int KPW = is_bf16<E>() ? ATTN_DKDV_KPW_BF16 : ATTN_DKDV_KPW_F32;
+  constexpr int NST = is_bf16<E>() ? ATTN_DKDV_NST_BF16 : ATTN_DKDV_NST_F32;
   using T = typename E::T;
-  const int nkt = (a.S + NW * 32 - 1) / (NW * 32);
+  constexpr int BKV = 32 * (NW / NSPLIT);
+  const int nkt = (a.S + BKV - 1) / BKV;
   dim3 grid(a.BH, nkt);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, BQ, CAUSAL>), grid, dim3(NW * 64), 0, a.stream,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout, a.lse,
-                     a.delta, (T*)a.dk, (T*)a.dv, a.S, a.scale * kLog2e, a.scale);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>), grid, dim3(NW * 64), 0,
+                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+                     a.delta, (T*)a.dk, (T*)a.dv, a.S, a.BH * a.S, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 

@@ -4,17 +4,20 @@
 // and Metal", arXiv 2608.01563) lower the attention derivative to a dQ
 // kernel and a fused dK+dV kernel (Section 3.3; profiled as FlashGradQ and
 // FlashGradKV in Section 7.3).  This is the dQ kernel:
-//   D_i  = sum_d dO_id O_id                      (written to the workspace)
+//   D_i  = sum_d dO_id O_id       (written to the workspace, with LSE*log2 e)
 //   P_ij = exp(scale * Q_i.K_j - LSE_i)          (recomputed from the LSE)
 //   dQ_i = scale * sum_j P_ij (dO_i.V_j - D_i) K_j
-// It owns its query rows outright, so dQ needs no atomics and no partial
-// sums: the price is recomputing the two score-shaped products that the
-// dK+dV kernel also forms.
+// A workgroup owns its query rows outright, so dQ needs no atomics and no
+// partial sums in device memory: the price is recomputing the two
+// score-shaped products that the dK+dV kernel also forms.
 //
-// Work split: one workgroup per (query tile of 32*NW rows, batch*head), one
-// wave per 32 queries, key tiles of BK keys staged in LDS and shared.  Per
-// 32-key block a wave forms S^T = K Q^T and dP^T = V dO^T (keys x queries;
-// each lane holds one query, so LSE_i and D_i are one register each), then
+// Work split: one workgroup per (query tile of 32*RB rows, batch*head); each
+// 32-query block is owned by NSPLIT waves that split the key blocks between
+// them and sum their partial dQ through LDS at the end.  K and V stream
+// through an NST-stage ring of LDS tiles filled by direct global->LDS loads
+// issued NST-1 tiles ahead (one barrier per tile).  Per 32-key block a wave
+// forms S^T = K Q^T and dP^T = V dO^T (keys x queries; each lane holds one
+// query, so LSE_i and D_i are one register each), then
 // dS^T = P^T o (dP^T - D) in registers, which is the A operand of
 // dQ (queries x d) += dS K with K read back from the same LDS tile.
 #include "attn_device.hpp"
@@ -22,35 +25,35 @@
 
 namespace attn {
 
-template <class E, int D, int NW, int BK, bool CAUSAL>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ O,
     const typename E::T* __restrict__ dO, const float* __restrict__ LSE,
-    typename E::T* __restrict__ dQ, float* __restrict__ Dws, int S, float c, float scale) {
+    typename E::T* __restrict__ dQ, float* __restrict__ Dws, int S, int L, float c, float scale) {
   using T = typename E::T;
-  constexpr int NT = NW * 64;
-  constexpr int BR = NW * 32;
+  using TL = Tile<E, D>;
+  constexpr int RB = NW / NSPLIT;        // 32-query blocks per workgroup
+  constexpr int BR = 32 * RB;
+  constexpr int BK = 32 * NSPLIT * KPW;  // keys per staged tile
   constexpr int NDB = D / 32;
-  constexpr int NKB = BK / 32;
-  constexpr int STR = row_stride<E, D>();
-  constexpr int STRT = tr_stride<BK>();
-  constexpr int T_ELEMS = BK * STR;
-  constexpr int KT_ELEMS = is_bf16<E>() ? D * STRT : 0;
-  __shared__ __attribute__((aligned(16))) T smem[2 * T_ELEMS + KT_ELEMS];
-  T* Ks = smem;                 // [key][d]
-  T* Vs = smem + T_ELEMS;       // [key][d]
-  T* KsT = smem + 2 * T_ELEMS;  // bf16 only: [d][key]
+  using LD = StageLoader<E, D, BK, NW>;
+  constexpr int TILEB = BK * TL::ROWB;  // one matrix tile; V follows K in a stage
+  constexpr int COMB = RB * (NSPLIT - 1) * 16 * NDB * 64 * 4;
+  constexpr int SMEM = NST * LD::BYTES > COMB ? NST * LD::BYTES : COMB;
+  static_assert(NW % NSPLIT == 0 && NST >= 2 && NST <= 4, "launch shape");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int qb = w / NSPLIT, sp = w % NSPLIT;
   const int bh = blockIdx.x;
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
   const size_t base = (size_t)bh * S * D;
   const T* k = K + base;
   const T* v = V + base;
 
-  const int q0 = qt * BR + w * 32;
+  const int q0 = qt * BR + qb * 32;
   const int qi = q0 + n;
   const bool wave_active = q0 < S;
   const bool qvalid = qi < S;
@@ -76,8 +79,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     }
     di += xhalf(di);
   }
-  if (qvalid && h == 0) Dws[(size_t)bh * S + qi] = di;
   const float lse2 = qvalid ? LSE[(size_t)bh * S + qi] * kLog2e : 0.f;
+  if (qvalid && h == 0 && sp == 0) {
+    Dws[(size_t)bh * S + qi] = di;        // D for the dK+dV kernel
+    Dws[(size_t)L + bh * S + qi] = lse2;  // and LSE in log2 units
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -86,29 +92,27 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   const int kend = CAUSAL ? min(S, qt * BR + BR) : S;
   const int nkt = (kend + BK - 1) / BK;
 
-  TileRegs<T, BK, D, NT> kr, vr;
-  kr.load(k, 0, S, tid);
-  vr.load(v, 0, S, tid);
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nkt) LD::issue(smem + s * LD::BYTES, k, v, s * BK, S, w, lane);
 
   for (int kt = 0; kt < nkt; ++kt) {
-    __syncthreads();
-    kr.template store<STR>(Ks, tid);
-    vr.template store<STR>(Vs, tid);
-    if constexpr (is_bf16<E>()) kr.template store_t<STRT>(KsT, tid);
-    __syncthreads();
-    if (kt + 1 < nkt) {
-      kr.load(k, (kt + 1) * BK, S, tid);
-      vr.load(v, (kt + 1) * BK, S, tid);
-    }
+    wait_tiles<LD::NLOADS>(min(NST - 2, nkt - 1 - kt));
+    lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1
+    if (kt + NST - 1 < nkt)
+      LD::issue(smem + ((kt + NST - 1) % NST) * LD::BYTES, k, v, (kt + NST - 1) * BK, S, w, lane);
     if (!wave_active) continue;
+    const char* Kt = smem + (kt % NST) * LD::BYTES;
+    const char* Vt = Kt + TILEB;
 
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
+    for (int j = 0; j < KPW; ++j) {
+      const int kb = sp + NSPLIT * j;
       const int kk0 = kt * BK + kb * 32;
       if (!(kk0 < S && (!CAUSAL || kk0 <= q0 + 31))) continue;  // wave-uniform
-      const int arow = (kb * 32 + pi32(n)) * STR + h * (D / 2);
-      f32x16 st = dot_rows<E, D>(Ks + arow, qf, zero16());
-      f32x16 dpt = dot_rows<E, D>(Vs + arow, dof, zero16());
+      const int arow = kb * 32 + pi32(n);
+      f32x16 st = dot_tile<E, D>(Kt, arow, h, qf, zero16());
+      f32x16 dpt = dot_tile<E, D>(Vt, arow, h, dof, zero16());
       if (kk0 + 32 > S || (CAUSAL && kk0 + 31 > q0)) {
         // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < S and key <= qi
         const int lim = min(S - 1, CAUSAL ? qi : S - 1) - kk0 - 8 * h;
@@ -125,10 +129,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
       dS.set(st);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        acc[db] = second_product<E, STR, STRT, true>(dS, Ks, KsT, kb * 32, db * 32 + n, h, acc[db]);
+        acc[db] = second_tile<E, D, true>(dS, Kt, kb * 32, db * 32, lane, acc[db]);
     }
   }
 
+  // Sum the NSPLIT partial dQ of each query block through LDS.
+  if constexpr (NSPLIT > 1) {
+    float* cb = reinterpret_cast<float*>(smem);
+    lds_barrier();  // every wave is done with the tiles (no loads pending)
+    if (sp != 0 && wave_active) {
+      float* dst = cb + ((qb * (NSPLIT - 1) + sp - 1) * 16 * NDB) * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[(db * 16 + r) * 64] = acc[db][r];
+    }
+    lds_barrier();
+    if (sp != 0) return;
+    if (wave_active) {
+#pragma unroll
+      for (int p = 0; p < NSPLIT - 1; ++p) {
+        const float* src = cb + ((qb * (NSPLIT - 1) + p) * 16 * NDB) * 64 + lane;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] += src[(db * 16 + r) * 64];
+      }
+    }
+  }
   if (!wave_active) return;
   // acc[db] element r: dQ[q0 + out_row(r, h)][db*32 + n]
   T* dq = dQ + base;
@@ -144,14 +172,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 
 template <class E, int D, bool CAUSAL>
 static hipError_t launch(const BwdArgs& a) {
-  constexpr int NW = 4;
-  constexpr int BK = D == 128 ? 32 : 64;
+  constexpr int NW = is_bf16<E>() ? ATTN_DQ_NW_BF16 : ATTN_DQ_NW_F32;
+  constexpr int NSPLIT = is_bf16<E>() ? ATTN_DQ_NSPLIT_BF16 : ATTN_DQ_NSPLIT_F32;
+  constexpr int KPW = is_bf16<E>() ? ATTN_DQ_KPW_BF16 : ATTN_DQ_KPW_F32;
+  constexpr int NST = is_bf16<E>() ? ATTN_DQ_NST_BF16 : ATTN_DQ_NST_F32;
   using T = typename E::T;
-  const int nqt = (a.S + NW * 32 - 1) / (NW * 32);
+  constexpr int BR = 32 * (NW / NSPLIT);
+  const int nqt = (a.S + BR - 1) / BR;
   dim3 grid(a.BH, nqt);
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, BK, CAUSAL>), grid, dim3(NW * 64), 0, a.stream,
-                     (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.o,
-                     (const T*)a.dout, a.lse, (T*)a.dq, a.delta, a.S, a.scale * kLog2e, a.scale);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>), grid, dim3(NW * 64), 0,
+                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.o,
+                     (const T*)a.dout, a.lse, (T*)a.dq, a.delta, a.S, a.BH * a.S,
+                     a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 

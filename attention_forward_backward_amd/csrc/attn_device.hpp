@@ -29,9 +29,10 @@ namespace attn {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -55,17 +56,7 @@ struct EBF16 {
   }
 };
 
-template <class E> constexpr bool is_bf16() { return E::KL == 8; }
-
-// Row stride (elements) of a row-major tile with D columns in LDS: pads each
-// row by 16 bytes so that 16 lanes reading 16-byte chunks from 16 different
-// rows, and 32 lanes reading one row while 32 read the row 8 further on,
-// touch disjoint banks.
-template <class E, int D> constexpr int row_stride() {
-  return is_bf16<E>() ? D + 8 : D + 4;
-}
-// Row stride of a transposed bf16 tile [column][row] holding N rows.
-template <int N> constexpr int tr_stride() { return N + 8; }
+template <class E> __host__ __device__ constexpr bool is_bf16() { return E::KL == 8; }
 
 // ------------------------------------------------------------------ lane maps
 __device__ inline int pi32(int m) {
@@ -92,8 +83,6 @@ __device__ inline f32x16 zero16() {
 __device__ inline float xhalf(float x) { return __shfl_xor(x, 32); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <class T> __device__ inline float to_f32(T x) { return (float)x; }
 
 // ------------------------------------------------------------------ row fragments
 // The register-resident operand of a score product: lane (n, h) holds
@@ -125,41 +114,123 @@ __device__ inline void load_row_frag(RowFrag<E, D>& rf, const typename E::T* p, 
   }
 }
 
-// acc += A * B where A row (this lane's) is the LDS row `arow` (already
-// offset by h*D/2) and B column is the register fragment `b`.
+// ------------------------------------------------------------------ LDS tiles
+// Tiles live in LDS row-major and unpadded (D elements per row), filled by
+// direct global->LDS 16-byte loads, with the 16-byte chunks of each row
+// permuted by an XOR swizzle so that every read pattern below is free of bank
+// conflicts:
+//   (A) score operand: 16 lanes read the same chunk of 16 different rows
+//       (ds_read_b128);
+//   (B) f32 second operand: 32 lanes read 32 consecutive floats of one row
+//       while the other 32 read the row 8 further on (ds_read_b32);
+//   (C) bf16 second operand: transposed reads of 4 consecutive rows x 32
+//       columns per half wave (ds_read_b64_tr_b16).
+// Every swizzle depends on row % 16 only, so offsets of 16-row aligned blocks
+// are additive.  (f32 with D = 32 keeps a 2-way conflict on pattern B: the
+// two rows 8 apart share a bank half whatever the swizzle.)
 template <class E, int D>
-__device__ inline f32x16 dot_rows(const typename E::T* arow, const RowFrag<E, D>& b, f32x16 acc) {
-  constexpr int NCH = (D / 2) * (int)sizeof(typename E::T) / 16;
-  const u32x4* src = reinterpret_cast<const u32x4*>(arow);
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const u32x4 x = src[c];
+struct Tile {
+  using T = typename E::T;
+  static constexpr int ROWB = D * (int)sizeof(T);  // bytes per row
+  static constexpr int CPR = ROWB / 16;            // 16-byte chunks per row
+  static constexpr int EPC = 16 / (int)sizeof(T);  // elements per chunk
+  __host__ __device__ static constexpr int swz(int row) {
     if constexpr (is_bf16<E>()) {
-      acc = E::mma(__builtin_bit_cast(bf16x8, x), b.f[c], acc);
+      if constexpr (CPR == 4) return (row >> 2) & 3;
+      else if constexpr (CPR == 8) return ((row >> 1) & 7) ^ (((row >> 1) & 1) << 2);
+      else return ((row & 3) << 2) | ((row >> 2) & 3);
     } else {
-      const f32x4 xf = __builtin_bit_cast(f32x4, x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = E::mma(xf[e], b.f[4 * c + e], acc);
+      if constexpr (CPR == 8) return (row >> 1) & 7;
+      else return row & 15;
     }
   }
-  return acc;
+  // Byte offset of element (row, col) in the tile.
+  __host__ __device__ static constexpr int off(int row, int col) {
+    return row * ROWB + (((col / EPC) ^ swz(row)) << 4) + (col % EPC) * (int)sizeof(T);
+  }
+};
+
+// Wait until at most N vector-memory operations of this wave are pending.
+template <int N>
+__device__ inline void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait for the oldest staged tile when `newer` younger tiles (NL loads each)
+// may stay in flight.
+template <int NL>
+__device__ inline void wait_tiles(int newer) {
+  if (newer >= 2) wait_vmem<2 * NL>();
+  else if (newer == 1) wait_vmem<NL>();
+  else wait_vmem<0>();
+}
+// Workgroup barrier that orders LDS accesses without waiting for pending
+// global loads (those are waited for explicitly with wait_vmem).
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Same as dot_rows with the operands swapped: the register fragment is A
-// (this lane's row) and the LDS row is B (this lane's column).
-template <class E, int D>
-__device__ inline f32x16 dot_rows_swapped(const RowFrag<E, D>& a, const typename E::T* brow, f32x16 acc) {
-  constexpr int NCH = (D / 2) * (int)sizeof(typename E::T) / 16;
-  const u32x4* src = reinterpret_cast<const u32x4*>(brow);
+// The direct loads of one staged tile: rows row0 .. row0+BT-1 of two
+// row-major [S x D] matrices (src0, src1) into two consecutive swizzled
+// tiles at `stage`.  Rows past S read row S-1 (finite; the caller masks
+// them).  Each wave issues NLOADS instructions, each filling 1 KiB of LDS.
+template <class E, int D, int BT, int NW>
+struct StageLoader {
+  using T = typename E::T;
+  using TL = Tile<E, D>;
+  static constexpr int CH_PER = BT * TL::CPR;            // chunks per matrix
+  static constexpr int NLOADS = 2 * CH_PER / (NW * 64);  // per wave
+  static constexpr int BYTES = 2 * BT * TL::ROWB;
+  static_assert((2 * CH_PER) % (NW * 64) == 0, "tile must split into whole wave loads");
+  __device__ static inline void issue(char* stage, const T* src0, const T* src1, int row0, int S,
+                                      int w, int lane) {
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const u32x4 x = src[c];
+    for (int i = 0; i < NLOADS; ++i) {
+      const int slot = i * NW + w;         // 1 KiB slot of the stage (wave-uniform)
+      const int chunk = slot * 64 + lane;  // physical chunk in the stage
+      const int mat = chunk / CH_PER;
+      const int pc = chunk - mat * CH_PER;
+      const int row = pc / TL::CPR;
+      const int logical = (pc % TL::CPR) ^ TL::swz(row);
+      const T* src = (mat == 0 ? src0 : src1) + (size_t)min(row0 + row, S - 1) * D + logical * TL::EPC;
+      __builtin_amdgcn_global_load_lds(src, stage + slot * 1024, 16, 0, 0);
+    }
+  }
+};
+
+// Per-query statistics of a staged query tile for the dK+dV kernel: BT
+// values of LSE*log2(e), then BT values of D, with one direct 4-byte load per
+// wave (2*BT/NW active lanes).  Queries past S read query S-1.
+template <int BT, int NW>
+__device__ inline void issue_stats(float* dst, const float* lse2, const float* dlt, int q0, int S,
+                                   int w, int lane) {
+  constexpr int PER = 2 * BT / NW;
+  static_assert(PER <= 64 && (2 * BT) % NW == 0, "stats split");
+  if (lane < PER) {
+    const int e = w * PER + lane;
+    const float* src = e < BT ? lse2 + min(q0 + e, S - 1) : dlt + min(q0 + e - BT, S - 1);
+    __builtin_amdgcn_global_load_lds(src, dst + w * PER, 4, 0, 0);
+  }
+}
+
+// acc += A*B over the D/2 columns of this lane's half, where the A row is
+// row `row` of a swizzled LDS tile and B is the register fragment.
+template <class E, int D>
+__device__ inline f32x16 dot_tile(const char* tile, int row, int h, const RowFrag<E, D>& b,
+                                  f32x16 acc) {
+  using TL = Tile<E, D>;
+  constexpr int NCH = TL::CPR / 2;
+#pragma unroll
+  for (int cc = 0; cc < NCH; ++cc) {
+    const int chunk = h * NCH + cc;
+    const u32x4 x =
+        *reinterpret_cast<const u32x4*>(tile + row * TL::ROWB + ((chunk ^ TL::swz(row)) << 4));
     if constexpr (is_bf16<E>()) {
-      acc = E::mma(a.f[c], __builtin_bit_cast(bf16x8, x), acc);
+      acc = E::mma(__builtin_bit_cast(bf16x8, x), b.f[cc], acc);
     } else {
       const f32x4 xf = __builtin_bit_cast(f32x4, x);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc = E::mma(a.f[4 * c + e], xf[e], acc);
+      for (int e = 0; e < 4; ++e) acc = E::mma(xf[e], b.f[4 * cc + e], acc);
     }
   }
   return acc;
@@ -192,90 +263,50 @@ struct RegOperand<EBF16> {
   }
 };
 
-// acc += R^T-side product over 32 logical rows of a tile in LDS.
+// acc += product over the 32 logical rows row0 .. row0+31 of an LDS tile X:
 //   REG_IS_A = true : acc[m][n] += sum_k R[m = this lane's row][k] * X[k][col0 + n]
 //   REG_IS_A = false: acc[m][n] += sum_k X[k][col0 + m] * R[k][n = this lane's column]
-// where k runs over the 32 logical rows row0 .. row0+31 of X, and R's k-slots
-// are the lane's rho rows.  X is read from
-//   f32 : the row-major tile `x` (stride STR): element [row][col]
-//   bf16: the transposed tile `xt` (stride STRT): element [col][row]
-template <class E, int STR, int STRT, bool REG_IS_A>
-__device__ inline f32x16 second_product(const RegOperand<E>& R, const typename E::T* x,
-                                        const typename E::T* xt, int row0, int col, int h,
-                                        f32x16 acc) {
+// R's k-slots are the lane's rho rows.  The X operand needs, per lane, the
+// k-slot rows of one column: f32 reads one element per MFMA; bf16 reads 8
+// consecutive rows of one column with two transposed LDS reads
+// (ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
+// element e of the 8-byte row read of lane 4e + i/4, position i%4; so lanes
+// that read rows kbase + r/4, columns colbase + 4(r%4) .. +3 hand lane i
+// rows kbase .. kbase+3 of column colbase + i).
+template <class E, int D, bool REG_IS_A>
+__device__ inline f32x16 second_tile(const RegOperand<E>& R, const char* tile, int row0, int col0,
+                                     int lane, f32x16 acc) {
+  using TL = Tile<E, D>;
+  const int h = lane >> 5, n = lane & 31;
   if constexpr (is_bf16<E>()) {
+    const int g = lane >> 4, r = lane & 15;
+    const int col = col0 + 16 * (g & 1) + 4 * (r & 3);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const bf16x8 o = *reinterpret_cast<const bf16x8*>(xt + col * STRT + row0 + 16 * u + 8 * h);
+      s16x4 part[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = row0 + 16 * u + 8 * h + 4 * j + (r >> 2);
+        part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(tile + TL::off(row, col)));
+      }
+      const s16x8 all = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 o = __builtin_bit_cast(bf16x8, all);
       acc = REG_IS_A ? E::mma(R.v[u], o, acc) : E::mma(o, R.v[u], acc);
     }
   } else {
 #pragma unroll
     for (int w = 0; w < 16; ++w) {
-      const float o = x[(row0 + rho(w, h)) * STR + col];
+      const float o = *reinterpret_cast<const float*>(tile + TL::off(row0 + rho(w, h), col0 + n));
       acc = REG_IS_A ? E::mma(R.v[w], o, acc) : E::mma(o, R.v[w], acc);
     }
   }
   return acc;
 }
 
-// ------------------------------------------------------------------ tile staging
-// A ROWS x D tile of a row-major [S x D] matrix, held in registers as 16-byte
-// chunks between the global load and the LDS store (so the next tile's loads
-// are in flight while the current tile is being used).  Rows >= S read as 0.
-template <class T, int ROWS, int D, int NT>
-struct TileRegs {
-  static constexpr int CH = 16 / (int)sizeof(T);
-  static constexpr int CPR = D / CH;           // chunks per row
-  static constexpr int TOTAL = ROWS * CPR;     // chunks per tile
-  static constexpr int N = (TOTAL + NT - 1) / NT;
-  u32x4 c[N];
-
-  __device__ inline void load(const T* base, int r0, int S, int tid) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + i * NT;
-      const int row = idx / CPR, col = (idx % CPR) * CH;
-      const bool ok = (TOTAL % NT == 0 || idx < TOTAL) && (r0 + row < S);
-      // the address is clamped into the matrix even when the value is unused
-      const int srow = min(r0 + row, S - 1);
-      const int scol = (TOTAL % NT == 0 || idx < TOTAL) ? col : 0;
-      c[i] = ok ? *reinterpret_cast<const u32x4*>(base + (size_t)srow * D + scol)
-                : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  // Row-major into LDS with row stride STR (elements).
-  template <int STR>
-  __device__ inline void store(T* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + i * NT;
-      if (TOTAL % NT == 0 || idx < TOTAL) {
-        const int row = idx / CPR, col = (idx % CPR) * CH;
-        *reinterpret_cast<u32x4*>(lds + row * STR + col) = c[i];
-      }
-    }
-  }
-  // Transposed into LDS: element [row][col] goes to lds[col * STRT + row].
-  template <int STRT>
-  __device__ inline void store_t(T* lds, int tid) const {
-    static_assert(sizeof(T) == 2, "transposed staging is for 16-bit elements");
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int idx = tid + i * NT;
-      if (TOTAL % NT == 0 || idx < TOTAL) {
-        const int row = idx / CPR, col = (idx % CPR) * CH;
-        const uint16_t* e = reinterpret_cast<const uint16_t*>(&c[i]);
-        uint16_t* dst = reinterpret_cast<uint16_t*>(lds);
-#pragma unroll
-        for (int t = 0; t < CH; ++t) dst[(col + t) * STRT + row] = e[t];
-      }
-    }
-  }
-};
-
-// Store the 4 consecutive values x[4j .. 4j+3] of a lane's output block to
-// p[0..3] (converted to T).
+// ------------------------------------------------------------------ stores
+// Store the 4 consecutive values of a lane's output block to p[0..3]
+// (converted to T).
 template <class T>
 __device__ inline void store4(T* p, float a, float b, float c, float d) {
   if constexpr (sizeof(T) == 4) {

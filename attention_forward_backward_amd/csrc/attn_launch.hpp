@@ -5,6 +5,83 @@
 
 #include <hip/hip_runtime.h>
 
+// Launch shapes per kernel and contract: NW waves per workgroup, NSPLIT
+// waves sharing each 32-row block (splitting its inner loop), KPW 32-row
+// blocks per wave per staged tile, NST LDS stages in the tile ring.  Defaults come from measurements on
+// MI355X; a build may override them with -D for tuning sweeps.
+#ifndef ATTN_FWD_NW_F32
+#define ATTN_FWD_NW_F32 4
+#endif
+#ifndef ATTN_FWD_NSPLIT_F32
+#define ATTN_FWD_NSPLIT_F32 2
+#endif
+#ifndef ATTN_FWD_KPW_F32
+#define ATTN_FWD_KPW_F32 1
+#endif
+#ifndef ATTN_FWD_NW_BF16
+#define ATTN_FWD_NW_BF16 4
+#endif
+#ifndef ATTN_FWD_NSPLIT_BF16
+#define ATTN_FWD_NSPLIT_BF16 2
+#endif
+#ifndef ATTN_FWD_KPW_BF16
+#define ATTN_FWD_KPW_BF16 1
+#endif
+#ifndef ATTN_DQ_NW_F32
+#define ATTN_DQ_NW_F32 4
+#endif
+#ifndef ATTN_DQ_NSPLIT_F32
+#define ATTN_DQ_NSPLIT_F32 2
+#endif
+#ifndef ATTN_DQ_KPW_F32
+#define ATTN_DQ_KPW_F32 1
+#endif
+#ifndef ATTN_DQ_NW_BF16
+#define ATTN_DQ_NW_BF16 4
+#endif
+#ifndef ATTN_DQ_NSPLIT_BF16
+#define ATTN_DQ_NSPLIT_BF16 2
+#endif
+#ifndef ATTN_DQ_KPW_BF16
+#define ATTN_DQ_KPW_BF16 1
+#endif
+#ifndef ATTN_DKDV_NW_F32
+#define ATTN_DKDV_NW_F32 4
+#endif
+#ifndef ATTN_DKDV_NSPLIT_F32
+#define ATTN_DKDV_NSPLIT_F32 2
+#endif
+#ifndef ATTN_DKDV_KPW_F32
+#define ATTN_DKDV_KPW_F32 1
+#endif
+#ifndef ATTN_DKDV_NW_BF16
+#define ATTN_DKDV_NW_BF16 4
+#endif
+#ifndef ATTN_DKDV_NSPLIT_BF16
+#define ATTN_DKDV_NSPLIT_BF16 2
+#endif
+#ifndef ATTN_DKDV_KPW_BF16
+#define ATTN_DKDV_KPW_BF16 1
+#endif
+#ifndef ATTN_FWD_NST_F32
+#define ATTN_FWD_NST_F32 2
+#endif
+#ifndef ATTN_FWD_NST_BF16
+#define ATTN_FWD_NST_BF16 3
+#endif
+#ifndef ATTN_DQ_NST_F32
+#define ATTN_DQ_NST_F32 2
+#endif
+#ifndef ATTN_DQ_NST_BF16
+#define ATTN_DQ_NST_BF16 3
+#endif
+#ifndef ATTN_DKDV_NST_F32
+#define ATTN_DKDV_NST_F32 2
+#endif
+#ifndef ATTN_DKDV_NST_BF16
+#define ATTN_DKDV_NST_BF16 3
+#endif
+
 namespace attn {
 
 struct FwdArgs {
@@ -23,7 +100,7 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float* lse;
   void *dq, *dk, *dv;
-  float* delta;  // [B*H*S] f32 workspace
+  float* delta;  // workspace: D [B*H*S] f32, then LSE*log2(e) [B*H*S] f32
   int BH, S, D;
   bool causal;
   float scale;

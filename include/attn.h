@@ -80,9 +80,9 @@ attn_status_t attn_fwd(attn_dtype_t dtype,
                        int causal, float scale, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs: the row vector
- * D_i = sum_d dO_id O_id, [B,H,S] float32, rounded up to 256 bytes.
- * Returns 0 for arguments attn_bwd would reject.  Pure host function.
+ * Bytes of device workspace attn_bwd needs: two [B,H,S] float32 row vectors,
+ * D_i = sum_d dO_id O_id followed by LSE_i * log2(e), rounded up to 256
+ * bytes.  Returns 0 for arguments attn_bwd would reject.  Pure host function.
  */
 size_t attn_bwd_workspace_size(attn_dtype_t dtype, int batch, int heads,
                                int seq, int head_dim, int causal);
@@ -96,7 +96,7 @@ size_t attn_bwd_workspace_size(attn_dtype_t dtype, int batch, int heads,
  *   out: dq, dk, dv        [B,H,S,D] dtype  gradients of the loss
  *   workspace              >= attn_bwd_workspace_size() bytes of device
  *                          memory, 16-byte aligned; contents on entry are
- *                          ignored, contents on return are D.
+ *                          ignored, contents on return are D and LSE*log2(e).
  * Deterministic: no atomics; every output element is written by exactly one
  * thread, so repeated calls give bitwise identical results.
  */
@@ -110,7 +110,7 @@ attn_status_t attn_bwd(attn_dtype_t dtype,
 
 /*
  * First backward stage alone (the pages' dQ kernel): for each query row,
- * D_i = sum_d dO_id O_id (written to workspace, [B,H,S] float32) and
+ * D_i = sum_d dO_id O_id and LSE_i * log2(e) (written to the workspace) and
  * dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j with P recomputed from LSE.
  * Same arguments and rules as attn_bwd minus dk/dv.
  */
@@ -124,9 +124,10 @@ attn_status_t attn_bwd_dq(attn_dtype_t dtype,
 /*
  * Second backward stage alone (the pages' fused dK+dV kernel): per key row,
  * dV_j = sum_i P_ij dO_i and dK_j = scale * sum_i P_ij (dP_ij - D_i) Q_i.
- * Reads D from `workspace`, so attn_bwd_dq must have run on the same
- * inputs first (stream order).  Same arguments and rules as attn_bwd
- * minus o and dq.
+ * Reads D and LSE*log2(e) from `workspace`, so attn_bwd_dq must have run on
+ * the same inputs first (stream order); `lse` is validated but the kernel
+ * uses the workspace copy.  Same arguments and rules as attn_bwd minus o
+ * and dq.
  */
 attn_status_t attn_bwd_dkdv(attn_dtype_t dtype,
                             const void* q, const void* k, const void* v,

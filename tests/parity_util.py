@@ -74,6 +74,7 @@ def gpu_fwd_bwd(inp: dict, shape, dtype: str, causal: bool, scale: float, guard:
     torch.cuda.synchronize()
     host = {k_: to_host(v_) for k_, v_ in t.items()}
     host["delta"] = ws[: B * H * S].cpu().numpy().reshape(B, H, S)
+    host["lse2"] = ws[B * H * S: 2 * B * H * S].cpu().numpy().reshape(B, H, S)
     if guard:
         for name, (buf, _) in bufs.items():
             tail = buf[buf.numel() - guard:].float().cpu().numpy()

@@ -59,7 +59,7 @@ def test_bwd_validation():
     assert _bwd(ws=None) == 1
     assert _bwd(D=96) == 2
     assert _bwd(dtype=3) == 2
-    assert _bwd(wsb=8 * 4 - 1) == 3
+    assert _bwd(wsb=2 * 8 * 4 - 1) == 3
     L = afb.lib()
     # split stages validate the same way
     assert L.attn_bwd_dq(0, *[FAKE] * 7, FAKE, 16, 1, 1, 8, 64, 1, 0.1, None) == 3
@@ -70,15 +70,16 @@ def test_bwd_validation():
 
 def test_workspace_size():
     ws = afb.attn_bwd_workspace_size
-    assert ws(0, 8, 12, 512, 64, True) == 8 * 12 * 512 * 4
+    # D and LSE*log2(e): two floats per query row, rounded up to 256 bytes
+    assert ws(0, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4
     assert ws(1, 1, 1, 1, 64, False) == 256
-    assert ws(0, 32, 8, 197, 64, False) == ((32 * 8 * 197 * 4 + 255) // 256) * 256
+    assert ws(0, 32, 8, 197, 64, False) == ((2 * 32 * 8 * 197 * 4 + 255) // 256) * 256
     assert ws(0, 1, 1, 8, 48, True) == 0 and ws(0, 0, 1, 8, 64, True) == 0
     assert ws(5, 1, 1, 8, 64, True) == 0
     prev = 0
     for s in (1, 17, 64, 197, 512, 1024):
         cur = ws(0, 2, 3, s, 64, True)
-        assert cur >= prev and cur >= 2 * 3 * s * 4 and cur % 256 == 0
+        assert cur >= prev and cur >= 2 * 2 * 3 * s * 4 and cur % 256 == 0
         prev = cur
 
 
