@@ -12,8 +12,9 @@ import ctypes
 import os
 import re
 
-__all__ = ["AttnError", "lib", "attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
-           "attn_bwd_workspace_size", "attn_status_string", "attn_version",
+__all__ = ["AttnError", "lib", "attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv",
+           "attn_bwd_dq", "attn_bwd_workspace_size", "attn_bwd_workspace_size_min",
+           "attn_status_string", "attn_version",
            "ATTN_F32", "ATTN_BF16", "STATUS", "LIB_PATH", "HEADER_PATH"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -36,12 +37,12 @@ _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "attn_fwd": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_bwd_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "attn_bwd_workspace_size_min": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "attn_bwd_prep": (_I, [_I, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _P]),
     "attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                       _I, _I, _I, _I, _I, _F, _P]),
-    "attn_bwd_dq": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
-                         _I, _I, _I, _I, _I, _F, _P]),
-    "attn_bwd_dkdv": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
-                           _I, _I, _I, _I, _I, _F, _P]),
+    "attn_bwd_dq": (_I, [_I, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_bwd_dkdv": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_version": (ctypes.c_char_p, []),
 }
@@ -123,6 +124,15 @@ def attn_bwd_workspace_size(dtype: int, batch: int, heads: int, seq: int, head_d
     return int(lib().attn_bwd_workspace_size(dtype, batch, heads, seq, head_dim, int(causal)))
 
 
+def attn_bwd_workspace_size_min(dtype: int, batch: int, heads: int, seq: int, head_dim: int,
+                                causal: bool) -> int:
+    return int(lib().attn_bwd_workspace_size_min(dtype, batch, heads, seq, head_dim, int(causal)))
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
     """O, LSE <- attention(Q, K, V); tensors [B,H,S,D] (LSE [B,H,S] float32)."""
     B, H, S, D = q.shape
@@ -145,30 +155,37 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: 
     code = lib().attn_bwd(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                           o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
                           dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-                          workspace.numel() * workspace.element_size(), B, H, S, D,
+                          _nbytes(workspace), B, H, S, D,
                           int(causal), float(scale), _stream(stream))
     _raise("attn_bwd", code)
 
 
-def attn_bwd_dq(q, k, v, o, dout, lse, dq, workspace, causal: bool, scale: float,
-                stream=None) -> None:
-    B, H, S, D = q.shape
-    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout, "dq": dq}, (B, H, S, D), q.dtype)
+def attn_bwd_prep(o, dout, lse, workspace, stream=None) -> None:
+    B, H, S, D = o.shape
+    _check({"o": o, "dout": dout}, (B, H, S, D), o.dtype)
     _check_f32({"lse": lse}, (B, H, S))
-    code = lib().attn_bwd_dq(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                             o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
-                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             B, H, S, D, int(causal), float(scale), _stream(stream))
-    _raise("attn_bwd_dq", code)
+    code = lib().attn_bwd_prep(_dtype_code(o), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                               workspace.data_ptr(), _nbytes(workspace), B, H, S, D,
+                               _stream(stream))
+    _raise("attn_bwd_prep", code)
 
 
-def attn_bwd_dkdv(q, k, v, dout, lse, dk, dv, workspace, causal: bool, scale: float,
+def attn_bwd_dkdv(q, k, v, dout, dk, dv, workspace, causal: bool, scale: float,
                   stream=None) -> None:
     B, H, S, D = q.shape
     _check({"q": q, "k": k, "v": v, "dout": dout, "dk": dk, "dv": dv}, (B, H, S, D), q.dtype)
-    _check_f32({"lse": lse}, (B, H, S))
     code = lib().attn_bwd_dkdv(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                               dout.data_ptr(), lse.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                               B, H, S, D, int(causal), float(scale), _stream(stream))
+                               dout.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                               _nbytes(workspace), B, H, S, D, int(causal), float(scale),
+                               _stream(stream))
     _raise("attn_bwd_dkdv", code)
+
+
+def attn_bwd_dq(q, k, v, dout, dq, workspace, causal: bool, scale: float, stream=None) -> None:
+    B, H, S, D = q.shape
+    _check({"q": q, "k": k, "v": v, "dout": dout, "dq": dq}, (B, H, S, D), q.dtype)
+    code = lib().attn_bwd_dq(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             dout.data_ptr(), dq.data_ptr(), workspace.data_ptr(),
+                             _nbytes(workspace), B, H, S, D, int(causal), float(scale),
+                             _stream(stream))
+    _raise("attn_bwd_dq", code)

@@ -36,23 +36,39 @@ attn_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
   return ATTN_OK;
 }
 
-size_t delta_bytes(int batch, int heads, int seq) {
-  // D, then LSE * log2(e), one float each per query row
-  const size_t b = 2 * (size_t)batch * heads * seq * sizeof(float);
-  return (b + 255) & ~(size_t)255;
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Minimum workspace: D, then LSE * log2(e), one float each per query row.
+size_t ws_min_bytes(int batch, int heads, int seq) {
+  return round256(2 * (size_t)batch * heads * seq * sizeof(float));
+}
+
+// Row stride of the stored dS: seq rounded up to the largest key tile.
+int ds_stride(int seq) { return (seq + 127) / 128 * 128; }
+
+// Full workspace: the minimum plus dS [B*H][seq][ds_stride(seq)] in dtype.
+size_t ws_full_bytes(attn_dtype_t dtype, int batch, int heads, int seq) {
+  const size_t esize = dtype == ATTN_BF16 ? 2 : 4;
+  return ws_min_bytes(batch, heads, seq) +
+         round256((size_t)batch * heads * seq * (size_t)ds_stride(seq) * esize);
 }
 
 attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// Backward launch descriptor; the dS path is taken iff the workspace holds
+// the full size.
 attn::BwdArgs make_bwd(attn_dtype_t dtype, const void* q, const void* k, const void* v,
                        const void* o, const void* dout, const float* lse, void* dq, void* dk,
-                       void* dv, void* ws, int batch, int heads, int seq, int head_dim,
-                       int causal, float scale, void* stream) {
+                       void* dv, void* ws, size_t ws_bytes, int batch, int heads, int seq,
+                       int head_dim, int causal, float scale, void* stream) {
   attn::BwdArgs a;
   a.bf16 = dtype == ATTN_BF16;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.delta = static_cast<float*>(ws);
+  const bool full = ws_bytes >= ws_full_bytes(dtype, batch, heads, seq);
+  a.ds = full ? static_cast<char*>(ws) + ws_min_bytes(batch, heads, seq) : nullptr;
+  a.SP = ds_stride(seq);
   a.BH = batch * heads; a.S = seq; a.D = head_dim;
   a.causal = causal != 0; a.scale = scale;
   a.stream = static_cast<hipStream_t>(stream);
@@ -81,34 +97,54 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* q, const void* k, const v
 size_t attn_bwd_workspace_size(attn_dtype_t dtype, int batch, int heads, int seq, int head_dim,
                                int causal) {
   if (check_shape(dtype, batch, heads, seq, head_dim, causal, 1.f, false) != ATTN_OK) return 0;
-  return delta_bytes(batch, heads, seq);
+  return ws_full_bytes(dtype, batch, heads, seq);
 }
 
-attn_status_t attn_bwd_dq(attn_dtype_t dtype, const void* q, const void* k, const void* v,
-                          const void* o, const void* dout, const float* lse, void* dq,
-                          void* workspace, size_t workspace_bytes, int batch, int heads, int seq,
-                          int head_dim, int causal, float scale, void* stream) {
-  attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, causal, scale, true);
+size_t attn_bwd_workspace_size_min(attn_dtype_t dtype, int batch, int heads, int seq,
+                                   int head_dim, int causal) {
+  if (check_shape(dtype, batch, heads, seq, head_dim, causal, 1.f, false) != ATTN_OK) return 0;
+  return ws_min_bytes(batch, heads, seq);
+}
+
+attn_status_t attn_bwd_prep(attn_dtype_t dtype, const void* o, const void* dout,
+                            const float* lse, void* workspace, size_t workspace_bytes, int batch,
+                            int heads, int seq, int head_dim, void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, 0, 1.f, false);
   if (st != ATTN_OK) return st;
-  if ((st = check_ptrs({q, k, v, o, dout, lse, dq, workspace})) != ATTN_OK) return st;
-  if (workspace_bytes < delta_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
-  const attn::BwdArgs a = make_bwd(dtype, q, k, v, o, dout, lse, dq, nullptr, nullptr, workspace,
-                                   batch, heads, seq, head_dim, causal, scale, stream);
-  return from_hip(attn::launch_bwd_dq(a));
+  if ((st = check_ptrs({o, dout, lse, workspace})) != ATTN_OK) return st;
+  if (workspace_bytes < ws_min_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
+  const attn::BwdArgs a = make_bwd(dtype, nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr,
+                                   nullptr, workspace, workspace_bytes, batch, heads, seq, head_dim,
+                                   0, 1.f, stream);
+  return from_hip(attn::launch_bwd_prep(a));
 }
 
 attn_status_t attn_bwd_dkdv(attn_dtype_t dtype, const void* q, const void* k, const void* v,
-                            const void* dout, const float* lse, void* dk, void* dv,
-                            const void* workspace, size_t workspace_bytes, int batch, int heads,
-                            int seq, int head_dim, int causal, float scale, void* stream) {
+                            const void* dout, void* dk, void* dv, void* workspace,
+                            size_t workspace_bytes, int batch, int heads, int seq, int head_dim,
+                            int causal, float scale, void* stream) {
   attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
-  if ((st = check_ptrs({q, k, v, dout, lse, dk, dv, workspace})) != ATTN_OK) return st;
-  if (workspace_bytes < delta_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
-  const attn::BwdArgs a =
-      make_bwd(dtype, q, k, v, nullptr, dout, lse, nullptr, dk, dv, const_cast<void*>(workspace),
-               batch, heads, seq, head_dim, causal, scale, stream);
+  if ((st = check_ptrs({q, k, v, dout, dk, dv, workspace})) != ATTN_OK) return st;
+  if (workspace_bytes < ws_min_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
+  const attn::BwdArgs a = make_bwd(dtype, q, k, v, nullptr, dout, nullptr, nullptr, dk, dv,
+                                   workspace, workspace_bytes, batch, heads, seq, head_dim, causal,
+                                   scale, stream);
   return from_hip(attn::launch_bwd_dkdv(a));
+}
+
+attn_status_t attn_bwd_dq(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                          const void* dout, void* dq, const void* workspace,
+                          size_t workspace_bytes, int batch, int heads, int seq, int head_dim,
+                          int causal, float scale, void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, causal, scale, true);
+  if (st != ATTN_OK) return st;
+  if ((st = check_ptrs({q, k, v, dout, dq, workspace})) != ATTN_OK) return st;
+  if (workspace_bytes < ws_min_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
+  const attn::BwdArgs a = make_bwd(dtype, q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr,
+                                   const_cast<void*>(workspace), workspace_bytes, batch, heads,
+                                   seq, head_dim, causal, scale, stream);
+  return from_hip(attn::launch_bwd_dq(a));
 }
 
 attn_status_t attn_bwd(attn_dtype_t dtype, const void* q, const void* k, const void* v,
@@ -118,11 +154,13 @@ attn_status_t attn_bwd(attn_dtype_t dtype, const void* q, const void* k, const v
   attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
   if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace})) != ATTN_OK) return st;
-  if (workspace_bytes < delta_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
-  const attn::BwdArgs a = make_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, batch,
-                                   heads, seq, head_dim, causal, scale, stream);
-  if ((st = from_hip(attn::launch_bwd_dq(a))) != ATTN_OK) return st;
-  return from_hip(attn::launch_bwd_dkdv(a));
+  if (workspace_bytes < ws_min_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
+  const attn::BwdArgs a = make_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace,
+                                   workspace_bytes, batch, heads, seq, head_dim, causal, scale,
+                                   stream);
+  if ((st = from_hip(attn::launch_bwd_prep(a))) != ATTN_OK) return st;
+  if ((st = from_hip(attn::launch_bwd_dkdv(a))) != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dq(a));
 }
 
 const char* attn_status_string(attn_status_t s) {
@@ -136,6 +174,6 @@ const char* attn_status_string(attn_status_t s) {
   return "unknown status";
 }
 
-const char* attn_version(void) { return "0.1.0"; }
+const char* attn_version(void) { return "0.2.0"; }
 
 }  // extern "C"

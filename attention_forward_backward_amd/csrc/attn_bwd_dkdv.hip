@@ -7,7 +7,9 @@
 //   P_ij  = exp(scale * Q_i.K_j - LSE_i)
 //   dV_j  = sum_i P_ij dO_i
 //   dK_j  = scale * sum_i P_ij (dO_i.V_j - D_i) Q_i
-// with D_i and LSE_i*log2(e) read from the workspace the dQ kernel wrote.
+// with D_i and LSE_i*log2(e) read from the workspace (the prep kernel).  When
+// the workspace holds room for it, the kernel also stores dS (the values it
+// feeds its own dK product), from which dQ = scale * dS K is a plain GEMM.
 //
 // Work split: one workgroup per (key tile of 32*RB rows, batch*head).  Each
 // 32-key block is owned by NSPLIT waves that keep its K and V rows in
@@ -23,12 +25,12 @@
 
 namespace attn {
 
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
-    int S, int L, float c, float scale) {
+    typename E::T* __restrict__ dSout, int SP, int S, int L, float c, float scale) {
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-key blocks per workgroup
@@ -132,6 +134,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         s[r] = p;
         dp[r] = p * (dp[r] - dq_[r]);
       }
+      if constexpr (WDS) {
+        // dS for the dQ GEMM: every entry of the block (exact zeros where
+        // masked and for keys past S), rows past S not stored.
+        T* dsq = dSout + (size_t)bh * S * SP + kj;
+        const bool kvalid = kj < S;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qq0 + rho(r, h);
+          if (qi < S) dsq[(size_t)qi * SP] = kvalid ? (T)dp[r] : (T)0.f;
+        }
+      }
       RegOperand<E> P, dS;
       P.set(s);
       dS.set(dp);
@@ -190,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
   }
 }
 
-template <class E, int D, bool CAUSAL>
+template <class E, int D, bool CAUSAL, bool WDS>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int NW = is_bf16<E>() ? ATTN_DKDV_NW_BF16 : ATTN_DKDV_NW_F32;
   constexpr int NSPLIT = is_bf16<E>() ? ATTN_DKDV_NSPLIT_BF16 : ATTN_DKDV_NSPLIT_F32;
@@ -200,15 +213,17 @@ static hipError_t launch(const BwdArgs& a) {
   constexpr int BKV = 32 * (NW / NSPLIT);
   const int nkt = (a.S + BKV - 1) / BKV;
   dim3 grid(a.BH, nkt);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>), grid, dim3(NW * 64), 0,
-                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                     a.delta, (T*)a.dk, (T*)a.dv, a.S, a.BH * a.S, a.scale * kLog2e, a.scale);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS>), grid,
+                     dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                     (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SP, a.S,
+                     a.BH * a.S, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 
 template <class E, int D>
 static hipError_t launch_c(const BwdArgs& a) {
-  return a.causal ? launch<E, D, true>(a) : launch<E, D, false>(a);
+  if (a.ds != nullptr) return a.causal ? launch<E, D, true, true>(a) : launch<E, D, false, true>(a);
+  return a.causal ? launch<E, D, true, false>(a) : launch<E, D, false, false>(a);
 }
 
 template <class E>

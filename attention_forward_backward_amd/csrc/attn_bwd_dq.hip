@@ -3,15 +3,19 @@
 // The pages ("Meganeura: Portable GPU Training and Inference through Vulkan
 // and Metal", arXiv 2608.01563) lower the attention derivative to a dQ
 // kernel and a fused dK+dV kernel (Section 3.3; profiled as FlashGradQ and
-// FlashGradKV in Section 7.3).  This is the dQ kernel:
-//   D_i  = sum_d dO_id O_id       (written to the workspace, with LSE*log2 e)
-//   P_ij = exp(scale * Q_i.K_j - LSE_i)          (recomputed from the LSE)
-//   dQ_i = scale * sum_j P_ij (dO_i.V_j - D_i) K_j
-// A workgroup owns its query rows outright, so dQ needs no atomics and no
-// partial sums in device memory: the price is recomputing the two
-// score-shaped products that the dK+dV kernel also forms.
+// FlashGradKV in Section 7.3).  This file holds the two ways to form
+//   dQ_i = scale * sum_j dS_ij K_j,   dS_ij = P_ij (dO_i.V_j - D_i)
+// without atomics or partial sums in device memory:
+//  * bwd_dq_gemm_kernel: when the workspace can hold dS (B*H*S*S values,
+//    written by the dK+dV kernel), dQ is a causal-blocked GEMM dS K;
+//  * bwd_dq_kernel: otherwise the dQ kernel recomputes P (from the LSE) and
+//    dP per key tile, as the pages' separate dQ kernel does; a workgroup
+//    owns its query rows outright.  The price is recomputing the two
+//    score-shaped products that the dK+dV kernel also forms.
+// D_i and LSE_i*log2(e) come from the workspace (the prep kernel).
 //
-// Work split: one workgroup per (query tile of 32*RB rows, batch*head); each
+// Recompute kernel work split: one workgroup per (query tile of 32*RB rows,
+// batch*head); each
 // 32-query block is owned by NSPLIT waves that split the key blocks between
 // them and sum their partial dQ through LDS at the end.  K and V stream
 // through an NST-stage ring of LDS tiles filled by direct global->LDS loads
@@ -28,9 +32,9 @@ namespace attn {
 template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
-    const typename E::T* __restrict__ V, const typename E::T* __restrict__ O,
-    const typename E::T* __restrict__ dO, const float* __restrict__ LSE,
-    typename E::T* __restrict__ dQ, float* __restrict__ Dws, int S, int L, float c, float scale) {
+    const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
+    typename E::T* __restrict__ dQ, const float* __restrict__ Dws, int S, int L, float c,
+    float scale) {
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-query blocks per workgroup
@@ -62,28 +66,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   RowFrag<E, D> qf, dof;
   load_row_frag<E, D>(qf, Q + qrow, qvalid);
   load_row_frag<E, D>(dof, dO + qrow, qvalid);
-
-  // D_i = sum_d dO_id O_id: this lane's half row, then the other half.
-  float di = 0.f;
-  {
-    RowFrag<E, D> of;
-    load_row_frag<E, D>(of, O + qrow, qvalid);
-#pragma unroll
-    for (int s = 0; s < RowFrag<E, D>::NS; ++s) {
-      if constexpr (is_bf16<E>()) {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) di += (float)dof.f[s][t] * (float)of.f[s][t];
-      } else {
-        di += dof.f[s] * of.f[s];
-      }
-    }
-    di += xhalf(di);
-  }
-  const float lse2 = qvalid ? LSE[(size_t)bh * S + qi] * kLog2e : 0.f;
-  if (qvalid && h == 0 && sp == 0) {
-    Dws[(size_t)bh * S + qi] = di;        // D for the dK+dV kernel
-    Dws[(size_t)L + bh * S + qi] = lse2;  // and LSE in log2 units
-  }
+  // D_i and LSE_i*log2(e), written by the prep kernel
+  const float di = qvalid ? Dws[(size_t)bh * S + qi] : 0.f;
+  const float lse2 = qvalid ? Dws[(size_t)L + (size_t)bh * S + qi] : 0.f;
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -170,6 +155,127 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   }
 }
 
+// dQ = scale * dS K from the stored dS.  One workgroup per (query tile of
+// 32*RB rows, batch*head); each 32-query block is owned by NSPLIT waves that
+// split the key blocks and sum their partials through LDS.  A staged tile is
+// the dS block [queries x 32*NSPLIT*KPW keys] and the matching K rows; the
+// dS rows are the register-operand (A) side in the same k-slot layout the
+// other kernels use, and K is read from LDS as in their second products.
+// Blocks with no visible key (above the causal diagonal, or past S) are
+// skipped; the dK+dV kernel wrote exact zeros for every masked entry and
+// every key past S inside the blocks it processed.
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
+    const typename E::T* __restrict__ K, const typename E::T* __restrict__ dS,
+    typename E::T* __restrict__ dQ, int S, int SP, float scale) {
+  using T = typename E::T;
+  constexpr int RB = NW / NSPLIT;
+  constexpr int BR = 32 * RB;
+  constexpr int BK = 32 * NSPLIT * KPW;
+  constexpr int NDB = D / 32;
+  using LDS_ = TileLoader<E, BK, BR, NW>;  // dS block: BR queries x BK keys
+  using LDK = TileLoader<E, D, BK, NW>;    // K rows:   BK keys x D
+  constexpr int STAGE = LDS_::BYTES + LDK::BYTES;
+  constexpr int NL = LDS_::NLOADS + LDK::NLOADS;
+  constexpr int COMB = RB * (NSPLIT - 1) * 16 * NDB * 64 * 4;
+  constexpr int SMEM = NST * STAGE > COMB ? NST * STAGE : COMB;
+  static_assert(NW % NSPLIT == 0 && NST >= 2 && NST <= 4, "launch shape");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int qb = w / NSPLIT, sp = w % NSPLIT;
+  const int bh = blockIdx.x;
+  const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
+  const T* k = K + (size_t)bh * S * D;
+  const T* ds = dS + (size_t)bh * S * SP;
+  const int qw0 = qt * BR;         // first query of the workgroup
+  const int q0 = qw0 + qb * 32;    // first query of this wave's block
+  const bool wave_active = q0 < S;
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = zero16();
+
+  const int kend = CAUSAL ? min(S, qw0 + BR) : S;
+  const int nkt = (kend + BK - 1) / BK;
+  auto issue = [&](int t) {
+    char* st = smem + (t % NST) * STAGE;
+    LDS_::issue(st, ds, SP, qw0, S, t * BK, w, lane);
+    LDK::issue(st + LDS_::BYTES, k, D, t * BK, S, 0, w, lane);
+  };
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < nkt) issue(s);
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    wait_tiles<NL>(min(NST - 2, nkt - 1 - kt));
+    lds_barrier();
+    if (kt + NST - 1 < nkt) issue(kt + NST - 1);
+    if (!wave_active) continue;
+    const char* St = smem + (kt % NST) * STAGE;
+    const char* Kt = St + LDS_::BYTES;
+#pragma unroll
+    for (int j = 0; j < KPW; ++j) {
+      const int kb = sp + NSPLIT * j;
+      const int kk0 = kt * BK + kb * 32;
+      if (!(kk0 < S && (!CAUSAL || kk0 <= q0 + 31))) continue;  // wave-uniform
+      RegOperand<E> R;
+      load_reg_operand<E, BK>(R, St, qb * 32 + n, kb * 32, h);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        acc[db] = second_tile<E, D, true>(R, Kt, kb * 32, db * 32, lane, acc[db]);
+    }
+  }
+
+  if constexpr (NSPLIT > 1) {
+    float* cb = reinterpret_cast<float*>(smem);
+    lds_barrier();
+    if (sp != 0 && wave_active) {
+      float* dst = cb + ((qb * (NSPLIT - 1) + sp - 1) * 16 * NDB) * 64 + lane;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[(db * 16 + r) * 64] = acc[db][r];
+    }
+    lds_barrier();
+    if (sp != 0) return;
+    if (wave_active) {
+#pragma unroll
+      for (int p = 0; p < NSPLIT - 1; ++p) {
+        const float* src = cb + ((qb * (NSPLIT - 1) + p) * 16 * NDB) * 64 + lane;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[db][r] += src[(db * 16 + r) * 64];
+      }
+    }
+  }
+  if (!wave_active) return;
+  T* dq = dQ + (size_t)bh * S * D;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = q0 + out_row(r, h);
+    if (row < S) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) dq[(size_t)row * D + db * 32 + n] = (T)(acc[db][r] * scale);
+    }
+  }
+}
+
+template <class E, int D, bool CAUSAL>
+static hipError_t launch_gemm(const BwdArgs& a) {
+  constexpr int NW = 4, NSPLIT = 2, KPW = 1;
+  constexpr int NST = is_bf16<E>() ? 3 : 2;
+  using T = typename E::T;
+  constexpr int BR = 32 * (NW / NSPLIT);
+  const int nqt = (a.S + BR - 1) / BR;
+  dim3 grid(a.BH, nqt);
+  hipLaunchKernelGGL((bwd_dq_gemm_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>), grid, dim3(NW * 64),
+                     0, a.stream, (const T*)a.k, (const T*)a.ds, (T*)a.dq, a.S, a.SP, a.scale);
+  return hipGetLastError();
+}
+
 template <class E, int D, bool CAUSAL>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int NW = is_bf16<E>() ? ATTN_DQ_NW_BF16 : ATTN_DQ_NW_F32;
@@ -181,14 +287,14 @@ static hipError_t launch(const BwdArgs& a) {
   const int nqt = (a.S + BR - 1) / BR;
   dim3 grid(a.BH, nqt);
   hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>), grid, dim3(NW * 64), 0,
-                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.o,
-                     (const T*)a.dout, a.lse, (T*)a.dq, a.delta, a.S, a.BH * a.S,
-                     a.scale * kLog2e, a.scale);
+                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+                     (T*)a.dq, a.delta, a.S, a.BH * a.S, a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }
 
 template <class E, int D>
 static hipError_t launch_c(const BwdArgs& a) {
+  if (a.ds != nullptr) return a.causal ? launch_gemm<E, D, true>(a) : launch_gemm<E, D, false>(a);
   return a.causal ? launch<E, D, true>(a) : launch<E, D, false>(a);
 }
 

@@ -1,0 +1,83 @@
+// attn_bwd_prep.hip -- per-query-row statistics the backward kernels share.
+//
+// For the attention derivative ("Meganeura: Portable GPU Training and
+// Inference through Vulkan and Metal", arXiv 2608.01563, Section 3.1 --
+// attention's local derivative rule; Section 3.3 -- dQ and fused dK+dV
+// kernels), every query row i needs
+//   D_i      = sum_d dO_id O_id        (dS_ij = P_ij (dP_ij - D_i))
+//   LSE_i * log2(e)                     (P_ij = exp2(scale*log2(e)*S_ij - LSE_i*log2(e)))
+// This memory-bound pass writes both to the workspace once, so the
+// compute kernels read two floats per query instead of recomputing them.
+//
+// Layout: a wave covers 64*16 bytes of consecutive rows per step (coalesced
+// 16-byte loads); the CPR lanes that share a row reduce their partial dot
+// products with cross-lane adds.
+#include "attn_device.hpp"
+#include "attn_launch.hpp"
+
+namespace attn {
+
+template <class E, int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __restrict__ O,
+                                                        const typename E::T* __restrict__ dO,
+                                                        const float* __restrict__ LSE,
+                                                        float* __restrict__ ws, int L) {
+  using T = typename E::T;
+  constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;              // chunks per row (<= 32)
+  constexpr int RPW = 64 / CPR;             // rows per wave step
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int row = wave * RPW + lane / CPR;
+  const int chunk = lane % CPR;
+  float acc = 0.f;
+  if (row < L) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + chunk * EPC);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + chunk * EPC);
+    if constexpr (is_bf16<E>()) {
+      const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc += (float)x[t] * (float)y[t];
+    } else {
+      const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc += x[t] * y[t];
+    }
+  }
+  // sum over the CPR lanes of the row (aligned groups of CPR lanes)
+#pragma unroll
+  for (int o = 1; o < CPR; o <<= 1) acc += __shfl_xor(acc, o);
+  if (row < L && chunk == 0) {
+    ws[row] = acc;
+    ws[(size_t)L + row] = LSE[row] * kLog2e;
+  }
+}
+
+template <class E, int D>
+static hipError_t launch(const BwdArgs& a) {
+  constexpr int EPC = 16 / (int)sizeof(typename E::T);
+  constexpr int RPW = 64 / (D / EPC);
+  const int L = a.BH * a.S;
+  const int waves = (L + RPW - 1) / RPW;
+  const int blocks = (waves + 3) / 4;
+  using T = typename E::T;
+  hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3(blocks), dim3(256), 0, a.stream, (const T*)a.o,
+                     (const T*)a.dout, a.lse, a.delta, L);
+  return hipGetLastError();
+}
+
+template <class E>
+static hipError_t launch_d(const BwdArgs& a) {
+  switch (a.D) {
+    case 32: return launch<E, 32>(a);
+    case 64: return launch<E, 64>(a);
+    case 128: return launch<E, 128>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_prep(const BwdArgs& a) {
+  return a.bf16 ? launch_d<EBF16>(a) : launch_d<EF32>(a);
+}
+
+}  // namespace attn

@@ -198,6 +198,31 @@ struct StageLoader {
   }
 };
 
+// The direct loads of one swizzled tile of a single row-major matrix:
+// rows row0 .. row0+BT-1 (rows past `rows` read row rows-1), columns
+// col0 .. col0+COLS-1 of a matrix with row stride `ld` elements.
+template <class E, int COLS, int BT, int NW>
+struct TileLoader {
+  using T = typename E::T;
+  using TL = Tile<E, COLS>;
+  static constexpr int CH = BT * TL::CPR;        // chunks in the tile
+  static constexpr int NLOADS = CH / (NW * 64);  // per wave
+  static constexpr int BYTES = BT * TL::ROWB;
+  static_assert(CH % (NW * 64) == 0, "tile must split into whole wave loads");
+  __device__ static inline void issue(char* dst, const T* src, size_t ld, int row0, int rows,
+                                      int col0, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < NLOADS; ++i) {
+      const int slot = i * NW + w;
+      const int pc = slot * 64 + lane;
+      const int row = pc / TL::CPR;
+      const int logical = (pc % TL::CPR) ^ TL::swz(row);
+      const T* g = src + (size_t)min(row0 + row, rows - 1) * ld + col0 + logical * TL::EPC;
+      __builtin_amdgcn_global_load_lds(g, dst + slot * 1024, 16, 0, 0);
+    }
+  }
+};
+
 // Per-query statistics of a staged query tile for the dK+dV kernel: BT
 // values of LSE*log2(e), then BT values of D, with one direct 4-byte load per
 // wave (2*BT/NW active lanes).  Queries past S read query S-1.
@@ -262,6 +287,29 @@ struct RegOperand<EBF16> {
       for (int t = 0; t < 8; ++t) v[u][t] = (__bf16)x[8 * u + t];  // round to nearest even
   }
 };
+
+// Load a register operand in the k-slot layout of RegOperand (k-slot
+// (w, h) <-> column rho(w, h) for f32; (u, h, t) <-> column 16u + 8h + t for
+// bf16) from row `row` of a swizzled LDS tile with COLS columns, columns
+// col0 .. col0+31.
+template <class E, int COLS>
+__device__ inline void load_reg_operand(RegOperand<E>& R, const char* tile, int row, int col0,
+                                        int h) {
+  using TL = Tile<E, COLS>;
+  if constexpr (is_bf16<E>()) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      R.v[u] = *reinterpret_cast<const bf16x8*>(tile + TL::off(row, col0 + 16 * u + 8 * h));
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // chunk of 4 columns starting at rho(4c, h) = 16*(c/2) + 8h + 4*(c%2)
+      const f32x4 x = *reinterpret_cast<const f32x4*>(tile + TL::off(row, col0 + rho(4 * c, h)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) R.v[4 * c + e] = x[e];
+    }
+  }
+}
 
 // acc += product over the 32 logical rows row0 .. row0+31 of an LDS tile X:
 //   REG_IS_A = true : acc[m][n] += sum_k R[m = this lane's row][k] * X[k][col0 + n]

@@ -101,6 +101,8 @@ struct BwdArgs {
   const float* lse;
   void *dq, *dk, *dv;
   float* delta;  // workspace: D [B*H*S] f32, then LSE*log2(e) [B*H*S] f32
+  void* ds;      // workspace dS [B*H][S][SP] (dtype), or null: dQ recomputes
+  int SP;        // row stride of dS (S rounded up to the key tile)
   int BH, S, D;
   bool causal;
   float scale;
@@ -110,5 +112,6 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
+hipError_t launch_bwd_prep(const BwdArgs& a);
 
 }  // namespace attn

@@ -32,10 +32,11 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd+bwd TFLOP/s (f32 / bf16-MFMA) at B8 H12 S512 D64 causal, 1 GPU"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}  # MI355X dense MFMA: f32, bf16
 PEAK_HBM_GBS = 8000.0
-# MFMA FLOP per visible pair that each kernel executes (its own contractions)
-KERNEL_FLOP_PER_PAIR_D = {"attn_fwd": 4, "attn_bwd_dq": 6, "attn_bwd_dkdv": 8}
-KERNEL_SYMBOL = {"attn_fwd": "fwd_kernel", "attn_bwd_dq": "bwd_dq_kernel",
-                 "attn_bwd_dkdv": "bwd_dkdv_kernel"}
+# MFMA FLOP per visible pair that each compute kernel executes (its own
+# contractions; the dQ stage is the dS*K GEMM with the recommended workspace)
+KERNEL_FLOP_PER_PAIR_D = {"attn_fwd": 4, "attn_bwd_dkdv": 8, "attn_bwd_dq": 2}
+KERNEL_SYMBOL = {"attn_fwd": "fwd_kernel", "attn_bwd_prep": "bwd_prep_kernel",
+                 "attn_bwd_dkdv": "bwd_dkdv_kernel", "attn_bwd_dq": "bwd_dq_gemm_kernel"}
 
 
 def parse():
@@ -143,11 +144,14 @@ def main():
         def fwd():
             afb.attn_fwd(q, k, v, o, lse, cfg.causal, sc, stream)
 
-        def bwd_dq():
-            afb.attn_bwd_dq(q, k, v, o, do, lse, dq, ws, cfg.causal, sc, stream)
+        def bwd_prep():
+            afb.attn_bwd_prep(o, do, lse, ws, stream)
 
         def bwd_dkdv():
-            afb.attn_bwd_dkdv(q, k, v, do, lse, dk, dv, ws, cfg.causal, sc, stream)
+            afb.attn_bwd_dkdv(q, k, v, do, dk, dv, ws, cfg.causal, sc, stream)
+
+        def bwd_dq():
+            afb.attn_bwd_dq(q, k, v, do, dq, ws, cfg.causal, sc, stream)
 
         def bwd():
             afb.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, cfg.causal, sc, stream)
@@ -175,18 +179,27 @@ def main():
                "value": flops["fwd_bwd"] / (ms_step * 1e-3) / 1e12}
         if not args.only_step:
             ms = {"fwd": timed(fwd, args.steps, 3), "bwd": timed(bwd, args.steps, 3)}
-            kern = {"attn_fwd": ms["fwd"], "attn_bwd_dq": timed(bwd_dq, args.steps, 3),
-                    "attn_bwd_dkdv": timed(bwd_dkdv, args.steps, 3)}
+            kern = {"attn_fwd": ms["fwd"], "attn_bwd_prep": timed(bwd_prep, args.steps, 3),
+                    "attn_bwd_dkdv": timed(bwd_dkdv, args.steps, 3),
+                    "attn_bwd_dq": timed(bwd_dq, args.steps, 3)}
             res["phases"] = {
                 ph: {"ms": ms[ph], "tflops": flops[ph] / (ms[ph] * 1e-3) / 1e12}
                 for ph in ("fwd", "bwd")}
             res["kernels"] = {}
+            esz = 2 if dt == "bf16" else 4
             for kname, kms in kern.items():
+                if kname == "attn_bwd_prep":
+                    # memory-bound: O and dO read, LSE read, D and LSE*log2(e) written
+                    kb = 2 * B * H * S * D * esz + 3 * B * H * S * 4
+                    res["kernels"][kname] = {
+                        "symbol": KERNEL_SYMBOL[kname], "avg_us": kms * 1e3,
+                        "bytes_per_launch": kb, "gbs": kb / (kms * 1e-3) / 1e9}
+                    continue
                 kf = KERNEL_FLOP_PER_PAIR_D[kname] * D * cfg.pairs
                 res["kernels"][kname] = {
                     "symbol": KERNEL_SYMBOL[kname], "avg_us": kms * 1e3,
                     "flop_per_launch": kf, "tflops": kf / (kms * 1e-3) / 1e12}
-            dom = max(kern, key=kern.get)
+            dom = max((kk for kk in kern if kk != "attn_bwd_prep"), key=kern.get)
             dk_ = res["kernels"][dom]
             achieved = dk_["tflops"]
             res["roofline"] = {

@@ -80,25 +80,35 @@ attn_status_t attn_fwd(attn_dtype_t dtype,
                        int causal, float scale, void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs: two [B,H,S] float32 row vectors,
- * D_i = sum_d dO_id O_id followed by LSE_i * log2(e), rounded up to 256
- * bytes.  Returns 0 for arguments attn_bwd would reject.  Pure host function.
+ * Workspace of the backward, in bytes (pure host functions; 0 for arguments
+ * attn_bwd would reject).  The workspace holds, for every query row,
+ * D_i = sum_d dO_id O_id and LSE_i * log2(e) (two [B,H,S] float32 vectors,
+ * rounded up to 256 bytes: the minimum), and -- only in the recommended
+ * size -- dS [B*H][S][ceil(S/128)*128] in the element type, which lets dQ be
+ * computed as one GEMM dS K instead of recomputing the scores.
+ *   attn_bwd_workspace_size      recommended size (the dS path)
+ *   attn_bwd_workspace_size_min  minimum size (dQ recomputes P and dP)
+ * The backward takes the dS path iff workspace_bytes >= the recommended
+ * size; the recommended size grows as S^2, so very long sequences can use
+ * the minimum instead.
  */
 size_t attn_bwd_workspace_size(attn_dtype_t dtype, int batch, int heads,
                                int seq, int head_dim, int causal);
+size_t attn_bwd_workspace_size_min(attn_dtype_t dtype, int batch, int heads,
+                                   int seq, int head_dim, int causal);
 
 /*
- * Backward pass: attn_bwd_dq followed by attn_bwd_dkdv on `stream`
- * (the pages' dQ kernel and fused dK+dV kernel, Section 3.3 and the
- * attention-backward profile of Section 7.3).
+ * Backward pass (the pages' attention derivative: dQ kernel and fused dK+dV
+ * kernel, Section 3.3; profiled in Section 7.3): attn_bwd_prep, then
+ * attn_bwd_dkdv, then attn_bwd_dq, enqueued on `stream`.
  *   in : q, k, v, o, dout  [B,H,S,D] dtype  (o = the forward's output)
  *        lse               [B,H,S]   float32 (the forward's LSE)
  *   out: dq, dk, dv        [B,H,S,D] dtype  gradients of the loss
- *   workspace              >= attn_bwd_workspace_size() bytes of device
+ *   workspace              >= attn_bwd_workspace_size_min() bytes of device
  *                          memory, 16-byte aligned; contents on entry are
- *                          ignored, contents on return are D and LSE*log2(e).
+ *                          ignored and left undefined.
  * Deterministic: no atomics; every output element is written by exactly one
- * thread, so repeated calls give bitwise identical results.
+ * thread in a fixed order, so repeated calls give bitwise identical results.
  */
 attn_status_t attn_bwd(attn_dtype_t dtype,
                        const void* q, const void* k, const void* v,
@@ -109,33 +119,41 @@ attn_status_t attn_bwd(attn_dtype_t dtype,
                        int causal, float scale, void* stream);
 
 /*
- * First backward stage alone (the pages' dQ kernel): for each query row,
- * D_i = sum_d dO_id O_id and LSE_i * log2(e) (written to the workspace) and
- * dQ_i = scale * sum_j P_ij (dP_ij - D_i) K_j with P recomputed from LSE.
- * Same arguments and rules as attn_bwd minus dk/dv.
+ * Backward stage 1 alone: D_i = sum_d dO_id O_id and LSE_i * log2(e) into
+ * the workspace (memory-bound, one pass over O and dO).
  */
-attn_status_t attn_bwd_dq(attn_dtype_t dtype,
-                          const void* q, const void* k, const void* v,
-                          const void* o, const void* dout, const float* lse,
-                          void* dq, void* workspace, size_t workspace_bytes,
-                          int batch, int heads, int seq, int head_dim,
-                          int causal, float scale, void* stream);
+attn_status_t attn_bwd_prep(attn_dtype_t dtype,
+                            const void* o, const void* dout, const float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            int batch, int heads, int seq, int head_dim,
+                            void* stream);
 
 /*
- * Second backward stage alone (the pages' fused dK+dV kernel): per key row,
- * dV_j = sum_i P_ij dO_i and dK_j = scale * sum_i P_ij (dP_ij - D_i) Q_i.
- * Reads D and LSE*log2(e) from `workspace`, so attn_bwd_dq must have run on
- * the same inputs first (stream order); `lse` is validated but the kernel
- * uses the workspace copy.  Same arguments and rules as attn_bwd minus o
- * and dq.
+ * Backward stage 2 alone (the pages' fused dK+dV kernel): per key row,
+ * dV_j = sum_i P_ij dO_i and dK_j = scale * sum_i P_ij (dP_ij - D_i) Q_i,
+ * with P recomputed from the workspace's LSE*log2(e) and D (stage 1 must have
+ * run first, in stream order).  With the recommended workspace it also
+ * stores dS for stage 3.
  */
 attn_status_t attn_bwd_dkdv(attn_dtype_t dtype,
                             const void* q, const void* k, const void* v,
-                            const void* dout, const float* lse,
-                            void* dk, void* dv,
-                            const void* workspace, size_t workspace_bytes,
+                            const void* dout, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes,
                             int batch, int heads, int seq, int head_dim,
                             int causal, float scale, void* stream);
+
+/*
+ * Backward stage 3 alone (the pages' dQ kernel): dQ_i = scale * sum_j dS_ij K_j,
+ * as a GEMM over the stored dS with the recommended workspace (stage 2 must
+ * have run first with the same workspace), else recomputing P and dP per key
+ * tile from the workspace's LSE*log2(e) and D (stage 1 must have run).
+ */
+attn_status_t attn_bwd_dq(attn_dtype_t dtype,
+                          const void* q, const void* k, const void* v,
+                          const void* dout, void* dq,
+                          const void* workspace, size_t workspace_bytes,
+                          int batch, int heads, int seq, int head_dim,
+                          int causal, float scale, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status_t status);

@@ -43,7 +43,7 @@ def to_host(t) -> np.ndarray:
 
 
 def gpu_fwd_bwd(inp: dict, shape, dtype: str, causal: bool, scale: float, guard: int = 0,
-                fill=float("nan")):
+                fill=float("nan"), ws_mode: str = "full"):
     """Run attn_fwd then attn_bwd (fed the GPU's own O and LSE).
 
     Outputs are prefilled with `fill` so an unwritten element shows; with
@@ -64,8 +64,10 @@ def gpu_fwd_bwd(inp: dict, shape, dtype: str, causal: bool, scale: float, guard:
     for name in ("o", "dq", "dk", "dv"):
         bufs[name] = out((B, H, S, D), tdt)
     bufs["lse"] = out((B, H, S), torch.float32)
-    ws_bytes = afb.attn_bwd_workspace_size(afb.ATTN_BF16 if dtype == "bf16" else afb.ATTN_F32,
-                                           B, H, S, D, causal)
+    code = afb.ATTN_BF16 if dtype == "bf16" else afb.ATTN_F32
+    # "full": room for dS (dQ as a GEMM); "min": dQ recomputes the scores
+    wsf = afb.attn_bwd_workspace_size if ws_mode == "full" else afb.attn_bwd_workspace_size_min
+    ws_bytes = wsf(code, B, H, S, D, causal)
     ws = torch.full((ws_bytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
     t = {k_: v_[1] for k_, v_ in bufs.items()}
     afb.attn_fwd(dev["q"], dev["k"], dev["v"], t["o"], t["lse"], causal, scale)
@@ -95,10 +97,10 @@ def compare(host: dict, ref: dict, names=("o", "lse", "dq", "dk", "dv")) -> dict
 
 
 def run_case(shape, seed: int, dtype: str, causal: bool, scale: float, sigma_qkv=1.0,
-             sigma_do=1.0, guard: int = 0):
+             sigma_do=1.0, guard: int = 0, ws_mode: str = "full"):
     note(f"[gpu case] shape={shape} seed={seed} dtype={dtype} causal={causal} "
-         f"-> attn_fwd + attn_bwd")
+         f"workspace={ws_mode} -> attn_fwd + attn_bwd")
     inp = synth.make_inputs(shape, seed, dtype, sigma_qkv, sigma_do)
-    host, dev, outs = gpu_fwd_bwd(inp, shape, dtype, causal, scale, guard=guard)
+    host, dev, outs = gpu_fwd_bwd(inp, shape, dtype, causal, scale, guard=guard, ws_mode=ws_mode)
     ref = oracle_all(inp, causal, scale)
     return compare(host, ref), host, ref, inp, dev, outs

@@ -15,11 +15,12 @@ MIS = 0x10008           # 8-byte aligned only
 def test_library_loads_and_exports_header_symbols():
     L = afb.lib()
     declared = afb.declared_symbols()
-    assert set(declared) == {"attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv",
-                             "attn_bwd_workspace_size", "attn_status_string", "attn_version"}
+    assert set(declared) == {"attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dq",
+                             "attn_bwd_dkdv", "attn_bwd_workspace_size",
+                             "attn_bwd_workspace_size_min", "attn_status_string", "attn_version"}
     for name in declared:
         assert hasattr(L, name), name
-    assert afb.attn_version() == "0.1.0"
+    assert afb.attn_version() == "0.2.0"
     for code in range(5):
         assert afb.attn_status_string(code) not in ("", "unknown status")
     assert afb.attn_status_string(99) == "unknown status"
@@ -62,25 +63,39 @@ def test_bwd_validation():
     assert _bwd(wsb=2 * 8 * 4 - 1) == 3
     L = afb.lib()
     # split stages validate the same way
-    assert L.attn_bwd_dq(0, *[FAKE] * 7, FAKE, 16, 1, 1, 8, 64, 1, 0.1, None) == 3
-    assert L.attn_bwd_dkdv(0, *[FAKE] * 7, FAKE, 16, 1, 1, 8, 64, 1, 0.1, None) == 3
-    assert L.attn_bwd_dq(0, *[FAKE] * 7, None, 1 << 20, 1, 1, 8, 64, 1, 0.1, None) == 1
-    assert L.attn_bwd_dkdv(0, *[FAKE] * 6, None, FAKE, 1 << 20, 1, 1, 8, 64, 1, 0.1, None) == 1
+    assert L.attn_bwd_prep(0, FAKE, FAKE, FAKE, FAKE, 16, 1, 1, 8, 64, None) == 3
+    assert L.attn_bwd_prep(0, FAKE, None, FAKE, FAKE, 1 << 20, 1, 1, 8, 64, None) == 1
+    assert L.attn_bwd_prep(0, FAKE, FAKE, FAKE, FAKE, 1 << 20, 1, 1, 8, 48, None) == 2
+    assert L.attn_bwd_dq(0, *[FAKE] * 5, FAKE, 16, 1, 1, 8, 64, 1, 0.1, None) == 3
+    assert L.attn_bwd_dkdv(0, *[FAKE] * 6, FAKE, 16, 1, 1, 8, 64, 1, 0.1, None) == 3
+    assert L.attn_bwd_dq(0, *[FAKE] * 5, None, 1 << 20, 1, 1, 8, 64, 1, 0.1, None) == 1
+    assert L.attn_bwd_dkdv(0, *[FAKE] * 6, None, 1 << 20, 1, 1, 8, 64, 1, 0.1, None) == 1
+    assert L.attn_bwd_dkdv(0, *[FAKE] * 6, FAKE, 1 << 20, 1, 1, 8, 64, 1, -1.0, None) == 1
+
+
+def r256(b):
+    return (b + 255) // 256 * 256
 
 
 def test_workspace_size():
-    ws = afb.attn_bwd_workspace_size
-    # D and LSE*log2(e): two floats per query row, rounded up to 256 bytes
-    assert ws(0, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4
-    assert ws(1, 1, 1, 1, 64, False) == 256
-    assert ws(0, 32, 8, 197, 64, False) == ((2 * 32 * 8 * 197 * 4 + 255) // 256) * 256
-    assert ws(0, 1, 1, 8, 48, True) == 0 and ws(0, 0, 1, 8, 64, True) == 0
-    assert ws(5, 1, 1, 8, 64, True) == 0
+    wmin, wfull = afb.attn_bwd_workspace_size_min, afb.attn_bwd_workspace_size
+    # minimum: D and LSE*log2(e), two floats per query row, rounded up to 256 bytes
+    assert wmin(0, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4
+    assert wmin(1, 1, 1, 1, 64, False) == 256
+    assert wmin(0, 32, 8, 197, 64, False) == r256(2 * 32 * 8 * 197 * 4)
+    # recommended: plus dS [B*H][S][S rounded up to 128] in the element type
+    assert wfull(0, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4 + 8 * 12 * 512 * 512 * 4
+    assert wfull(1, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4 + 8 * 12 * 512 * 512 * 2
+    assert wfull(0, 32, 8, 197, 64, False) == r256(2 * 32 * 8 * 197 * 4) + r256(32 * 8 * 197 * 256 * 4)
+    for f in (wmin, wfull):
+        assert f(0, 1, 1, 8, 48, True) == 0 and f(0, 0, 1, 8, 64, True) == 0
+        assert f(5, 1, 1, 8, 64, True) == 0
     prev = 0
     for s in (1, 17, 64, 197, 512, 1024):
-        cur = ws(0, 2, 3, s, 64, True)
-        assert cur >= prev and cur >= 2 * 2 * 3 * s * 4 and cur % 256 == 0
-        prev = cur
+        lo, hi = wmin(0, 2, 3, s, 64, True), wfull(0, 2, 3, s, 64, True)
+        assert lo >= 2 * 2 * 3 * s * 4 and lo % 256 == 0 and hi % 256 == 0
+        assert hi >= lo + 2 * 3 * s * s * 4 and hi >= prev
+        prev = hi
 
 
 def test_no_cpu_fallback_when_library_missing(monkeypatch, tmp_path):

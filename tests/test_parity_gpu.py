@@ -10,37 +10,40 @@ from parity_util import TOL, compare, gpu_fwd_bwd, max_rel_err, note, run_case
 
 pytestmark = pytest.mark.gpu
 
-CFG_CASES = [(name, dt, seed) for name, cfg in synth.CONFIGS.items()
-             for dt in (("f32", "bf16") if name != "tiny" else ("f32", "bf16"))
-             for seed in (0, 1, 2)]
+CFG_CASES = [(name, dt, seed, ws) for name in synth.CONFIGS for dt in ("f32", "bf16")
+             for seed in (0, 1, 2) for ws in ("full", "min")]
 
 
-@pytest.mark.parametrize("name,dtype,seed", CFG_CASES)
-def test_config_parity(name, dtype, seed):
-    """The five measured workloads at full size, three seeds, both contracts."""
+@pytest.mark.parametrize("name,dtype,seed,ws", CFG_CASES)
+def test_config_parity(name, dtype, seed, ws):
+    """The five measured workloads at full size, three seeds, both contracts,
+    both backward paths (dS + GEMM with the recommended workspace; recompute
+    with the minimum one)."""
     cfg = synth.CONFIGS[name]
     errs, host, ref, *_ = run_case(cfg.shape, seed, dtype, cfg.causal, cfg.scale,
-                                   cfg.sigma_qkv, cfg.sigma_do)
-    note(f"  errors {name} {dtype} seed {seed}: " +
+                                   cfg.sigma_qkv, cfg.sigma_do, ws_mode=ws)
+    note(f"  errors {name} {dtype} seed {seed} ws {ws}: " +
          ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= TOL[dtype], (k, v)
-    # D written to the workspace by the dQ kernel
+    # D and LSE*log2(e) written to the workspace by the prep kernel
     assert max_rel_err(host["delta"], ref["delta"]) <= TOL[dtype]
+    assert max_rel_err(host["lse2"], ref["lse"] * np.log2(np.e)) <= TOL[dtype]
 
 
 MICRO = [(S, D, causal) for S in (1, 17, 33, 67, 130, 197) for D in (32, 64, 128)
          for causal in (True, False)]
 
 
+@pytest.mark.parametrize("ws", ["full", "min"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("S,D,causal", MICRO)
-def test_ragged_micro_shapes(S, D, causal, dtype):
+def test_ragged_micro_shapes(S, D, causal, dtype, ws):
     """Sequence lengths that end mid-tile, every head_dim, guard bands after
-    every output, NaN-prefilled outputs."""
+    every output, NaN-prefilled outputs and workspace, both backward paths."""
     shape = (2, 3, S, D)
     scale = 1.0 / np.sqrt(D)
-    errs, host, ref, inp, *_ = run_case(shape, 7, dtype, causal, scale, guard=64)
+    errs, host, ref, inp, *_ = run_case(shape, 7, dtype, causal, scale, guard=64, ws_mode=ws)
     if S == 1:
         # One key: P = 1, so O = V and dV = dO, while dQ and dK are exactly 0
         # (dS = P (dP - D) with dP = D); the oracle's float64 dQ, dK are
@@ -57,16 +60,17 @@ def test_ragged_micro_shapes(S, D, causal, dtype):
         assert host[name + "_guard_ok"], name
 
 
+@pytest.mark.parametrize("ws", ["full", "min"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_deterministic_and_inputs_untouched(dtype):
+def test_deterministic_and_inputs_untouched(dtype, ws):
     import torch
     shape = (2, 4, 197, 64)
     inp = synth.make_inputs(shape, 3, dtype)
-    note(f"[gpu case] determinism shape={shape} dtype={dtype}")
-    h1, dev, _ = gpu_fwd_bwd(inp, shape, dtype, True, 0.125)
+    note(f"[gpu case] determinism shape={shape} dtype={dtype} workspace={ws}")
+    h1, dev, _ = gpu_fwd_bwd(inp, shape, dtype, True, 0.125, ws_mode=ws)
     before = {k: v.clone() for k, v in dev.items()}
-    h2, dev2, _ = gpu_fwd_bwd(inp, shape, dtype, True, 0.125)
-    for n in ("o", "lse", "dq", "dk", "dv", "delta"):
+    h2, dev2, _ = gpu_fwd_bwd(inp, shape, dtype, True, 0.125, ws_mode=ws)
+    for n in ("o", "lse", "dq", "dk", "dv", "delta", "lse2"):
         assert np.array_equal(h1[n], h2[n]), n
     for n, t in dev.items():
         assert torch.equal(t, before[n]), n
@@ -118,22 +122,37 @@ def test_backward_alone_on_oracle_forward():
             assert max_rel_err(to_host(t), ref[n]) <= TOL[dtype], (dtype, n)
 
 
-def test_split_stages_match_fused_call():
-    """attn_bwd_dq then attn_bwd_dkdv gives bitwise the same as attn_bwd."""
+@pytest.mark.parametrize("ws", ["full", "min"])
+def test_split_stages_match_fused_call(ws):
+    """attn_bwd_prep, attn_bwd_dkdv, attn_bwd_dq in turn give bitwise the same
+    as attn_bwd."""
     import torch
     import attention_forward_backward_amd as afb
     shape = (1, 4, 130, 64)
     inp = synth.make_inputs(shape, 2, "f32")
-    note(f"[gpu case] split stages shape={shape}")
-    h, dev, outs = gpu_fwd_bwd(inp, shape, "f32", True, 0.125)
+    note(f"[gpu case] split stages shape={shape} workspace={ws}")
+    h, dev, outs = gpu_fwd_bwd(inp, shape, "f32", True, 0.125, ws_mode=ws)
     dq = torch.empty_like(outs["dq"])
     dk = torch.empty_like(outs["dk"])
     dv = torch.empty_like(outs["dv"])
-    ws = torch.empty(afb.attn_bwd_workspace_size(0, *shape, True), dtype=torch.uint8,
-                     device="cuda")
-    afb.attn_bwd_dq(dev["q"], dev["k"], dev["v"], outs["o"], dev["do"], outs["lse"], dq, ws,
-                    True, 0.125)
-    afb.attn_bwd_dkdv(dev["q"], dev["k"], dev["v"], dev["do"], outs["lse"], dk, dv, ws,
-                      True, 0.125)
+    wsf = afb.attn_bwd_workspace_size if ws == "full" else afb.attn_bwd_workspace_size_min
+    wsb = torch.empty(wsf(0, *shape, True), dtype=torch.uint8, device="cuda")
+    afb.attn_bwd_prep(outs["o"], dev["do"], outs["lse"], wsb)
+    afb.attn_bwd_dkdv(dev["q"], dev["k"], dev["v"], dev["do"], dk, dv, wsb, True, 0.125)
+    afb.attn_bwd_dq(dev["q"], dev["k"], dev["v"], dev["do"], dq, wsb, True, 0.125)
     torch.cuda.synchronize()
     assert torch.equal(dq, outs["dq"]) and torch.equal(dk, outs["dk"]) and torch.equal(dv, outs["dv"])
+
+
+def test_paths_agree():
+    """The dS + GEMM path and the recompute path give the same gradients to
+    within rounding (they sum the same terms in a different order)."""
+    shape = (2, 3, 197, 64)
+    for dtype in ("f32", "bf16"):
+        inp = synth.make_inputs(shape, 4, dtype)
+        note(f"[gpu case] paths agree shape={shape} dtype={dtype}")
+        hf, *_ = gpu_fwd_bwd(inp, shape, dtype, True, 0.125, ws_mode="full")
+        hm, *_ = gpu_fwd_bwd(inp, shape, dtype, True, 0.125, ws_mode="min")
+        for n in ("o", "lse", "dk", "dv"):
+            assert np.array_equal(hf[n], hm[n]), n
+        assert max_rel_err(hf["dq"], hm["dq"]) <= TOL[dtype]
