@@ -46,11 +46,11 @@ size_t ws_min_bytes(int batch, int heads, int seq) {
 // Row stride of the stored dS: seq rounded up to the largest key tile.
 int ds_stride(int seq) { return (seq + 127) / 128 * 128; }
 
-// Full workspace: the minimum plus dS [B*H][seq][ds_stride(seq)] in dtype.
+// Full workspace: the minimum plus dS^T [B*H][ds_stride(seq)]^2 in dtype.
 size_t ws_full_bytes(attn_dtype_t dtype, int batch, int heads, int seq) {
   const size_t esize = dtype == ATTN_BF16 ? 2 : 4;
-  return ws_min_bytes(batch, heads, seq) +
-         round256((size_t)batch * heads * seq * (size_t)ds_stride(seq) * esize);
+  const size_t sp = (size_t)ds_stride(seq);
+  return ws_min_bytes(batch, heads, seq) + round256((size_t)batch * heads * sp * sp * esize);
 }
 
 attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }

@@ -8,7 +8,7 @@
 //   dV_j  = sum_i P_ij dO_i
 //   dK_j  = scale * sum_i P_ij (dO_i.V_j - D_i) Q_i
 // with D_i and LSE_i*log2(e) read from the workspace (the prep kernel).  When
-// the workspace holds room for it, the kernel also stores dS (the values it
+// the workspace holds room for it, the kernel also stores dS^T (the values it
 // feeds its own dK product), from which dQ = scale * dS K is a plain GEMM.
 //
 // Work split: one workgroup per (key tile of 32*RB rows, batch*head).  Each
@@ -26,7 +26,7 @@
 namespace attn {
 
 template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(NW * 64, is_bf16<E>() ? 1 : ATTN_DKDV_MINW_F32) void bwd_dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
@@ -113,36 +113,46 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(
         }
       }
       // LSE*log2(e) and D of this lane's 16 queries: two runs of 8 at rho(0, h)
-      // and rho(8, h).
-      float lq[16], dq_[16];
+      // and rho(8, h), handled one run at a time to keep registers down.
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
+        const int off = qbl * 32 + 16 * u + 8 * h;
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2s + off);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2s + off + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(Ds + off);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(Ds + off + 4);
 #pragma unroll
-        for (int v4 = 0; v4 < 2; ++v4) {
-          const int off = qbl * 32 + 16 * u + 8 * h + 4 * v4;
-          const f32x4 a = *reinterpret_cast<const f32x4*>(lse2s + off);
-          const f32x4 b = *reinterpret_cast<const f32x4*>(Ds + off);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            lq[8 * u + 4 * v4 + e] = a[e];
-            dq_[8 * u + 4 * v4 + e] = b[e];
-          }
+        for (int t = 0; t < 8; ++t) {
+          const int r = 8 * u + t;
+          const float lq = t < 4 ? l0[t] : l1[t - 4];
+          const float dq = t < 4 ? d0[t] : d1[t - 4];
+          const float p = fast_exp2(fmaf(s[r], c, -lq));  // 0 where masked
+          s[r] = p;
+          dp[r] = p * (dp[r] - dq);
         }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(s[r], c, -lq[r]));  // 0 where masked
-        s[r] = p;
-        dp[r] = p * (dp[r] - dq_[r]);
       }
       if constexpr (WDS) {
-        // dS for the dQ GEMM: every entry of the block (exact zeros where
-        // masked and for keys past S), rows past S not stored.
-        T* dsq = dSout + (size_t)bh * S * SP + kj;
+        // dS^T for the dQ GEMM, row kj: this lane's 16 values are queries
+        // qq0 + 8h + {0..7} and qq0 + 16 + 8h + {0..7} (exact zeros where
+        // masked, for queries past S and for keys past S).
+        T* row = dSout + ((size_t)bh * SP + kj) * SP + qq0 + 8 * h;
         const bool kvalid = kj < S;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = qq0 + rho(r, h);
-          if (qi < S) dsq[(size_t)qi * SP] = kvalid ? (T)dp[r] : (T)0.f;
+        for (int u = 0; u < 2; ++u) {
+          if constexpr (is_bf16<E>()) {
+            bf16x8 o;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) o[t] = (__bf16)(kvalid ? dp[8 * u + t] : 0.f);
+            *reinterpret_cast<bf16x8*>(row + 16 * u) = o;
+          } else {
+#pragma unroll
+            for (int v4 = 0; v4 < 2; ++v4) {
+              f32x4 o;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = kvalid ? dp[8 * u + 4 * v4 + e] : 0.f;
+              *reinterpret_cast<f32x4*>(row + 16 * u + 4 * v4) = o;
+            }
+          }
         }
       }
       RegOperand<E> P, dS;

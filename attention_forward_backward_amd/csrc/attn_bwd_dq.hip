@@ -6,8 +6,8 @@
 // FlashGradKV in Section 7.3).  This file holds the two ways to form
 //   dQ_i = scale * sum_j dS_ij K_j,   dS_ij = P_ij (dO_i.V_j - D_i)
 // without atomics or partial sums in device memory:
-//  * bwd_dq_gemm_kernel: when the workspace can hold dS (B*H*S*S values,
-//    written by the dK+dV kernel), dQ is a causal-blocked GEMM dS K;
+//  * bwd_dq_gemm_kernel: when the workspace can hold dS (stored transposed,
+//    dS^T [key][query], by the dK+dV kernel), dQ is a causal-blocked GEMM;
 //  * bwd_dq_kernel: otherwise the dQ kernel recomputes P (from the LSE) and
 //    dP per key tile, as the pages' separate dQ kernel does; a workgroup
 //    owns its query rows outright.  The price is recomputing the two
@@ -155,25 +155,25 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   }
 }
 
-// dQ = scale * dS K from the stored dS.  One workgroup per (query tile of
+// dQ = scale * dS K from the stored dS^T.  One workgroup per (query tile of
 // 32*RB rows, batch*head); each 32-query block is owned by NSPLIT waves that
 // split the key blocks and sum their partials through LDS.  A staged tile is
-// the dS block [queries x 32*NSPLIT*KPW keys] and the matching K rows; the
-// dS rows are the register-operand (A) side in the same k-slot layout the
-// other kernels use, and K is read from LDS as in their second products.
+// the dS^T block [32*NSPLIT*KPW keys x queries] and the matching K rows; both
+// operands are read in the k-slot layout (keys on k) the second products of
+// the other kernels use.
 // Blocks with no visible key (above the causal diagonal, or past S) are
 // skipped; the dK+dV kernel wrote exact zeros for every masked entry and
 // every key past S inside the blocks it processed.
 template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
-    const typename E::T* __restrict__ K, const typename E::T* __restrict__ dS,
+    const typename E::T* __restrict__ K, const typename E::T* __restrict__ dST,
     typename E::T* __restrict__ dQ, int S, int SP, float scale) {
   using T = typename E::T;
   constexpr int RB = NW / NSPLIT;
   constexpr int BR = 32 * RB;
   constexpr int BK = 32 * NSPLIT * KPW;
   constexpr int NDB = D / 32;
-  using LDS_ = TileLoader<E, BK, BR, NW>;  // dS block: BR queries x BK keys
+  using LDS_ = TileLoader<E, BR, BK, NW>;  // dS^T block: BK keys x BR queries
   using LDK = TileLoader<E, D, BK, NW>;    // K rows:   BK keys x D
   constexpr int STAGE = LDS_::BYTES + LDK::BYTES;
   constexpr int NL = LDS_::NLOADS + LDK::NLOADS;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   const int bh = blockIdx.x;
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
   const T* k = K + (size_t)bh * S * D;
-  const T* ds = dS + (size_t)bh * S * SP;
+  const T* dst_ = dST + (size_t)bh * SP * SP;
   const int qw0 = qt * BR;         // first query of the workgroup
   const int q0 = qw0 + qb * 32;    // first query of this wave's block
   const bool wave_active = q0 < S;
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   const int nkt = (kend + BK - 1) / BK;
   auto issue = [&](int t) {
     char* st = smem + (t % NST) * STAGE;
-    LDS_::issue(st, ds, SP, qw0, S, t * BK, w, lane);
+    LDS_::issue(st, dst_, SP, t * BK, SP, qw0, w, lane);
     LDK::issue(st + LDS_::BYTES, k, D, t * BK, S, 0, w, lane);
   };
 #pragma unroll
@@ -220,8 +220,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
       const int kb = sp + NSPLIT * j;
       const int kk0 = kt * BK + kb * 32;
       if (!(kk0 < S && (!CAUSAL || kk0 <= q0 + 31))) continue;  // wave-uniform
-      RegOperand<E> R;
-      load_reg_operand<E, BK>(R, St, qb * 32 + n, kb * 32, h);
+      RegOperand<E> R;  // dS[q0 + n][keys]: k-slots from the dS^T rows
+      read_kslot_operand<E, BR>(R, St, kb * 32, qb * 32, lane);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
         acc[db] = second_tile<E, D, true>(R, Kt, kb * 32, db * 32, lane, acc[db]);

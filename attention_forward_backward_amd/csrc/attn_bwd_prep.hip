@@ -17,7 +17,7 @@
 
 namespace attn {
 
-template <class E, int D>
+template <class E, int D, int UNR>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __restrict__ O,
                                                         const typename E::T* __restrict__ dO,
                                                         const float* __restrict__ LSE,
@@ -28,28 +28,34 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __re
   constexpr int RPW = 64 / CPR;             // rows per wave step
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-  const int row = wave * RPW + lane / CPR;
   const int chunk = lane % CPR;
-  float acc = 0.f;
-  if (row < L) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + chunk * EPC);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + chunk * EPC);
+  u32x4 a[UNR], b[UNR];
+#pragma unroll
+  for (int i = 0; i < UNR; ++i) {  // all loads first, then the arithmetic
+    const int row = min((wave * UNR + i) * RPW + lane / CPR, L - 1);
+    a[i] = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + chunk * EPC);
+    b[i] = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + chunk * EPC);
+  }
+#pragma unroll
+  for (int i = 0; i < UNR; ++i) {
+    const int row = (wave * UNR + i) * RPW + lane / CPR;
+    float acc = 0.f;
     if constexpr (is_bf16<E>()) {
-      const bf16x8 x = __builtin_bit_cast(bf16x8, a), y = __builtin_bit_cast(bf16x8, b);
+      const bf16x8 x = __builtin_bit_cast(bf16x8, a[i]), y = __builtin_bit_cast(bf16x8, b[i]);
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc += (float)x[t] * (float)y[t];
     } else {
-      const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
+      const f32x4 x = __builtin_bit_cast(f32x4, a[i]), y = __builtin_bit_cast(f32x4, b[i]);
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc += x[t] * y[t];
     }
-  }
-  // sum over the CPR lanes of the row (aligned groups of CPR lanes)
+    // sum over the CPR lanes of the row (aligned groups of CPR lanes)
 #pragma unroll
-  for (int o = 1; o < CPR; o <<= 1) acc += __shfl_xor(acc, o);
-  if (row < L && chunk == 0) {
-    ws[row] = acc;
-    ws[(size_t)L + row] = LSE[row] * kLog2e;
+    for (int o = 1; o < CPR; o <<= 1) acc += __shfl_xor(acc, o);
+    if (row < L && chunk == 0) {
+      ws[row] = acc;
+      ws[(size_t)L + row] = LSE[row] * kLog2e;
+    }
   }
 }
 
@@ -57,12 +63,13 @@ template <class E, int D>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int EPC = 16 / (int)sizeof(typename E::T);
   constexpr int RPW = 64 / (D / EPC);
+  constexpr int UNR = 4;
   const int L = a.BH * a.S;
-  const int waves = (L + RPW - 1) / RPW;
+  const int waves = (L + RPW * UNR - 1) / (RPW * UNR);
   const int blocks = (waves + 3) / 4;
   using T = typename E::T;
-  hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3(blocks), dim3(256), 0, a.stream, (const T*)a.o,
-                     (const T*)a.dout, a.lse, a.delta, L);
+  hipLaunchKernelGGL((bwd_prep_kernel<E, D, UNR>), dim3(blocks), dim3(256), 0, a.stream,
+                     (const T*)a.o, (const T*)a.dout, a.lse, a.delta, L);
   return hipGetLastError();
 }
 

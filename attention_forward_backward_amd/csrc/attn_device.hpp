@@ -288,43 +288,23 @@ struct RegOperand<EBF16> {
   }
 };
 
-// Load a register operand in the k-slot layout of RegOperand (k-slot
-// (w, h) <-> column rho(w, h) for f32; (u, h, t) <-> column 16u + 8h + t for
-// bf16) from row `row` of a swizzled LDS tile with COLS columns, columns
-// col0 .. col0+31.
-template <class E, int COLS>
-__device__ inline void load_reg_operand(RegOperand<E>& R, const char* tile, int row, int col0,
-                                        int h) {
-  using TL = Tile<E, COLS>;
-  if constexpr (is_bf16<E>()) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      R.v[u] = *reinterpret_cast<const bf16x8*>(tile + TL::off(row, col0 + 16 * u + 8 * h));
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      // chunk of 4 columns starting at rho(4c, h) = 16*(c/2) + 8h + 4*(c%2)
-      const f32x4 x = *reinterpret_cast<const f32x4*>(tile + TL::off(row, col0 + rho(4 * c, h)));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) R.v[4 * c + e] = x[e];
-    }
-  }
-}
-
 // acc += product over the 32 logical rows row0 .. row0+31 of an LDS tile X:
 //   REG_IS_A = true : acc[m][n] += sum_k R[m = this lane's row][k] * X[k][col0 + n]
 //   REG_IS_A = false: acc[m][n] += sum_k X[k][col0 + m] * R[k][n = this lane's column]
-// R's k-slots are the lane's rho rows.  The X operand needs, per lane, the
-// k-slot rows of one column: f32 reads one element per MFMA; bf16 reads 8
-// consecutive rows of one column with two transposed LDS reads
+// R's k-slots are the lane's rho rows.  The X operand (read_kslot_operand)
+// needs, per lane, the k-slot rows of one column: f32 reads one element per
+// MFMA; bf16 reads 8 consecutive rows of one column with two transposed LDS
+// reads
 // (ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives
 // element e of the 8-byte row read of lane 4e + i/4, position i%4; so lanes
 // that read rows kbase + r/4, columns colbase + 4(r%4) .. +3 hand lane i
 // rows kbase .. kbase+3 of column colbase + i).
-template <class E, int D, bool REG_IS_A>
-__device__ inline f32x16 second_tile(const RegOperand<E>& R, const char* tile, int row0, int col0,
-                                     int lane, f32x16 acc) {
-  using TL = Tile<E, D>;
+template <class E, int COLS>
+__device__ inline void read_kslot_operand(RegOperand<E>& X, const char* tile, int row0, int col0,
+                                          int lane) {
+  // X in the k-slot layout of RegOperand: for this lane's column col0 + n,
+  // the k-slot rows row0 + rho(w, h) (f32) or row0 + 16u + 8h + t (bf16).
+  using TL = Tile<E, COLS>;
   const int h = lane >> 5, n = lane & 31;
   if constexpr (is_bf16<E>()) {
     const int g = lane >> 4, r = lane & 15;
@@ -339,16 +319,23 @@ __device__ inline f32x16 second_tile(const RegOperand<E>& R, const char* tile, i
             (__attribute__((address_space(3))) s16x4*)(tile + TL::off(row, col)));
       }
       const s16x8 all = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      const bf16x8 o = __builtin_bit_cast(bf16x8, all);
-      acc = REG_IS_A ? E::mma(R.v[u], o, acc) : E::mma(o, R.v[u], acc);
+      X.v[u] = __builtin_bit_cast(bf16x8, all);
     }
   } else {
 #pragma unroll
-    for (int w = 0; w < 16; ++w) {
-      const float o = *reinterpret_cast<const float*>(tile + TL::off(row0 + rho(w, h), col0 + n));
-      acc = REG_IS_A ? E::mma(R.v[w], o, acc) : E::mma(o, R.v[w], acc);
-    }
+    for (int w = 0; w < 16; ++w)
+      X.v[w] = *reinterpret_cast<const float*>(tile + TL::off(row0 + rho(w, h), col0 + n));
   }
+}
+
+template <class E, int D, bool REG_IS_A>
+__device__ inline f32x16 second_tile(const RegOperand<E>& R, const char* tile, int row0, int col0,
+                                     int lane, f32x16 acc) {
+  RegOperand<E> X;
+  read_kslot_operand<E, D>(X, tile, row0, col0, lane);
+  constexpr int NU = is_bf16<E>() ? 2 : 16;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc = REG_IS_A ? E::mma(R.v[u], X.v[u], acc) : E::mma(X.v[u], R.v[u], acc);
   return acc;
 }
 

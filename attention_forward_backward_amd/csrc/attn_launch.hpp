@@ -81,6 +81,9 @@
 #ifndef ATTN_DKDV_NST_BF16
 #define ATTN_DKDV_NST_BF16 3
 #endif
+#ifndef ATTN_DKDV_MINW_F32
+#define ATTN_DKDV_MINW_F32 1
+#endif
 
 namespace attn {
 
@@ -101,7 +104,7 @@ struct BwdArgs {
   const float* lse;
   void *dq, *dk, *dv;
   float* delta;  // workspace: D [B*H*S] f32, then LSE*log2(e) [B*H*S] f32
-  void* ds;      // workspace dS [B*H][S][SP] (dtype), or null: dQ recomputes
+  void* ds;      // workspace dS^T [B*H][SP][SP] (dtype), or null: dQ recomputes
   int SP;        // row stride of dS (S rounded up to the key tile)
   int BH, S, D;
   bool causal;

@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time for the oracle baseline sample")
+    p.add_argument("--workspace", choices=("full", "min"), default="full",
+                   help="backward workspace: full (dS stored, dQ as a GEMM) or min (dQ recomputes)")
     p.add_argument("--only-step", action="store_true",
                    help="time only the full step (used under a profiler)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -137,8 +139,9 @@ def main():
         o = torch.empty_like(q)
         lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
         dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-        ws = torch.empty(afb.attn_bwd_workspace_size(code, B, H, S, D, cfg.causal),
-                         dtype=torch.uint8, device="cuda")
+        wsf = afb.attn_bwd_workspace_size if args.workspace == "full" else \
+            afb.attn_bwd_workspace_size_min
+        ws = torch.empty(wsf(code, B, H, S, D, cfg.causal), dtype=torch.uint8, device="cuda")
         sc = cfg.scale
 
         def fwd():
@@ -232,7 +235,8 @@ def main():
         "config": {"workload": workload, "batch": B, "heads": H, "seq_len": S,
                    "head_dim": D, "causal": cfg.causal, "scale": cfg.scale,
                    "credited_gflop_per_step": flops["fwd_bwd"] / 1e9,
-                   "flop_convention": "14*D per visible pair, causal pairs S(S+1)/2"},
+                   "flop_convention": "14*D per visible pair, causal pairs S(S+1)/2",
+                   "backward_workspace": args.workspace},
         "kernel_sources": src_hash,
     }
     for key in ("roofline", "phases", "kernels", "step_frac_of_mfma_peak"):

@@ -83,9 +83,10 @@ attn_status_t attn_fwd(attn_dtype_t dtype,
  * Workspace of the backward, in bytes (pure host functions; 0 for arguments
  * attn_bwd would reject).  The workspace holds, for every query row,
  * D_i = sum_d dO_id O_id and LSE_i * log2(e) (two [B,H,S] float32 vectors,
- * rounded up to 256 bytes: the minimum), and -- only in the recommended
- * size -- dS [B*H][S][ceil(S/128)*128] in the element type, which lets dQ be
- * computed as one GEMM dS K instead of recomputing the scores.
+ * rounded up to 256 bytes: the minimum), and -- only in the full size --
+ * dS transposed, [B*H][Sp][Sp] with Sp = ceil(S/128)*128, in the element
+ * type, which lets dQ be computed as one GEMM dS K instead of recomputing the
+ * scores.
  *   attn_bwd_workspace_size      recommended size (the dS path)
  *   attn_bwd_workspace_size_min  minimum size (dQ recomputes P and dP)
  * The backward takes the dS path iff workspace_bytes >= the recommended

@@ -83,10 +83,10 @@ def test_workspace_size():
     assert wmin(0, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4
     assert wmin(1, 1, 1, 1, 64, False) == 256
     assert wmin(0, 32, 8, 197, 64, False) == r256(2 * 32 * 8 * 197 * 4)
-    # recommended: plus dS [B*H][S][S rounded up to 128] in the element type
+    # full: plus dS^T [B*H][Sp][Sp] (Sp = S rounded up to 128) in the element type
     assert wfull(0, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4 + 8 * 12 * 512 * 512 * 4
     assert wfull(1, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4 + 8 * 12 * 512 * 512 * 2
-    assert wfull(0, 32, 8, 197, 64, False) == r256(2 * 32 * 8 * 197 * 4) + r256(32 * 8 * 197 * 256 * 4)
+    assert wfull(0, 32, 8, 197, 64, False) == r256(2 * 32 * 8 * 197 * 4) + r256(32 * 8 * 256 * 256 * 4)
     for f in (wmin, wfull):
         assert f(0, 1, 1, 8, 48, True) == 0 and f(0, 0, 1, 8, 64, True) == 0
         assert f(5, 1, 1, 8, 64, True) == 0
