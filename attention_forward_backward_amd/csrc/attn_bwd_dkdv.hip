@@ -84,8 +84,14 @@ __global__ __launch_bounds__(NW * 64, is_bf16<E>() ? 1 : ATTN_DKDV_MINW_F32) voi
   for (int s = 0; s < NST - 1; ++s)
     if (qt0 + s < nqt) issue(qt0 + s);
 
+  // dS^T store instructions per stored block: 16 values of T in 16-byte stores
+  constexpr int NSTORE = WDS ? 16 * (int)sizeof(T) / 16 : 0;
+  static_assert(KPW <= 2, "wait_tiles counts at most two stored blocks");
+  int stored = 0;  // blocks whose dS^T this wave stored in the previous iteration
   for (int qt = qt0; qt < nqt; ++qt) {
-    wait_tiles<NL>(min(NST - 2, nqt - 1 - qt));
+    // Those stores were issued after the loads of every tile still in flight.
+    wait_tiles<NL, NSTORE>(min(NST - 2, nqt - 1 - qt), stored);
+    stored = 0;
     lds_barrier();  // tile qt is in LDS; every wave is done with tile qt-1
     if (qt + NST - 1 < nqt) issue(qt + NST - 1);
     if (!wave_active) continue;
@@ -132,6 +138,7 @@ __global__ __launch_bounds__(NW * 64, is_bf16<E>() ? 1 : ATTN_DKDV_MINW_F32) voi
         }
       }
       if constexpr (WDS) {
+        ++stored;
         // dS^T for the dQ GEMM, row kj: this lane's 16 values are queries
         // qq0 + 8h + {0..7} and qq0 + 16 + 8h + {0..7} (exact zeros where
         // masked, for queries past S and for keys past S).

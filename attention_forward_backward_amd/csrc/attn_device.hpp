@@ -157,12 +157,25 @@ __device__ inline void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 // Wait for the oldest staged tile when `newer` younger tiles (NL loads each)
-// may stay in flight.
-template <int NL>
-__device__ inline void wait_tiles(int newer) {
-  if (newer >= 2) wait_vmem<2 * NL>();
-  else if (newer == 1) wait_vmem<NL>();
-  else wait_vmem<0>();
+// may stay in flight, and after them `blocks` groups of NS stores each
+// (vmcnt counts stores as well as loads, and vector memory operations retire
+// in issue order, so the stores issued after the younger tiles' loads are
+// the ones that may stay outstanding).
+template <int NL, int NS = 0>
+__device__ inline void wait_tiles(int newer, int blocks = 0) {
+  if (blocks >= 2) {
+    if (newer >= 2) wait_vmem<2 * NL + 2 * NS>();
+    else if (newer == 1) wait_vmem<NL + 2 * NS>();
+    else wait_vmem<2 * NS>();
+  } else if (blocks == 1) {
+    if (newer >= 2) wait_vmem<2 * NL + NS>();
+    else if (newer == 1) wait_vmem<NL + NS>();
+    else wait_vmem<NS>();
+  } else {
+    if (newer >= 2) wait_vmem<2 * NL>();
+    else if (newer == 1) wait_vmem<NL>();
+    else wait_vmem<0>();
+  }
 }
 // Workgroup barrier that orders LDS accesses without waiting for pending
 // global loads (those are waited for explicitly with wait_vmem).
