@@ -47,7 +47,8 @@ __global__ __launch_bounds__(NW * 64, is_bf16<E>() ? 1 : ATTN_DKDV_MINW_F32) voi
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int lane = tid & 63, h = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int kbk = w / NSPLIT, sp = w % NSPLIT;
   const int bh = blockIdx.x;
   const int kt = blockIdx.y;  // causal: tile 0 has the most queries, dispatched first
@@ -75,9 +76,10 @@ __global__ __launch_bounds__(NW * 64, is_bf16<E>() ? 1 : ATTN_DKDV_MINW_F32) voi
 
   const int nqt = (S + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
+  const unsigned lo = LD::lane_offset(w, lane);
   auto issue = [&](int qt) {
     char* st = smem + ((qt - qt0) % NST) * STAGE;
-    LD::issue(st, q, dout, qt * BQ, S, w, lane);
+    LD::issue(st, q, dout, qt * BQ, S, w, lane, lo);
     issue_stats<BQ, NW>(reinterpret_cast<float*>(st + LD::BYTES), lse2g, dlt, qt * BQ, S, w, lane);
   };
 #pragma unroll

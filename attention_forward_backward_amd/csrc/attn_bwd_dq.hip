@@ -49,7 +49,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int lane = tid & 63, h = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int qb = w / NSPLIT, sp = w % NSPLIT;
   const int bh = blockIdx.x;
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
@@ -77,15 +78,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   const int kend = CAUSAL ? min(S, qt * BR + BR) : S;
   const int nkt = (kend + BK - 1) / BK;
 
+  const unsigned lo = LD::lane_offset(w, lane);
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < nkt) LD::issue(smem + s * LD::BYTES, k, v, s * BK, S, w, lane);
+    if (s < nkt) LD::issue(smem + s * LD::BYTES, k, v, s * BK, S, w, lane, lo);
 
   for (int kt = 0; kt < nkt; ++kt) {
     wait_tiles<LD::NLOADS>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1
     if (kt + NST - 1 < nkt)
-      LD::issue(smem + ((kt + NST - 1) % NST) * LD::BYTES, k, v, (kt + NST - 1) * BK, S, w, lane);
+      LD::issue(smem + ((kt + NST - 1) % NST) * LD::BYTES, k, v, (kt + NST - 1) * BK, S, w, lane, lo);
     if (!wave_active) continue;
     const char* Kt = smem + (kt % NST) * LD::BYTES;
     const char* Vt = Kt + TILEB;
@@ -183,7 +185,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int lane = tid & 63, h = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int qb = w / NSPLIT, sp = w % NSPLIT;
   const int bh = blockIdx.x;
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
@@ -199,10 +202,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
 
   const int kend = CAUSAL ? min(S, qw0 + BR) : S;
   const int nkt = (kend + BK - 1) / BK;
+  const unsigned los = LDS_::lane_offset(SP, w, lane), lok = LDK::lane_offset(D, w, lane);
   auto issue = [&](int t) {
     char* st = smem + (t % NST) * STAGE;
-    LDS_::issue(st, dst_, SP, t * BK, SP, qw0, w, lane);
-    LDK::issue(st + LDS_::BYTES, k, D, t * BK, S, 0, w, lane);
+    LDS_::issue(st, dst_, SP, t * BK, SP, qw0, w, lane, los);
+    LDK::issue(st + LDS_::BYTES, k, D, t * BK, S, 0, w, lane, lok);
   };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)

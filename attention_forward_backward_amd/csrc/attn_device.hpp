@@ -187,6 +187,12 @@ __device__ inline void lds_barrier() {
 // row-major [S x D] matrices (src0, src1) into two consecutive swizzled
 // tiles at `stage`.  Rows past S read row S-1 (finite; the caller masks
 // them).  Each wave issues NLOADS instructions, each filling 1 KiB of LDS.
+//
+// A wave's consecutive loads are RS rows apart.  The swizzle repeats every
+// 16 rows, so when RS and BT are multiples of 16 every load of a wave has the
+// same lane offset from its (wave-uniform) first row: lane_offset() is then
+// computed once per kernel and a whole tile costs one address add per load.
+// The clamped per-lane form remains for tiles that cross S.
 template <class E, int D, int BT, int NW>
 struct StageLoader {
   using T = typename E::T;
@@ -194,12 +200,32 @@ struct StageLoader {
   static constexpr int CH_PER = BT * TL::CPR;            // chunks per matrix
   static constexpr int NLOADS = 2 * CH_PER / (NW * 64);  // per wave
   static constexpr int BYTES = 2 * BT * TL::ROWB;
+  static constexpr int RPS = 64 / TL::CPR;               // rows per 1 KiB slot
+  static constexpr int RS = NW * RPS;                    // rows between a wave's loads
+  static constexpr bool FAST = RS % 16 == 0 && BT % 16 == 0;
   static_assert((2 * CH_PER) % (NW * 64) == 0, "tile must split into whole wave loads");
+  static_assert(CH_PER % 64 == 0, "a 1 KiB slot lies in one matrix");
+  // Element offset of this lane's chunk from the first row of the wave's
+  // first load (valid for every load of the wave when FAST).
+  __device__ static inline unsigned lane_offset(int w, int lane) {
+    const int row = w * RPS + lane / TL::CPR;
+    return (unsigned)(row * D + ((lane % TL::CPR) ^ TL::swz(row)) * TL::EPC);
+  }
   __device__ static inline void issue(char* stage, const T* src0, const T* src1, int row0, int S,
-                                      int w, int lane) {
+                                      int w, int lane, unsigned lo) {
+    if (FAST && row0 + BT <= S) {
+#pragma unroll
+      for (int i = 0; i < NLOADS; ++i) {
+        const int slot = i * NW + w;           // 1 KiB slot of the stage (wave-uniform)
+        const int mat = slot * 64 / CH_PER;    // wave-uniform
+        const T* base = (mat == 0 ? src0 : src1) + (size_t)(row0 + i * RS - mat * BT) * D;
+        __builtin_amdgcn_global_load_lds(base + lo, stage + slot * 1024, 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NLOADS; ++i) {
-      const int slot = i * NW + w;         // 1 KiB slot of the stage (wave-uniform)
+      const int slot = i * NW + w;
       const int chunk = slot * 64 + lane;  // physical chunk in the stage
       const int mat = chunk / CH_PER;
       const int pc = chunk - mat * CH_PER;
@@ -213,7 +239,8 @@ struct StageLoader {
 
 // The direct loads of one swizzled tile of a single row-major matrix:
 // rows row0 .. row0+BT-1 (rows past `rows` read row rows-1), columns
-// col0 .. col0+COLS-1 of a matrix with row stride `ld` elements.
+// col0 .. col0+COLS-1 of a matrix with row stride `ld` elements.  Same
+// uniform-step fast path as StageLoader.
 template <class E, int COLS, int BT, int NW>
 struct TileLoader {
   using T = typename E::T;
@@ -221,9 +248,25 @@ struct TileLoader {
   static constexpr int CH = BT * TL::CPR;        // chunks in the tile
   static constexpr int NLOADS = CH / (NW * 64);  // per wave
   static constexpr int BYTES = BT * TL::ROWB;
+  static constexpr int RPS = 64 / TL::CPR;
+  static constexpr int RS = NW * RPS;
+  static constexpr bool FAST = RS % 16 == 0;
   static_assert(CH % (NW * 64) == 0, "tile must split into whole wave loads");
+  __device__ static inline unsigned lane_offset(size_t ld, int w, int lane) {
+    const int row = w * RPS + lane / TL::CPR;
+    return (unsigned)((size_t)row * ld + ((lane % TL::CPR) ^ TL::swz(row)) * TL::EPC);
+  }
   __device__ static inline void issue(char* dst, const T* src, size_t ld, int row0, int rows,
-                                      int col0, int w, int lane) {
+                                      int col0, int w, int lane, unsigned lo) {
+    if (FAST && row0 + BT <= rows) {
+#pragma unroll
+      for (int i = 0; i < NLOADS; ++i) {
+        const int slot = i * NW + w;
+        const T* base = src + (size_t)(row0 + i * RS) * ld + col0;
+        __builtin_amdgcn_global_load_lds(base + lo, dst + slot * 1024, 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NLOADS; ++i) {
       const int slot = i * NW + w;
