@@ -30,6 +30,12 @@ HIP_FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
+# Per-source additions.  The f32 dK+dV kernel (D <= 64) is asked to fit two
+# waves per SIMD (256 registers); LLVM's ILP-first scheduler is the one that
+# meets that bound without spilling, so its source uses it.
+FILE_FLAGS = {
+    "attn_bwd_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
 
 
 def hipcc() -> str:
@@ -41,7 +47,8 @@ def hipcc() -> str:
 
 def _compile(src: str, extra: list[str]) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIP_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src,
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

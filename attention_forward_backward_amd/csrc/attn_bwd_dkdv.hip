@@ -26,7 +26,7 @@
 namespace attn {
 
 template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS>
-__global__ __launch_bounds__(NW * 64, is_bf16<E>() ? 1 : ATTN_DKDV_MINW_F32) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_F32 : 1) void bwd_dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,

@@ -183,6 +183,16 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Address of a direct load: a wave-uniform base plus this lane's byte
+// offset.  The base is passed through an empty asm statement so the
+// compiler keeps it in SGPRs and adds the one lane offset per load, instead
+// of hoisting base+offset pairs into loop-invariant VGPRs.
+__device__ inline const void* lane_addr(const void* base, unsigned lane_bytes) {
+  unsigned long long b = reinterpret_cast<unsigned long long>(base);
+  asm volatile("" : "+s"(b));
+  return reinterpret_cast<const void*>(b + lane_bytes);
+}
+
 // The direct loads of one staged tile: rows row0 .. row0+BT-1 of two
 // row-major [S x D] matrices (src0, src1) into two consecutive swizzled
 // tiles at `stage`.  Rows past S read row S-1 (finite; the caller masks
@@ -205,11 +215,11 @@ struct StageLoader {
   static constexpr bool FAST = RS % 16 == 0 && BT % 16 == 0;
   static_assert((2 * CH_PER) % (NW * 64) == 0, "tile must split into whole wave loads");
   static_assert(CH_PER % 64 == 0, "a 1 KiB slot lies in one matrix");
-  // Element offset of this lane's chunk from the first row of the wave's
-  // first load (valid for every load of the wave when FAST).
+  // Byte offset of this lane's chunk from the first row of the wave's first
+  // load (valid for every load of the wave when FAST).
   __device__ static inline unsigned lane_offset(int w, int lane) {
     const int row = w * RPS + lane / TL::CPR;
-    return (unsigned)(row * D + ((lane % TL::CPR) ^ TL::swz(row)) * TL::EPC);
+    return (unsigned)((row * D + ((lane % TL::CPR) ^ TL::swz(row)) * TL::EPC) * sizeof(T));
   }
   __device__ static inline void issue(char* stage, const T* src0, const T* src1, int row0, int S,
                                       int w, int lane, unsigned lo) {
@@ -219,7 +229,7 @@ struct StageLoader {
         const int slot = i * NW + w;           // 1 KiB slot of the stage (wave-uniform)
         const int mat = slot * 64 / CH_PER;    // wave-uniform
         const T* base = (mat == 0 ? src0 : src1) + (size_t)(row0 + i * RS - mat * BT) * D;
-        __builtin_amdgcn_global_load_lds(base + lo, stage + slot * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(lane_addr(base, lo), stage + slot * 1024, 16, 0, 0);
       }
       return;
     }
@@ -254,7 +264,7 @@ struct TileLoader {
   static_assert(CH % (NW * 64) == 0, "tile must split into whole wave loads");
   __device__ static inline unsigned lane_offset(size_t ld, int w, int lane) {
     const int row = w * RPS + lane / TL::CPR;
-    return (unsigned)((size_t)row * ld + ((lane % TL::CPR) ^ TL::swz(row)) * TL::EPC);
+    return (unsigned)(((size_t)row * ld + ((lane % TL::CPR) ^ TL::swz(row)) * TL::EPC) * sizeof(T));
   }
   __device__ static inline void issue(char* dst, const T* src, size_t ld, int row0, int rows,
                                       int col0, int w, int lane, unsigned lo) {
@@ -263,7 +273,7 @@ struct TileLoader {
       for (int i = 0; i < NLOADS; ++i) {
         const int slot = i * NW + w;
         const T* base = src + (size_t)(row0 + i * RS) * ld + col0;
-        __builtin_amdgcn_global_load_lds(base + lo, dst + slot * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(lane_addr(base, lo), dst + slot * 1024, 16, 0, 0);
       }
       return;
     }

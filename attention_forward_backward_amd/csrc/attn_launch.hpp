@@ -81,8 +81,10 @@
 #ifndef ATTN_DKDV_NST_BF16
 #define ATTN_DKDV_NST_BF16 3
 #endif
+// Workgroups per CU the f32 dK+dV kernel (D <= 64) must fit: 2 holds its
+// registers to 256, so two of its single-wave-per-SIMD workgroups share a CU.
 #ifndef ATTN_DKDV_MINW_F32
-#define ATTN_DKDV_MINW_F32 1
+#define ATTN_DKDV_MINW_F32 2
 #endif
 
 namespace attn {
