@@ -11,15 +11,23 @@
 // the workspace holds room for it, the kernel also stores dS^T (the values it
 // feeds its own dK product), from which dQ = scale * dS K is a plain GEMM.
 //
-// Work split: one workgroup per (key tile of 32*RB rows, batch*head).  Each
-// 32-key block is owned by NSPLIT waves that keep its K and V rows in
-// registers, split the query blocks between them, accumulate dK and dV in
-// registers and sum their partials through LDS at the end.  Query tiles (Q,
-// dO, and the queries' LSE and D) stream through an NST-stage ring of LDS
-// tiles filled by direct global->LDS loads issued NST-1 tiles ahead.  Per
-// 32-query block a wave forms S = Q K^T and dP = dO V^T (queries x keys; each
-// lane holds one key), then P^T and dS^T are the register A operands of
-// dV (keys x d) += P^T dO and dK += dS^T Q, with dO and Q read back from LDS.
+// Work split (persistent): an item is (key tile of BKV = 32*RB rows,
+// batch*head), numbered in order of decreasing causal work; the launch puts
+// about one workgroup on every resident slot and each walks its items in the
+// static snake order (snake_item).  Each 32-key block of an item is owned by
+// NSPLIT waves that keep its K and V rows in registers, split the query
+// blocks between them, accumulate dK and dV in registers and sum their
+// partials through LDS when the item ends.
+//
+// Tiles stream through an NST-stage ring of LDS tiles filled by direct
+// global->LDS loads issued NST-1 tiles ahead.  The stream runs across item
+// boundaries: per item, a header tile (the item's K and V rows, read into
+// registers from LDS) and then its query tiles (Q, dO, and the queries' LSE
+// and D), so the next item's rows and first queries load while the current
+// item finishes.  Per 32-query block a wave forms S = Q K^T and dP = dO V^T
+// (queries x keys; each lane holds one key), then P^T and dS^T are the
+// register A operands of dV (keys x d) += P^T dO and dK += dS^T Q, with dO
+// and Q read back from LDS.
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
 
@@ -30,195 +38,260 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
-    typename E::T* __restrict__ dSout, int SP, int S, int L, float c, float scale) {
+    typename E::T* __restrict__ dSout, int SP, int S, int L, float c, float scale, int BH,
+    int nitems) {
   using T = typename E::T;
   using TL = Tile<E, D>;
-  constexpr int RB = NW / NSPLIT;        // 32-key blocks per workgroup
-  constexpr int BKV = 32 * RB;           // keys per workgroup
+  constexpr int RB = NW / NSPLIT;        // 32-key blocks per item
+  constexpr int BKV = 32 * RB;           // keys per item
   constexpr int BQ = 32 * NSPLIT * KPW;  // queries per staged tile
   constexpr int NDB = D / 32;
   using LD = StageLoader<E, D, BQ, NW>;
   constexpr int TILEB = BQ * TL::ROWB;                            // dO follows Q in a stage
   constexpr int STAGE = (LD::BYTES + 2 * BQ * 4 + 1023) / 1024 * 1024;  // + LSE*log2e, D
   constexpr int NL = LD::NLOADS + 1;                              // loads per wave per tile
-  constexpr int COMB = RB * (NSPLIT - 1) * 32 * NDB * 64 * 4;
-  constexpr int SMEM = NST * STAGE > COMB ? NST * STAGE : COMB;
+  // Partials of the NSPLIT-1 helper waves of every key block, one matrix
+  // (dK or dV): summed through the stage just consumed, in one pass when it
+  // holds both matrices, else in two.
+  constexpr int PART = RB * (NSPLIT - 1) * 16 * NDB * 64 * 4;
+  constexpr int NPASS = 2 * PART <= STAGE ? 1 : 2;
+  static_assert(PART * (3 - NPASS) <= STAGE, "split partials must fit one stage");
+  static_assert(BKV == BQ, "a K/V header tile has the shape of a query tile");
   static_assert(NW % NSPLIT == 0 && NST >= 2 && NST <= 4, "launch shape");
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int kbk = w / NSPLIT, sp = w % NSPLIT;
-  const int bh = blockIdx.x;
-  const int kt = blockIdx.y;  // causal: tile 0 has the most queries, dispatched first
-  const size_t base = (size_t)bh * S * D;
-  const T* q = Q + base;
-  const T* dout = dO + base;
-  const float* dlt = Dws + (size_t)bh * S;
-  const float* lse2g = Dws + (size_t)L + (size_t)bh * S;
-
-  const int k0 = kt * BKV + kbk * 32;
-  const int kj = k0 + n;
-  const bool wave_active = k0 < S;
-  const size_t krow = base + (size_t)min(kj, S - 1) * D + h * (D / 2);
-
-  RowFrag<E, D> kf, vf;
-  load_row_frag<E, D>(kf, K + krow, kj < S);
-  load_row_frag<E, D>(vf, V + krow, kj < S);
-
-  f32x16 dkacc[NDB], dvacc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) {
-    dkacc[i] = zero16();
-    dvacc[i] = zero16();
-  }
-
+  const int g = blockIdx.x, G = gridDim.x;
   const int nqt = (S + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
-  const unsigned lo = LD::lane_offset(w, lane);
-  auto issue = [&](int qt) {
-    char* st = smem + ((qt - qt0) % NST) * STAGE;
-    LD::issue(st, q, dout, qt * BQ, S, w, lane, lo);
-    issue_stats<BQ, NW>(reinterpret_cast<float*>(st + LD::BYTES), lse2g, dlt, qt * BQ, S, w, lane);
+  const unsigned lane_off = LD::lane_offset(w, lane);
+  auto first_qt = [&](int kt) { return CAUSAL ? (kt * BKV) / BQ : 0; };
+
+  // Loader cursor: the next stream tile to issue (lqt < 0: the header of
+  // item lit, whose K and V rows it stages; else query tile lqt).  Every
+  // stream tile is NL loads per wave (the header also loads statistics it
+  // does not use, to keep that count).
+  int lr = 0, lit = snake_item(0, g, G), lqt = -1, lkt = lit / BH;
+  size_t lho = (size_t)(lit % BH) * S;  // first row of the item's head
+  int nissued = 0;
+  auto issue_next = [&]() {
+    if (lit >= nitems) return;
+    char* st = smem + (nissued % NST) * STAGE;
+    const bool head = lqt < 0;
+    const int row0 = head ? lkt * BKV : lqt * BQ;
+    LD::issue(st, (head ? K : Q) + lho * D, (head ? V : dO) + lho * D, row0, S, w, lane, lane_off);
+    issue_stats<BQ, NW>(reinterpret_cast<float*>(st + LD::BYTES), Dws + L + lho, Dws + lho,
+                        head ? 0 : row0, S, w, lane);
+    ++nissued;
+    if (head) {
+      lqt = first_qt(lkt);
+    } else if (++lqt == nqt) {
+      lit = snake_item(++lr, g, G);
+      lqt = -1;
+      lkt = lit / BH;
+      lho = (size_t)(lit % BH) * S;
+    }
   };
+
+  if (snake_item(0, g, G) >= nitems) return;  // (the launch never makes more workgroups than items)
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (qt0 + s < nqt) issue(qt0 + s);
+  for (int i = 0; i < NST - 1; ++i) issue_next();
 
   // dS^T store instructions per stored block: 16 values of T in 16-byte stores
   constexpr int NSTORE = WDS ? 16 * (int)sizeof(T) / 16 : 0;
-  static_assert(KPW <= 2, "wait_tiles counts at most two stored blocks");
-  int stored = 0;  // blocks whose dS^T this wave stored in the previous iteration
-  for (int qt = qt0; qt < nqt; ++qt) {
-    // Those stores were issued after the loads of every tile still in flight.
-    wait_tiles<NL, NSTORE>(min(NST - 2, nqt - 1 - qt), stored);
+  f32x16 dkacc[NDB], dvacc[NDB];
+  RowFrag<E, D> kf, vf;
+  // Sum the NSPLIT partial dK, dV of each key block of the item through
+  // `buf` (an LDS stage no load targets), then store dK and dV.
+  // Returns the store instructions counted for the tile waits: only rows that
+  // every lane writes, so the count never exceeds the instructions issued.
+  auto merge_store = [&](char* buf, int bh, int k0, bool active) -> int {
+    if constexpr (NSPLIT > 1) {
+      float* cb = reinterpret_cast<float*>(buf);
+      constexpr int PER = (NPASS == 1 ? 2 : 1) * 16 * NDB;  // floats per lane per helper wave
+      constexpr int VOFF = NPASS == 1 ? 16 * NDB : 0;       // dV after dK in one pass
+#pragma unroll
+      for (int pass = 0; pass < NPASS; ++pass) {
+        const bool withk = NPASS == 1 || pass == 0, withv = NPASS == 1 || pass == 1;
+        lds_barrier();  // every wave is done reading the stage (or the previous pass)
+        if (sp != 0 && active) {
+          float* dst = cb + ((kbk * (NSPLIT - 1) + sp - 1) * PER) * 64 + lane;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              if (withk) dst[(db * 16 + r) * 64] = dkacc[db][r];
+              if (withv) dst[(VOFF + db * 16 + r) * 64] = dvacc[db][r];
+            }
+        }
+        lds_barrier();
+        if (sp == 0 && active) {
+#pragma unroll
+          for (int p = 0; p < NSPLIT - 1; ++p) {
+            const float* src = cb + ((kbk * (NSPLIT - 1) + p) * PER) * 64 + lane;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                if (withk) dkacc[db][r] += src[(db * 16 + r) * 64];
+                if (withv) dvacc[db][r] += src[(VOFF + db * 16 + r) * 64];
+              }
+          }
+        }
+      }
+    }
+    int nstores = 0;
+    if (sp == 0 && active) {
+      // element r of acc[db]: row k0 + out_row(r, h), column db*32 + n
+      T* dk = dK + (size_t)bh * S * D;
+      T* dv = dV + (size_t)bh * S * D;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = k0 + out_row(r, h);
+        if (row < S) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            dk[(size_t)row * D + db * 32 + n] = (T)(dkacc[db][r] * scale);
+            dv[(size_t)row * D + db * 32 + n] = (T)dvacc[db][r];
+          }
+        }
+        if (k0 + out_row(r, 1) < S) nstores += 2 * NDB;
+      }
+    }
+    return nstores;
+  };
+
+  // Vector-memory operations this wave issued in the previous iteration after
+  // the loads of every tile still in flight: dS^T stores (NSTORE per stored
+  // block) and dK, dV stores.  A tile waits until no more than those and the
+  // younger tiles' loads are pending (vmcnt counts stores too, and vector
+  // memory retires in issue order).
+  int stored = 0, estores = 0;
+  int pos = 0;  // stream position of the tile being consumed
+  for (int cr = 0;; ++cr) {
+    const int cit = snake_item(cr, g, G);
+    if (cit >= nitems) break;
+    const int kt = cit / BH, bh = cit % BH;
+    const int k0 = kt * BKV + kbk * 32;
+    const int kj = k0 + n;
+    const bool wave_active = k0 < S;
+
+    // Header: this wave's K, V rows into registers.
+    wait_vmem_dyn(NL * (nissued - pos - 1) + NSTORE * stored + estores);
     stored = 0;
-    lds_barrier();  // tile qt is in LDS; every wave is done with tile qt-1
-    if (qt + NST - 1 < nqt) issue(qt + NST - 1);
-    if (!wave_active) continue;
-    const char* Qt = smem + ((qt - qt0) % NST) * STAGE;
-    const char* dOt = Qt + TILEB;
-    const float* lse2s = reinterpret_cast<const float*>(Qt + LD::BYTES);
-    const float* Ds = lse2s + BQ;
+    estores = 0;
+    lds_barrier();  // the header is in LDS; every wave is done with the tile before
+    issue_next();
+    __builtin_amdgcn_sched_barrier(0);  // the counts above assume this issue order
+    const char* hst = smem + (pos % NST) * STAGE;
+    load_row_frag_lds<E, D>(kf, hst, kbk * 32 + n, h, kj < S);
+    load_row_frag_lds<E, D>(vf, hst + TILEB, kbk * 32 + n, h, kj < S);
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+      dkacc[i] = zero16();
+      dvacc[i] = zero16();
+    }
+    ++pos;
+
+    for (int qt = first_qt(kt); qt < nqt; ++qt, ++pos) {
+      if (estores == 0) wait_tiles<NL, NSTORE>(nissued - pos - 1, stored);
+      else wait_vmem_dyn(NL * (nissued - pos - 1) + NSTORE * stored + estores);
+      stored = 0;
+      estores = 0;
+      lds_barrier();  // tile pos is in LDS; every wave is done with the one before
+      issue_next();
+      __builtin_amdgcn_sched_barrier(0);
+      if (!wave_active) continue;
+      const char* Qt = smem + (pos % NST) * STAGE;
+      const char* dOt = Qt + TILEB;
+      const float* lse2s = reinterpret_cast<const float*>(Qt + LD::BYTES);
+      const float* Ds = lse2s + BQ;
 
 #pragma unroll
-    for (int j = 0; j < KPW; ++j) {
-      const int qbl = sp + NSPLIT * j;  // query block within the tile
-      const int qq0 = qt * BQ + qbl * 32;
-      if (!(qq0 < S && (!CAUSAL || qq0 + 31 >= k0))) continue;  // wave-uniform
-      const int arow = qbl * 32 + pi32(n);
-      f32x16 s = dot_tile<E, D>(Qt, arow, h, kf, zero16());
-      f32x16 dp = dot_tile<E, D>(dOt, arow, h, vf, zero16());
-      if ((CAUSAL && qq0 < k0 + 31) || qq0 + 32 > S) {
-        // query(r) = qq0 + 8h + (16*(r/8) + r%8) sees key kj iff kj <= query < S
-        const int lo = CAUSAL ? kj - qq0 - 8 * h : -64;
-        const int hi = S - 1 - qq0 - 8 * h;
+      for (int j = 0; j < KPW; ++j) {
+        const int qbl = sp + NSPLIT * j;  // query block within the tile
+        const int qq0 = qt * BQ + qbl * 32;
+        if (!(qq0 < S && (!CAUSAL || qq0 + 31 >= k0))) continue;  // wave-uniform
+        const int arow = qbl * 32 + pi32(n);
+        f32x16 s = dot_tile<E, D>(Qt, arow, h, kf, zero16());
+        f32x16 dp = dot_tile<E, D>(dOt, arow, h, vf, zero16());
+        if ((CAUSAL && qq0 < k0 + 31) || qq0 + 32 > S) {
+          // query(r) = qq0 + 8h + (16*(r/8) + r%8) sees key kj iff kj <= query < S
+          const int lo = CAUSAL ? kj - qq0 - 8 * h : -64;
+          const int hi = S - 1 - qq0 - 8 * h;
+          // all-ones where o < lo or o > hi, built without per-element
+          // compare masks (which would hold 16 scalar register pairs); the
+          // whole vector is bit-cast (a bit_cast of one element of an
+          // ext_vector is not reliable in this toolchain)
+          u32x16 sb = __builtin_bit_cast(u32x16, s);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int o = 16 * (r >> 3) + (r & 7);
-          if (o < lo || o > hi) s[r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int o = 16 * (r >> 3) + (r & 7);
+            const unsigned out = (unsigned)(((o - lo) | (hi - o)) >> 31);
+            sb[r] = (sb[r] & ~out) | (0xff800000u & out);
+          }
+          s = __builtin_bit_cast(f32x16, sb);
         }
-      }
-      // LSE*log2(e) and D of this lane's 16 queries: two runs of 8 at rho(0, h)
-      // and rho(8, h), handled one run at a time to keep registers down.
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int off = qbl * 32 + 16 * u + 8 * h;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2s + off);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2s + off + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(Ds + off);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(Ds + off + 4);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int r = 8 * u + t;
-          const float lq = t < 4 ? l0[t] : l1[t - 4];
-          const float dq = t < 4 ? d0[t] : d1[t - 4];
-          const float p = fast_exp2(fmaf(s[r], c, -lq));  // 0 where masked
-          s[r] = p;
-          dp[r] = p * (dp[r] - dq);
-        }
-      }
-      if constexpr (WDS) {
-        ++stored;
-        // dS^T for the dQ GEMM, row kj: this lane's 16 values are queries
-        // qq0 + 8h + {0..7} and qq0 + 16 + 8h + {0..7} (exact zeros where
-        // masked, for queries past S and for keys past S).
-        T* row = dSout + ((size_t)bh * SP + kj) * SP + qq0 + 8 * h;
-        const bool kvalid = kj < S;
+        // LSE*log2(e) and D of this lane's 16 queries: two runs of 8 at rho(0, h)
+        // and rho(8, h), handled one run at a time to keep registers down.
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          if constexpr (is_bf16<E>()) {
-            bf16x8 o;
+          const int off = qbl * 32 + 16 * u + 8 * h;
+          const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2s + off);
+          const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2s + off + 4);
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(Ds + off);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(Ds + off + 4);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) o[t] = (__bf16)(kvalid ? dp[8 * u + t] : 0.f);
-            *reinterpret_cast<bf16x8*>(row + 16 * u) = o;
-          } else {
+          for (int t = 0; t < 8; ++t) {
+            const int r = 8 * u + t;
+            const float lq = t < 4 ? l0[t] : l1[t - 4];
+            const float dq = t < 4 ? d0[t] : d1[t - 4];
+            const float p = fast_exp2(fmaf(s[r], c, -lq));  // 0 where masked
+            s[r] = p;
+            dp[r] = p * (dp[r] - dq);
+          }
+        }
+        if constexpr (WDS) {
+          ++stored;
+          // dS^T for the dQ GEMM, row kj: this lane's 16 values are queries
+          // qq0 + 8h + {0..7} and qq0 + 16 + 8h + {0..7} (exact zeros where
+          // masked, for queries past S and for keys past S).
+          T* row = dSout + ((size_t)bh * SP + kj) * SP + qq0 + 8 * h;
+          const bool kvalid = kj < S;
 #pragma unroll
-            for (int v4 = 0; v4 < 2; ++v4) {
-              f32x4 o;
+          for (int u = 0; u < 2; ++u) {
+            if constexpr (is_bf16<E>()) {
+              bf16x8 o;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) o[e] = kvalid ? dp[8 * u + 4 * v4 + e] : 0.f;
-              *reinterpret_cast<f32x4*>(row + 16 * u + 4 * v4) = o;
+              for (int t = 0; t < 8; ++t) o[t] = (__bf16)(kvalid ? dp[8 * u + t] : 0.f);
+              *reinterpret_cast<bf16x8*>(row + 16 * u) = o;
+            } else {
+#pragma unroll
+              for (int v4 = 0; v4 < 2; ++v4) {
+                f32x4 o;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = kvalid ? dp[8 * u + 4 * v4 + e] : 0.f;
+                *reinterpret_cast<f32x4*>(row + 16 * u + 4 * v4) = o;
+              }
             }
           }
         }
-      }
-      RegOperand<E> P, dS;
-      P.set(s);
-      dS.set(dp);
+        RegOperand<E> P, dS;
+        P.set(s);
+        dS.set(dp);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dvacc[db] = second_tile<E, D, true>(P, dOt, qbl * 32, db * 32, lane, dvacc[db]);
-        dkacc[db] = second_tile<E, D, true>(dS, Qt, qbl * 32, db * 32, lane, dkacc[db]);
-      }
-    }
-  }
-
-  // Sum the NSPLIT partial dK, dV of each key block through LDS.
-  if constexpr (NSPLIT > 1) {
-    float* cb = reinterpret_cast<float*>(smem);
-    lds_barrier();  // every wave is done with the tiles (no loads pending)
-    if (sp != 0 && wave_active) {
-      float* dst = cb + ((kbk * (NSPLIT - 1) + sp - 1) * 32 * NDB) * 64 + lane;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          dst[(db * 16 + r) * 64] = dkacc[db][r];
-          dst[((NDB + db) * 16 + r) * 64] = dvacc[db][r];
+        for (int db = 0; db < NDB; ++db) {
+          dvacc[db] = second_tile<E, D, true>(P, dOt, qbl * 32, db * 32, lane, dvacc[db]);
+          dkacc[db] = second_tile<E, D, true>(dS, Qt, qbl * 32, db * 32, lane, dkacc[db]);
         }
-    }
-    lds_barrier();
-    if (sp != 0) return;
-    if (wave_active) {
-#pragma unroll
-      for (int p = 0; p < NSPLIT - 1; ++p) {
-        const float* src = cb + ((kbk * (NSPLIT - 1) + p) * 32 * NDB) * 64 + lane;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            dkacc[db][r] += src[(db * 16 + r) * 64];
-            dvacc[db][r] += src[((NDB + db) * 16 + r) * 64];
-          }
       }
     }
-  }
-  if (!wave_active) return;
-  // element r of acc[db]: row k0 + out_row(r, h), column db*32 + n
-  T* dk = dK + base;
-  T* dv = dV + base;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = k0 + out_row(r, h);
-    if (row < S) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dk[(size_t)row * D + db * 32 + n] = (T)(dkacc[db][r] * scale);
-        dv[(size_t)row * D + db * 32 + n] = (T)dvacc[db][r];
-      }
-    }
+
+    // The item is done: merge through the stage of its last tile (the tiles
+    // in flight are the next NST-1, so no load targets it).
+    estores = merge_store(smem + ((pos - 1) % NST) * STAGE, bh, k0, wave_active);
   }
 }
 
@@ -229,13 +302,14 @@ static hipError_t launch(const BwdArgs& a) {
   constexpr int KPW = is_bf16<E>() ? ATTN_DKDV_KPW_BF16 : ATTN_DKDV_KPW_F32;
   constexpr int NST = is_bf16<E>() ? ATTN_DKDV_NST_BF16 : ATTN_DKDV_NST_F32;
   using T = typename E::T;
+  constexpr auto kern = bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS>;
   constexpr int BKV = 32 * (NW / NSPLIT);
   const int nkt = (a.S + BKV - 1) / BKV;
-  dim3 grid(a.BH, nkt);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS>), grid,
-                     dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SP, a.S,
-                     a.BH * a.S, a.scale * kLog2e, a.scale);
+  const int nitems = a.BH * nkt;
+  const int grid = std::min(nitems, resident_workgroups<kern>(NW * 64));
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
+                     (const T*)a.v, (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SP,
+                     a.S, a.BH * a.S, a.scale * kLog2e, a.scale, a.BH, nitems);
   return hipGetLastError();
 }
 

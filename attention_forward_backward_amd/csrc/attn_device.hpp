@@ -29,6 +29,7 @@ namespace attn {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -94,24 +95,27 @@ struct RowFrag {
   typename E::Frag f[NS];
 };
 
+// Store 16 bytes (chunk c of the lane's half row) into the fragment.
+template <class E, int D>
+__device__ inline void set_frag_chunk(RowFrag<E, D>& rf, int c, u32x4 x) {
+  if constexpr (is_bf16<E>()) {
+    rf.f[c] = __builtin_bit_cast(bf16x8, x);
+  } else {
+    // bit-cast the whole vector: a bit_cast of one ext_vector element is
+    // not reliable here (it read element 0 for every e)
+    const f32x4 xf = __builtin_bit_cast(f32x4, x);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rf.f[4 * c + e] = xf[e];
+  }
+}
+
 template <class E, int D>
 __device__ inline void load_row_frag(RowFrag<E, D>& rf, const typename E::T* p, bool valid) {
   // p points at element h*D/2 of the row; reads D/2 contiguous elements.
   constexpr int NCH = (D / 2) * (int)sizeof(typename E::T) / 16;
   const u32x4* src = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    u32x4 x = valid ? src[c] : u32x4{0u, 0u, 0u, 0u};
-    if constexpr (is_bf16<E>()) {
-      rf.f[c] = __builtin_bit_cast(bf16x8, x);
-    } else {
-      // bit-cast the whole vector: a bit_cast of one ext_vector element is
-      // not reliable here (it read element 0 for every e)
-      const f32x4 xf = __builtin_bit_cast(f32x4, x);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rf.f[4 * c + e] = xf[e];
-    }
-  }
+  for (int c = 0; c < NCH; ++c) set_frag_chunk(rf, c, valid ? src[c] : u32x4{0u, 0u, 0u, 0u});
 }
 
 // ------------------------------------------------------------------ LDS tiles
@@ -150,12 +154,48 @@ struct Tile {
   }
 };
 
+// The row fragment of tile row `row` (this lane's key or query), read from a
+// swizzled LDS tile: half h of the row, 16 bytes at a time (read pattern A).
+// Rows that are not valid read as zero.
+template <class E, int D>
+__device__ inline void load_row_frag_lds(RowFrag<E, D>& rf, const char* tile, int row, int h,
+                                         bool valid) {
+  using TL = Tile<E, D>;
+  constexpr int NCH = TL::CPR / 2;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const u32x4 x =
+        *reinterpret_cast<const u32x4*>(tile + row * TL::ROWB + (((h * NCH + c) ^ TL::swz(row)) << 4));
+    set_frag_chunk(rf, c, valid ? x : u32x4{0u, 0u, 0u, 0u});
+  }
+}
+
+// Static persistent schedule: workgroup g of G takes the items (numbered in
+// order of decreasing work) g, 2G-1-g, 2G+g, 4G-1-g, ...  Item numbers grow
+// with the round r, so a workgroup stops at its first number >= the count.
+__device__ inline int snake_item(int r, int g, int G) { return r * G + ((r & 1) ? G - 1 - g : g); }
+
 // Wait until at most N vector-memory operations of this wave are pending.
 template <int N>
 __device__ inline void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Wait until at most n (clamped to 0..63) vector-memory operations of this
+// wave are pending, for a wave-uniform n known only at run time: a binary
+// search over the immediate forms.
+template <int LO, int HI>
+__device__ inline void wait_vmem_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vmem<LO>();
+  } else {
+    constexpr int MID = (LO + HI + 1) / 2;
+    if (n >= MID) wait_vmem_range<MID, HI>(n);
+    else wait_vmem_range<LO, MID - 1>(n);
+  }
+}
+__device__ inline void wait_vmem_dyn(int n) { wait_vmem_range<0, 63>(n < 0 ? 0 : n); }
+
 // Wait for the oldest staged tile when `newer` younger tiles (NL loads each)
 // may stay in flight, and after them `blocks` groups of NS stores each
 // (vmcnt counts stores as well as loads, and vector memory operations retire
@@ -223,13 +263,28 @@ struct StageLoader {
   }
   __device__ static inline void issue(char* stage, const T* src0, const T* src1, int row0, int S,
                                       int w, int lane, unsigned lo) {
-    if (FAST && row0 + BT <= S) {
+    if constexpr (FAST) {
+      if (row0 + BT <= S) {
+#pragma unroll
+        for (int i = 0; i < NLOADS; ++i) {
+          const int slot = i * NW + w;         // 1 KiB slot of the stage (wave-uniform)
+          const int mat = slot * 64 / CH_PER;  // wave-uniform
+          const T* base = (mat == 0 ? src0 : src1) + (size_t)(row0 + i * RS - mat * BT) * D;
+          __builtin_amdgcn_global_load_lds(lane_addr(base, lo), stage + slot * 1024, 16, 0, 0);
+        }
+        return;
+      }
+      // The tile crosses S: the same lane pattern with the global row clamped.
+      const int lrow = lo / (D * (int)sizeof(T));  // tile row of the lane in the first load
+      const unsigned col = lo - lrow * D * (int)sizeof(T);
 #pragma unroll
       for (int i = 0; i < NLOADS; ++i) {
-        const int slot = i * NW + w;           // 1 KiB slot of the stage (wave-uniform)
-        const int mat = slot * 64 / CH_PER;    // wave-uniform
-        const T* base = (mat == 0 ? src0 : src1) + (size_t)(row0 + i * RS - mat * BT) * D;
-        __builtin_amdgcn_global_load_lds(lane_addr(base, lo), stage + slot * 1024, 16, 0, 0);
+        const int slot = i * NW + w;
+        const int mat = slot * 64 / CH_PER;
+        const int grow = min(row0 + i * RS - mat * BT + lrow, S - 1);
+        const char* src = reinterpret_cast<const char*>(mat == 0 ? src0 : src1) +
+                          (size_t)grow * D * sizeof(T) + col;
+        __builtin_amdgcn_global_load_lds(src, stage + slot * 1024, 16, 0, 0);
       }
       return;
     }
@@ -268,12 +323,24 @@ struct TileLoader {
   }
   __device__ static inline void issue(char* dst, const T* src, size_t ld, int row0, int rows,
                                       int col0, int w, int lane, unsigned lo) {
-    if (FAST && row0 + BT <= rows) {
+    if constexpr (FAST) {
+      if (row0 + BT <= rows) {
+#pragma unroll
+        for (int i = 0; i < NLOADS; ++i) {
+          const int slot = i * NW + w;
+          const T* base = src + (size_t)(row0 + i * RS) * ld + col0;
+          __builtin_amdgcn_global_load_lds(lane_addr(base, lo), dst + slot * 1024, 16, 0, 0);
+        }
+        return;
+      }
+      // The tile crosses `rows`: the same lane pattern with the row clamped.
+      const int lrow = w * RPS + lane / TL::CPR;
+      const int lcol = ((lane % TL::CPR) ^ TL::swz(lrow)) * TL::EPC;
 #pragma unroll
       for (int i = 0; i < NLOADS; ++i) {
         const int slot = i * NW + w;
-        const T* base = src + (size_t)(row0 + i * RS) * ld + col0;
-        __builtin_amdgcn_global_load_lds(lane_addr(base, lo), dst + slot * 1024, 16, 0, 0);
+        const T* g = src + (size_t)min(row0 + i * RS + lrow, rows - 1) * ld + col0 + lcol;
+        __builtin_amdgcn_global_load_lds(g, dst + slot * 1024, 16, 0, 0);
       }
       return;
     }

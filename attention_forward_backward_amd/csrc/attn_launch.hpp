@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 // Launch shapes per kernel and contract: NW waves per workgroup, NSPLIT
 // waves sharing each 32-row block (splitting its inner loop), KPW 32-row
 // blocks per wave per staged tile, NST LDS stages in the tile ring.  Defaults come from measurements on
@@ -113,6 +115,29 @@ struct BwdArgs {
   float scale;
   hipStream_t stream;
 };
+
+// Workgroups of kernel Kern (launched with `threads` threads and no dynamic
+// LDS) that the current device holds at once: CUs x resident workgroups per
+// CU.  Persistent kernels launch this many (or fewer) workgroups.  Queried
+// once per device and cached; falls back to one per CU if a query fails.
+template <auto Kern>
+inline int resident_workgroups(int threads) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int ncu = 0, nb = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu <= 0)
+    ncu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(Kern), threads, 0) !=
+          hipSuccess ||
+      nb <= 0)
+    nb = 1;
+  v = ncu * nb;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
