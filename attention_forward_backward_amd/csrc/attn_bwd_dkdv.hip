@@ -48,7 +48,11 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   constexpr int NDB = D / 32;
   using LD = StageLoader<E, D, BQ, NW>;
   constexpr int TILEB = BQ * TL::ROWB;                            // dO follows Q in a stage
-  constexpr int STAGE = (LD::BYTES + 2 * BQ * 4 + 1023) / 1024 * 1024;  // + LSE*log2e, D
+  // A ring stage holds the tiles only (its LDS addresses then fit the read
+  // instructions' 16-bit offsets); the per-stage statistics (LSE*log2e, D)
+  // follow all the stages.
+  constexpr int STAGE = LD::BYTES;
+  constexpr int STATS = 2 * BQ * 4;
   constexpr int NL = LD::NLOADS + 1;                              // loads per wave per tile
   // Partials of the NSPLIT-1 helper waves of every key block, one matrix
   // (dK or dV): summed through the stage just consumed, in one pass when it
@@ -58,7 +62,8 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   static_assert(PART * (3 - NPASS) <= STAGE, "split partials must fit one stage");
   static_assert(BKV == BQ, "a K/V header tile has the shape of a query tile");
   static_assert(NW % NSPLIT == 0 && NST >= 2 && NST <= 4, "launch shape");
-  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE + NST * STATS];
+  float* const stats0 = reinterpret_cast<float*>(smem + NST * STAGE);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5, n = lane & 31;
@@ -82,7 +87,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     const bool head = lqt < 0;
     const int row0 = head ? lkt * BKV : lqt * BQ;
     LD::issue(st, (head ? K : Q) + lho * D, (head ? V : dO) + lho * D, row0, S, w, lane, lane_off);
-    issue_stats<BQ, NW>(reinterpret_cast<float*>(st + LD::BYTES), Dws + L + lho, Dws + lho,
+    issue_stats<BQ, NW>(stats0 + (nissued % NST) * (2 * BQ), Dws + L + lho, Dws + lho,
                         head ? 0 : row0, S, w, lane);
     ++nissued;
     if (head) {
@@ -204,9 +209,10 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
       issue_next();
       __builtin_amdgcn_sched_barrier(0);
       if (!wave_active) continue;
-      const char* Qt = smem + (pos % NST) * STAGE;
+      const int si = pos % NST;
+      const char* Qt = smem + si * STAGE;
       const char* dOt = Qt + TILEB;
-      const float* lse2s = reinterpret_cast<const float*>(Qt + LD::BYTES);
+      const float* lse2s = stats0 + si * (2 * BQ);
       const float* Ds = lse2s + BQ;
 
 #pragma unroll
@@ -259,20 +265,21 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
           // qq0 + 8h + {0..7} and qq0 + 16 + 8h + {0..7} (exact zeros where
           // masked, for queries past S and for keys past S).
           T* row = dSout + ((size_t)bh * SP + kj) * SP + qq0 + 8 * h;
-          const bool kvalid = kj < S;
+          // keys past S (only in the last key tile) store zeros
+          if (k0 + 32 > S && kj >= S) dp = zero16();
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             if constexpr (is_bf16<E>()) {
               bf16x8 o;
 #pragma unroll
-              for (int t = 0; t < 8; ++t) o[t] = (__bf16)(kvalid ? dp[8 * u + t] : 0.f);
+              for (int t = 0; t < 8; ++t) o[t] = (__bf16)dp[8 * u + t];
               *reinterpret_cast<bf16x8*>(row + 16 * u) = o;
             } else {
 #pragma unroll
               for (int v4 = 0; v4 < 2; ++v4) {
                 f32x4 o;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = kvalid ? dp[8 * u + 4 * v4 + e] : 0.f;
+                for (int e = 0; e < 4; ++e) o[e] = dp[8 * u + 4 * v4 + e];
                 *reinterpret_cast<f32x4*>(row + 16 * u + 4 * v4) = o;
               }
             }

@@ -103,9 +103,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
       if (kk0 + 32 > S || (CAUSAL && kk0 + 31 > q0)) {
         // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < S and key <= qi
         const int lim = min(S - 1, CAUSAL ? qi : S - 1) - kk0 - 8 * h;
+        // -inf where 16*(r/8) + r%8 > lim, built arithmetically (no
+        // per-element compare masks in scalar registers); the whole vector
+        // is bit-cast (a bit_cast of one ext_vector element is not reliable)
+        u32x16 sb = __builtin_bit_cast(u32x16, st);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (16 * (r >> 3) + (r & 7) > lim) st[r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const unsigned out = (unsigned)((lim - (16 * (r >> 3) + (r & 7))) >> 31);
+          sb[r] = (sb[r] & ~out) | (0xff800000u & out);
+        }
+        st = __builtin_bit_cast(f32x16, sb);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
