@@ -22,6 +22,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 namespace attn {
@@ -167,6 +169,27 @@ __device__ inline void load_row_frag_lds(RowFrag<E, D>& rf, const char* tile, in
     const u32x4 x =
         *reinterpret_cast<const u32x4*>(tile + row * TL::ROWB + (((h * NCH + c) ^ TL::swz(row)) << 4));
     set_frag_chunk(rf, c, valid ? x : u32x4{0u, 0u, 0u, 0u});
+  }
+}
+
+// Run f(t, stage) for t = 0 .. n-1, where stage = t % NST is passed as a
+// compile-time constant (std::integral_constant): the loop is unrolled by
+// NST so that each stage's LDS base folds into the reads' 16-bit immediate
+// offsets, and the loop-carried state flows from one stage's body into the
+// next.
+template <int NST, class F>
+__device__ inline void for_stages(int n, F&& f) {
+  for (int t0 = 0; t0 < n; t0 += NST) {
+    f(t0, std::integral_constant<int, 0>{});
+    if constexpr (NST >= 2) {
+      if (t0 + 1 < n) f(t0 + 1, std::integral_constant<int, 1>{});
+    }
+    if constexpr (NST >= 3) {
+      if (t0 + 2 < n) f(t0 + 2, std::integral_constant<int, 2>{});
+    }
+    if constexpr (NST >= 4) {
+      if (t0 + 3 < n) f(t0 + 3, std::integral_constant<int, 3>{});
+    }
   }
 }
 

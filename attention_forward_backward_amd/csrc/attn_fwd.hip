@@ -77,70 +77,78 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   for (int s = 0; s < NST - 1; ++s)
     if (s < nkt) LD::issue(smem + s * LD::BYTES, k, v, s * BK, S, w, lane, lo);
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  // One staged tile of keys.  When the stages' LDS addresses fit 16-bit
+  // offsets, the loop is unrolled by NST with the stage index constant.
+  auto step = [&](const int kt, auto sc) {
+    const int si = sc;  // kt % NST
     wait_tiles<LD::NLOADS>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1
     if (kt + NST - 1 < nkt)
       LD::issue(smem + ((kt + NST - 1) % NST) * LD::BYTES, k, v, (kt + NST - 1) * BK, S, w, lane, lo);
-    if (!wave_active) continue;
-    const char* Kt = smem + (kt % NST) * LD::BYTES;
+    if (!wave_active) return;
+    const char* Kt = smem + si * LD::BYTES;
     const char* Vt = Kt + TILEB;
 
-    // This wave's 32-key blocks of the tile.  A block is skipped when no key
-    // in it is visible from any of the wave's queries, and masked only when
-    // some but not all of it is (the causal diagonal, the ragged end).  Every
-    // processed block has at least one visible key for every query (block
-    // starts are multiples of 32), so row maxima are finite.
-#pragma unroll
-    for (int j = 0; j < KPW; ++j) {
-      const int kb = sp + NSPLIT * j;
-      const int kk0 = kt * BK + kb * 32;
-      if (!(kk0 < S && (!CAUSAL || kk0 <= q0 + 31))) continue;  // wave-uniform
-      f32x16 sacc = dot_tile<E, D>(Kt, kb * 32 + pi32(n), h, qf, zero16());
-      if (kk0 + 32 > S || (CAUSAL && kk0 + 31 > q0)) {
-        // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < S and key <= qi
-        const int lim = min(S - 1, CAUSAL ? qi : S - 1) - kk0 - 8 * h;
-        // -inf where 16*(r/8) + r%8 > lim, built arithmetically (no
-        // per-element compare masks in scalar registers); the whole vector
-        // is bit-cast (a bit_cast of one ext_vector element is not reliable)
-        u32x16 sb = __builtin_bit_cast(u32x16, sacc);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const unsigned out = (unsigned)((lim - (16 * (r >> 3) + (r & 7))) >> 31);
-          sb[r] = (sb[r] & ~out) | (0xff800000u & out);
+      // This wave's 32-key blocks of the tile.  A block is skipped when no key
+      // in it is visible from any of the wave's queries, and masked only when
+      // some but not all of it is (the causal diagonal, the ragged end).  Every
+      // processed block has at least one visible key for every query (block
+      // starts are multiples of 32), so row maxima are finite.
+  #pragma unroll
+      for (int j = 0; j < KPW; ++j) {
+        const int kb = sp + NSPLIT * j;
+        const int kk0 = kt * BK + kb * 32;
+        if (!(kk0 < S && (!CAUSAL || kk0 <= q0 + 31))) continue;  // wave-uniform
+        f32x16 sacc = dot_tile<E, D>(Kt, kb * 32 + pi32(n), h, qf, zero16());
+        if (kk0 + 32 > S || (CAUSAL && kk0 + 31 > q0)) {
+          // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < S and key <= qi
+          const int lim = min(S - 1, CAUSAL ? qi : S - 1) - kk0 - 8 * h;
+          // -inf where 16*(r/8) + r%8 > lim, built arithmetically (no
+          // per-element compare masks in scalar registers); the whole vector
+          // is bit-cast (a bit_cast of one ext_vector element is not reliable)
+          u32x16 sb = __builtin_bit_cast(u32x16, sacc);
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned out = (unsigned)((lim - (16 * (r >> 3) + (r & 7))) >> 31);
+            sb[r] = (sb[r] & ~out) | (0xff800000u & out);
+          }
+          sacc = __builtin_bit_cast(f32x16, sb);
         }
-        sacc = __builtin_bit_cast(f32x16, sb);
+        float mx = -INFINITY;  // max of the raw (unscaled) visible scores
+  #pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[r], sacc[r + 1]));
+        mx = fmaxf(mx, xhalf(mx));
+        // Lazy rescaling: exponents are taken against a reference m that may
+        // lag the running max by up to 2^8, so O and l are rescaled only when
+        // some row's max grows past that (on a wave's first block they are 0).
+        const float mc = mx * c;
+        if (__any(mc > m + 8.f)) {
+          const float mnew = fmaxf(m, mc);
+          const float alpha = fast_exp2(m - mnew);
+          m = mnew;
+          l *= alpha;
+  #pragma unroll
+          for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+        }
+        float rs = 0.f;
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[r], c, -m));
+          sacc[r] = p;
+          rs += p;
+        }
+        l += rs;
+        RegOperand<E> P;
+        P.set(sacc);
+  #pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          oacc[db] = second_tile<E, D, false>(P, Vt, kb * 32, db * 32, lane, oacc[db]);
       }
-      float mx = -INFINITY;  // max of the raw (unscaled) visible scores
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[r], sacc[r + 1]));
-      mx = fmaxf(mx, xhalf(mx));
-      // Lazy rescaling: exponents are taken against a reference m that may
-      // lag the running max by up to 2^8, so O and l are rescaled only when
-      // some row's max grows past that (on a wave's first block they are 0).
-      const float mc = mx * c;
-      if (__any(mc > m + 8.f)) {
-        const float mnew = fmaxf(m, mc);
-        const float alpha = fast_exp2(m - mnew);
-        m = mnew;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      }
-      float rs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sacc[r], c, -m));
-        sacc[r] = p;
-        rs += p;
-      }
-      l += rs;
-      RegOperand<E> P;
-      P.set(sacc);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        oacc[db] = second_tile<E, D, false>(P, Vt, kb * 32, db * 32, lane, oacc[db]);
-    }
+  };
+  if constexpr (NST * LD::BYTES <= 65536) {
+    for_stages<NST>(nkt, step);
+  } else {
+    for (int kt = 0; kt < nkt; ++kt) step(kt, kt % NST);
   }
 
   // Merge the NSPLIT partial (m, l, O) of each query block through LDS.
