@@ -83,13 +83,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   for (int s = 0; s < NST - 1; ++s)
     if (s < nkt) LD::issue(smem + s * LD::BYTES, k, v, s * BK, S, w, lane, lo);
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  // One staged tile of keys.  When the stages' LDS addresses fit 16-bit
+  // offsets, the loop is unrolled by NST with the stage index constant.
+  auto step = [&](const int kt, auto sc) {
+    const int si = sc;  // kt % NST
     wait_tiles<LD::NLOADS>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1
     if (kt + NST - 1 < nkt)
       LD::issue(smem + ((kt + NST - 1) % NST) * LD::BYTES, k, v, (kt + NST - 1) * BK, S, w, lane, lo);
-    if (!wave_active) continue;
-    const char* Kt = smem + (kt % NST) * LD::BYTES;
+    if (!wave_active) return;
+    const char* Kt = smem + si * LD::BYTES;
     const char* Vt = Kt + TILEB;
 
 #pragma unroll
@@ -125,6 +128,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
       for (int db = 0; db < NDB; ++db)
         acc[db] = second_tile<E, D, true>(dS, Kt, kb * 32, db * 32, lane, acc[db]);
     }
+  };
+  if constexpr (NST * LD::BYTES <= 65536) {
+    for_stages<NST>(nkt, step);
+  } else {
+    for (int kt = 0; kt < nkt; ++kt) step(kt, kt % NST);
   }
 
   // Sum the NSPLIT partial dQ of each query block through LDS.
@@ -219,12 +227,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   for (int s = 0; s < NST - 1; ++s)
     if (s < nkt) issue(s);
 
-  for (int kt = 0; kt < nkt; ++kt) {
+  auto step = [&](const int kt, auto sc) {
+    const int si = sc;  // kt % NST
     wait_tiles<NL>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();
     if (kt + NST - 1 < nkt) issue(kt + NST - 1);
-    if (!wave_active) continue;
-    const char* St = smem + (kt % NST) * STAGE;
+    if (!wave_active) return;
+    const char* St = smem + si * STAGE;
     const char* Kt = St + LDS_::BYTES;
 #pragma unroll
     for (int j = 0; j < KPW; ++j) {
@@ -237,6 +246,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
       for (int db = 0; db < NDB; ++db)
         acc[db] = second_tile<E, D, true>(R, Kt, kb * 32, db * 32, lane, acc[db]);
     }
+  };
+  if constexpr (NST * STAGE <= 65536) {
+    for_stages<NST>(nkt, step);
+  } else {
+    for (int kt = 0; kt < nkt; ++kt) step(kt, kt % NST);
   }
 
   if constexpr (NSPLIT > 1) {
