@@ -85,7 +85,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 
   // One staged tile of keys.  When the stages' LDS addresses fit 16-bit
   // offsets, the loop is unrolled by NST with the stage index constant.
-  auto step = [&](const int kt, auto sc) {
+  auto step = [&](const int kt, auto sc) __attribute__((always_inline)) {
     const int si = sc;  // kt % NST
     wait_tiles<LD::NLOADS>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   const int kend = CAUSAL ? min(S, qw0 + BR) : S;
   const int nkt = (kend + BK - 1) / BK;
   const unsigned los = LDS_::lane_offset(SP, w, lane), lok = LDK::lane_offset(D, w, lane);
-  auto issue = [&](int t) {
+  auto issue = [&](int t) __attribute__((always_inline)) {
     char* st = smem + (t % NST) * STAGE;
     LDS_::issue(st, dst_, SP, t * BK, SP, qw0, w, lane, los);
     LDK::issue(st + LDS_::BYTES, k, D, t * BK, S, 0, w, lane, lok);
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   for (int s = 0; s < NST - 1; ++s)
     if (s < nkt) issue(s);
 
-  auto step = [&](const int kt, auto sc) {
+  auto step = [&](const int kt, auto sc) __attribute__((always_inline)) {
     const int si = sc;  // kt % NST
     wait_tiles<NL>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();

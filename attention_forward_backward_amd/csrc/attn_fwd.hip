@@ -79,7 +79,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
 
   // One staged tile of keys.  When the stages' LDS addresses fit 16-bit
   // offsets, the loop is unrolled by NST with the stage index constant.
-  auto step = [&](const int kt, auto sc) {
+  auto step = [&](const int kt, auto sc) __attribute__((always_inline)) {
     const int si = sc;  // kt % NST
     wait_tiles<LD::NLOADS>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1
