@@ -193,10 +193,18 @@ __device__ inline void for_stages(int n, F&& f) {
   }
 }
 
-// Static persistent schedule: workgroup g of G takes the items (numbered in
-// order of decreasing work) g, 2G-1-g, 2G+g, 4G-1-g, ...  Item numbers grow
-// with the round r, so a workgroup stops at its first number >= the count.
-__device__ inline int snake_item(int r, int g, int G) { return r * G + ((r & 1) ? G - 1 - g : g); }
+// Static persistent schedule: in round r workgroup g of G takes item
+// r*G + g (r even) or r*G + g' (r odd), where g' reverses the order of the
+// workgroups that share g's residue mod 8 (items are numbered in order of
+// decreasing work, so the reversal evens out the per-workgroup totals).
+// Workgroups are dispatched round-robin over the 8 XCDs, so keeping the
+// residue keeps every item of a head on one XCD and its L2.  Item numbers
+// grow with r, so a workgroup stops at its first number >= the count.
+__device__ inline int snake_item(int r, int g, int G) {
+  if (!(r & 1)) return r * G + g;
+  const int gr = (G % 8 == 0) ? g % 8 + 8 * (G / 8 - 1 - g / 8) : G - 1 - g;
+  return r * G + gr;
+}
 
 // Wait until at most N vector-memory operations of this wave are pending.
 template <int N>
