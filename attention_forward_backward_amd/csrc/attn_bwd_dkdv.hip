@@ -14,7 +14,8 @@
 // Work split (persistent): an item is (key tile of BKV = 32*RB rows,
 // batch*head), numbered in order of decreasing causal work; the launch puts
 // about one workgroup on every resident slot and each walks its items in the
-// static snake order (snake_item).  Each 32-key block of an item is owned by
+// static schedule (sched_item: balanced over the CUs, each head's items on
+// one XCD).  Each 32-key block of an item is owned by
 // NSPLIT waves that keep its K and V rows in registers, split the query
 // blocks between them, accumulate dK and dV in registers and sum their
 // partials through LDS when the item ends.
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
     typename E::T* __restrict__ dSout, int SP, int S, int L, float c, float scale, int BH,
-    int nitems) {
+    int nitems, const Sched sched) {
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-key blocks per item
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   // item lit, whose K and V rows it stages; else query tile lqt).  Every
   // stream tile is NL loads per wave (the header also loads statistics it
   // does not use, to keep that count).
-  int lr = 0, lit = snake_item(0, g, G), lqt = -1, lkt = lit / BH;
+  int lr = 0, lit = sched_item(sched, 0, g, G, BH), lqt = -1, lkt = lit / BH;
   size_t lho = (size_t)(lit % BH) * S;  // first row of the item's head
   int nissued = 0;
   auto issue_next = [&]() {
@@ -93,14 +94,14 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     if (head) {
       lqt = first_qt(lkt);
     } else if (++lqt == nqt) {
-      lit = snake_item(++lr, g, G);
+      lit = sched_item(sched, ++lr, g, G, BH);
       lqt = -1;
       lkt = lit / BH;
       lho = (size_t)(lit % BH) * S;
     }
   };
 
-  if (snake_item(0, g, G) >= nitems) return;  // (the launch never makes more workgroups than items)
+  if (sched_item(sched, 0, g, G, BH) >= nitems) return;  // (the launch never makes more workgroups than items)
 #pragma unroll
   for (int i = 0; i < NST - 1; ++i) issue_next();
 
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   int stored = 0, estores = 0;
   int pos = 0;  // stream position of the tile being consumed
   for (int cr = 0;; ++cr) {
-    const int cit = snake_item(cr, g, G);
+    const int cit = sched_item(sched, cr, g, G, BH);
     if (cit >= nitems) break;
     const int kt = cit / BH, bh = cit % BH;
     const int k0 = kt * BKV + kbk * 32;
@@ -314,9 +315,15 @@ static hipError_t launch(const BwdArgs& a) {
   const int nkt = (a.S + BKV - 1) / BKV;
   const int nitems = a.BH * nkt;
   const int grid = std::min(nitems, resident_workgroups<kern>(NW * 64));
+  // work of a key tile: its header tile and the query tiles it visits
+  constexpr int BQ = 32 * NSPLIT * KPW;
+  const int nqt = (a.S + BQ - 1) / BQ;
+  std::vector<int> works(nkt);
+  for (int kt = 0; kt < nkt; ++kt) works[kt] = 1 + nqt - (CAUSAL ? (kt * BKV) / BQ : 0);
+  const Sched sched = make_sched(grid, a.BH, works);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SP,
-                     a.S, a.BH * a.S, a.scale * kLog2e, a.scale, a.BH, nitems);
+                     a.S, a.BH * a.S, a.scale * kLog2e, a.scale, a.BH, nitems, sched);
   return hipGetLastError();
 }
 

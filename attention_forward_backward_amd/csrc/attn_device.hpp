@@ -206,6 +206,37 @@ __device__ inline int snake_item(int r, int g, int G) {
   return r * G + gr;
 }
 
+// Static schedule of a persistent launch, computed on the host and passed by
+// value in the kernel arguments.  Workgroups are dispatched round-robin over
+// the 8 XCDs, so workgroup g runs on XCD g % 8 as its slot g / 8.  When the
+// head count is a multiple of 8, head b is kept on XCD b % 8 and every XCD
+// runs the same pattern: slot j takes first[j] in round 0 and
+// ent[(r-1) * M + j] in round r >= 1 (0xffff: none, and none after it), each
+// naming (work class c, local head u) as (c << 8) | u, which is item
+// c * BH + 8u + g % 8.  Every lookup is one load at an address that needs
+// no other load (round 0's not even M), so a workgroup's first item is known
+// one scalar-load latency after it starts.  M = 0: no pattern, the snake
+// order applies.
+constexpr int kSchedSlots = 256;
+constexpr int kSchedEntries = 1280;
+struct Sched {
+  int M;  // slots per XCD, or 0
+  int R;  // rounds in the table
+  uint16_t first[kSchedSlots];
+  uint16_t ent[kSchedEntries];
+};
+
+// Item of round r of workgroup g (a value >= every item count once g has no
+// more items).
+__device__ inline int sched_item(const Sched& s, int r, int g, int G, int BH) {
+  const int e0 = s.first[(g >> 3) & (kSchedSlots - 1)];
+  if (s.M == 0) return snake_item(r, g, G);
+  if (r >= s.R) return 0x7fffffff;
+  const int e = r == 0 ? e0 : s.ent[(r - 1) * s.M + (g >> 3)];
+  if (e == 0xffff) return 0x7fffffff;
+  return (e >> 8) * BH + 8 * (e & 255) + (g & 7);
+}
+
 // Wait until at most N vector-memory operations of this wave are pending.
 template <int N>
 __device__ inline void wait_vmem() {

@@ -6,15 +6,22 @@
 // LSE, with the softmax taken online over key tiles so that no S x S matrix
 // exists.
 //
-// Work split: one workgroup per (query tile of 32*RB rows, batch*head).  Each
-// 32-query block is owned by NSPLIT waves that split the key range between
-// them (block kb of every staged tile goes to wave kb % NSPLIT); each keeps
-// its own running max, sum and O, and the NSPLIT partial results are merged
-// through LDS at the end.
+// Work split (persistent): an item is (query tile of BR = 32*RB rows,
+// batch*head), numbered in order of decreasing causal work; the launch puts
+// about one workgroup on every resident slot and each walks the items a
+// static schedule gives it (sched_item: balanced over the CUs, each head's
+// items on one XCD).  Each 32-query block of an item is owned by
+// NSPLIT waves that split the key range between them (block kb of every
+// staged tile goes to wave kb % NSPLIT); each keeps its own running max, sum
+// and O, and the NSPLIT partial results are merged through LDS when the item
+// ends.
 //
 // K and V stream through an NST-stage ring of LDS tiles (32*NSPLIT*KPW keys
 // each) filled by direct global->LDS loads issued NST-1 tiles ahead, with one
-// workgroup barrier per tile.
+// workgroup barrier per tile.  The stream runs across item boundaries, so the
+// next item's first keys load while the current item finishes; the next
+// item's Q tile loads into its own LDS buffer one item ahead, and each wave
+// reads its Q rows into registers when its item starts.
 //
 // Per wave and 32-key block the scores are computed transposed,
 // S^T = K Q^T (32 keys x 32 queries): each lane then holds one query and 16
@@ -31,70 +38,194 @@ template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O,
-    float* __restrict__ LSE, int S, float c) {
+    float* __restrict__ LSE, int S, float c, int BH, int nitems, const Sched sched) {
   using T = typename E::T;
   using TL = Tile<E, D>;
-  constexpr int RB = NW / NSPLIT;        // 32-query blocks per workgroup
-  constexpr int BR = 32 * RB;            // queries per workgroup
+  constexpr int RB = NW / NSPLIT;        // 32-query blocks per item
+  constexpr int BR = 32 * RB;            // queries per item
   constexpr int BK = 32 * NSPLIT * KPW;  // keys per staged tile
   constexpr int NDB = D / 32;
   using LD = StageLoader<E, D, BK, NW>;
+  constexpr int STAGE = LD::BYTES;
   constexpr int TILEB = BK * TL::ROWB;  // one matrix tile; V follows K in a stage
-  constexpr int NV = 16 * NDB + 2;      // floats per lane in a partial result
-  constexpr int COMB = RB * (NSPLIT - 1) * NV * 64 * 4;
-  constexpr int SMEM = NST * LD::BYTES > COMB ? NST * LD::BYTES : COMB;
+  using QL = TileLoader<E, D, BR, NW>;
   static_assert(NW % NSPLIT == 0 && NST >= 2 && NST <= 4, "launch shape");
-  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+  __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE + QL::BYTES];
+  char* const qtile = smem + NST * STAGE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int qb = w / NSPLIT, sp = w % NSPLIT;
-  const int bh = blockIdx.x;
-  const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;  // longest causal tiles first
-  const size_t base = (size_t)bh * S * D;
-  const T* k = K + base;
-  const T* v = V + base;
+  const int g = blockIdx.x, G = gridDim.x;
+  const int nqt = (S + BR - 1) / BR;
+  const unsigned lo = LD::lane_offset(w, lane);
+  const unsigned qlo = QL::lane_offset(D, w, lane);
+  auto item_qt = [&](int it) { return nqt - 1 - it / BH; };
+  auto item_nkt = [&](int it) {
+    const int kend = CAUSAL ? min(S, item_qt(it) * BR + BR) : S;
+    return (kend + BK - 1) / BK;
+  };
+  if (sched_item(sched, 0, g, G, BH) >= nitems) return;  // (the launch never makes more workgroups than items)
 
-  const int q0 = qt * BR + qb * 32;
-  const int qi = q0 + n;
-  const bool wave_active = q0 < S;
+  // Vector-memory instructions this wave has issued (loads, and the stores
+  // counted by the rule below), and the count just after the loads of each
+  // tile in the ring and of the prefetched Q rows.  Waiting until at most
+  // vm - mark operations are pending completes everything up to that mark
+  // (vmcnt counts loads and stores, and they retire in issue order);
+  // counting fewer stores than issued only makes a wait stricter.
+  int vm = 0, qmark = 0;
+  int mk[NST];
+#pragma unroll
+  for (int i = 0; i < NST; ++i) mk[i] = 0;
 
+  // Loader cursor: tile lkt of item lit is the next one to issue.
+  int lr = 0, lit = sched_item(sched, 0, g, G, BH), lkt = 0, lnkt = item_nkt(lit);
+  size_t lbase = (size_t)(lit % BH) * S * D;
+  // While tiles remain, the tile issued at stream position pos goes to ring
+  // slot (pos + NST - 1) % NST, a constant of the unrolled step.
+  auto issue_next = [&](const int slot) __attribute__((always_inline)) {
+    if (lit >= nitems) return;
+    LD::issue(smem + slot * STAGE, K + lbase, V + lbase, lkt * BK, S, w, lane, lo);
+    vm += LD::NLOADS;
+#pragma unroll
+    for (int i = 0; i < NST; ++i)
+      if (slot == i) mk[i] = vm;
+    if (++lkt == lnkt) {
+      lit = sched_item(sched, ++lr, g, G, BH);
+      lkt = 0;
+      if (lit < nitems) {
+        lnkt = item_nkt(lit);
+        lbase = (size_t)(lit % BH) * S * D;
+      }
+    }
+  };
+  // The Q tile of item it (rows past S read row S-1) into its LDS buffer.
+  auto load_q = [&](int it) __attribute__((always_inline)) {
+    QL::issue(qtile, Q + (size_t)(it % BH) * S * D, D, item_qt(it) * BR, S, 0, w, lane, qlo);
+    vm += QL::NLOADS;
+    qmark = vm;
+  };
   RowFrag<E, D> qf;
-  load_row_frag<E, D>(qf, Q + base + (size_t)min(qi, S - 1) * D + h * (D / 2), qi < S);
 
+  // Consumer state: item cit (round cr), its tile kt of nkt.  (Taken before
+  // the first issues, which may move the loader cursor past the first item.)
+  int cr = 0, cit = lit, kt = 0, nkt = lnkt;
+  load_q(lit);
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) issue_next(s);
+  int bh = cit % BH, q0 = item_qt(cit) * BR + qb * 32;
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
   float m = -INFINITY;  // exponent reference (log2 domain), lags the row max by < 2^8
   float l = 0.f;        // this half's running sum of exp2(c*score - m)
 
-  const int kend = CAUSAL ? min(S, qt * BR + BR) : S;
-  const int nkt = (kend + BK - 1) / BK;
-
-  const unsigned lo = LD::lane_offset(w, lane);
+  // Merge the NSPLIT partial (m, l, O) of each query block through the LDS
+  // stage at `buf` (no load targets it), in passes of as many d-blocks as
+  // the stage holds: the first pass also carries m and l, from which every
+  // partial's factor exp2(m_p - max m) is formed once.
+  auto merge = [&](char* buf, bool active) __attribute__((always_inline)) {
+    if constexpr (NSPLIT > 1) {
+      constexpr int HELP = RB * (NSPLIT - 1);
+      constexpr int PERDB = HELP * 16 * 64 * 4;
+      constexpr int MLB = HELP * 2 * 64 * 4;
+      constexpr int DB0 = (STAGE - MLB) / PERDB < NDB ? (STAGE - MLB) / PERDB : NDB;
+      constexpr int DBN = STAGE / PERDB < NDB ? STAGE / PERDB : NDB;
+      static_assert(DBN >= 1, "a d-block of partials fits one stage");
+      constexpr int NPASS = 1 + (NDB - DB0 + DBN - 1) / DBN;
+      float* cb = reinterpret_cast<float*>(buf);
+      float a0 = 1.f, ap[NSPLIT - 1];
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
-    if (s < nkt) LD::issue(smem + s * LD::BYTES, k, v, s * BK, S, w, lane, lo);
+      for (int pass = 0; pass < NPASS; ++pass) {
+        const int dlo = pass == 0 ? 0 : DB0 + (pass - 1) * DBN;
+        const int dhi = pass == 0 ? DB0 : (dlo + DBN < NDB ? dlo + DBN : NDB);
+        const int nv = (pass == 0 ? 2 : 0) + 16 * (dhi - dlo);  // floats per lane per helper
+        const int ov = pass == 0 ? 2 : 0;
+        lds_barrier();  // every wave is done reading the stage (or the previous pass)
+        if (sp != 0 && active) {
+          float* dst = cb + ((qb * (NSPLIT - 1) + sp - 1) * nv) * 64 + lane;
+          if (pass == 0) {
+            dst[0] = m;
+            dst[64] = l;
+          }
+#pragma unroll
+          for (int db = dlo; db < dhi; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[(ov + (db - dlo) * 16 + r) * 64] = oacc[db][r];
+        }
+        lds_barrier();
+        if (sp == 0 && active) {
+          if (pass == 0) {
+            float mp[NSPLIT - 1], lp[NSPLIT - 1];
+            float mx = m;  // finite: split 0 always sees key 0
+#pragma unroll
+            for (int p = 0; p < NSPLIT - 1; ++p) {
+              const float* src = cb + ((qb * (NSPLIT - 1) + p) * nv) * 64 + lane;
+              mp[p] = src[0];
+              lp[p] = src[64];
+              mx = fmaxf(mx, mp[p]);
+            }
+            a0 = fast_exp2(m - mx);
+            l *= a0;
+#pragma unroll
+            for (int p = 0; p < NSPLIT - 1; ++p) {
+              ap[p] = fast_exp2(mp[p] - mx);  // 0 for a split that saw no key
+              l += lp[p] * ap[p];
+            }
+            m = mx;
+          }
+#pragma unroll
+          for (int db = dlo; db < dhi; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float o = oacc[db][r] * a0;
+#pragma unroll
+              for (int p = 0; p < NSPLIT - 1; ++p)
+                o += cb[((qb * (NSPLIT - 1) + p) * nv + ov + (db - dlo) * 16 + r) * 64 + lane] * ap[p];
+              oacc[db][r] = o;
+            }
+        }
+      }
+    }
+  };
 
-  // One staged tile of keys.  When the stages' LDS addresses fit 16-bit
-  // offsets, the loop is unrolled by NST with the stage index constant.
-  auto step = [&](const int kt, auto sc) __attribute__((always_inline)) {
-    const int si = sc;  // kt % NST
-    wait_tiles<LD::NLOADS>(min(NST - 2, nkt - 1 - kt));
-    lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1
-    if (kt + NST - 1 < nkt)
-      LD::issue(smem + ((kt + NST - 1) % NST) * LD::BYTES, k, v, (kt + NST - 1) * BK, S, w, lane, lo);
-    if (!wave_active) return;
-    const char* Kt = smem + si * LD::BYTES;
-    const char* Vt = Kt + TILEB;
-
-      // This wave's 32-key blocks of the tile.  A block is skipped when no key
-      // in it is visible from any of the wave's queries, and masked only when
-      // some but not all of it is (the causal diagonal, the ragged end).  Every
-      // processed block has at least one visible key for every query (block
-      // starts are multiples of 32), so row maxima are finite.
-  #pragma unroll
+  // One staged tile of keys at stream position pos (ring slot sc when
+  // constant).  When the stages' LDS addresses fit 16-bit offsets, the loop
+  // is unrolled by NST with the slot constant.
+  auto step = [&](const int pos, auto sc) __attribute__((always_inline)) {
+    const int si = sc;  // pos % NST
+    int mark = mk[0];
+#pragma unroll
+    for (int i = 1; i < NST; ++i)
+      if (si == i) mark = mk[i];
+    if (kt == 0) mark = max(mark, qmark);  // the item's Q rows too
+    wait_vmem_dyn(vm - mark);
+    lds_barrier();  // tile pos (and on an item's first tile its Q) is in LDS;
+                    // every wave is done with tile pos-1
+    issue_next((si + NST - 1) % NST);
+    if (kt == 0) {
+      // This wave's Q rows, then the next item's Q tile (if any) once every
+      // wave has read its rows.
+      load_row_frag_lds<E, D>(qf, qtile, qb * 32 + n, h, true);
+      const int nit = sched_item(sched, cr + 1, g, G, BH);
+      if (nit < nitems) {
+        lds_barrier();
+        load_q(nit);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // the counts above assume this issue order
+    const int qi = q0 + n;
+    const bool wave_active = q0 < S;
+    if (wave_active) {
+      const char* Kt = smem + si * STAGE;
+      const char* Vt = Kt + TILEB;
+      // This wave's 32-key blocks of the tile.  A block is skipped when no
+      // key in it is visible from any of the wave's queries, and masked only
+      // when some but not all of it is (the causal diagonal, the ragged end).
+      // Every processed block has at least one visible key for every query
+      // (block starts are multiples of 32), so row maxima are finite.
+#pragma unroll
       for (int j = 0; j < KPW; ++j) {
         const int kb = sp + NSPLIT * j;
         const int kk0 = kt * BK + kb * 32;
@@ -107,7 +238,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
           // per-element compare masks in scalar registers); the whole vector
           // is bit-cast (a bit_cast of one ext_vector element is not reliable)
           u32x16 sb = __builtin_bit_cast(u32x16, sacc);
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; ++r) {
             const unsigned out = (unsigned)((lim - (16 * (r >> 3) + (r & 7))) >> 31);
             sb[r] = (sb[r] & ~out) | (0xff800000u & out);
@@ -115,7 +246,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
           sacc = __builtin_bit_cast(f32x16, sb);
         }
         float mx = -INFINITY;  // max of the raw (unscaled) visible scores
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[r], sacc[r + 1]));
         mx = fmaxf(mx, xhalf(mx));
         // Lazy rescaling: exponents are taken against a reference m that may
@@ -127,11 +258,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
           const float alpha = fast_exp2(m - mnew);
           m = mnew;
           l *= alpha;
-  #pragma unroll
+#pragma unroll
           for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
         }
         float rs = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(sacc[r], c, -m));
           sacc[r] = p;
@@ -140,63 +271,59 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
         l += rs;
         RegOperand<E> P;
         P.set(sacc);
-  #pragma unroll
+#pragma unroll
         for (int db = 0; db < NDB; ++db)
           oacc[db] = second_tile<E, D, false>(P, Vt, kb * 32, db * 32, lane, oacc[db]);
       }
-  };
-  if constexpr (NST * LD::BYTES <= 65536) {
-    for_stages<NST>(nkt, step);
-  } else {
-    for (int kt = 0; kt < nkt; ++kt) step(kt, kt % NST);
-  }
-
-  // Merge the NSPLIT partial (m, l, O) of each query block through LDS.
-  l += xhalf(l);
-  if constexpr (NSPLIT > 1) {
-    float* cb = reinterpret_cast<float*>(smem);
-    lds_barrier();  // every wave is done with the K/V tiles (no loads pending)
-    if (sp != 0 && wave_active) {
-      float* dst = cb + ((qb * (NSPLIT - 1) + sp - 1) * NV) * 64 + lane;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dst[(db * 16 + r) * 64] = oacc[db][r];
-      dst[(16 * NDB) * 64] = m;
-      dst[(16 * NDB + 1) * 64] = l;
     }
-    lds_barrier();
-    if (sp != 0 || !wave_active) return;
-#pragma unroll
-    for (int p = 0; p < NSPLIT - 1; ++p) {
-      const float* src = cb + ((qb * (NSPLIT - 1) + p) * NV) * 64 + lane;
-      const float mp = src[(16 * NDB) * 64];
-      const float lp = src[(16 * NDB + 1) * 64];
-      const float mnew = fmaxf(m, mp);  // finite: split 0 always sees key 0
-      const float a0 = fast_exp2(m - mnew), a1 = fast_exp2(mp - mnew);
-      l = l * a0 + lp * a1;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = oacc[db][r] * a0 + src[(db * 16 + r) * 64] * a1;
-      m = mnew;
-    }
-  } else {
-    if (!wave_active) return;
-  }
+    if (++kt < nkt) return;
 
-  const float inv = 1.f / l;
-  if (qi < S) {
-    T* orow = O + base + (size_t)qi * D;
+    // The item is done: merge the splits through the stage just consumed
+    // (the tiles in flight are the next NST-1), then store O and the LSE.
+    l += xhalf(l);
+    merge(smem + si * STAGE, wave_active);
+    if (sp == 0 && wave_active) {
+      const float inv = 1.f / l;
+      if (qi < S) {
+        T* orow = O + ((size_t)bh * S + qi) * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = db * 32 + 8 * j + 4 * h;
-        store4<T>(orow + d, oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
-                  oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+          for (int j = 0; j < 4; ++j) {
+            const int d = db * 32 + 8 * j + 4 * h;
+            store4<T>(orow + d, oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
+                      oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+          }
+        if (h == 0) LSE[(size_t)bh * S + qi] = (m + __log2f(l)) * kLn2;
       }
-    if (h == 0) LSE[(size_t)bh * S + qi] = (m + __log2f(l)) * kLn2;
+      // Only the O stores of a wave whose every lane stores are counted.
+      if (q0 + 31 < S) vm += 4 * NDB;
+    }
+    // Next item.
+    cit = sched_item(sched, ++cr, g, G, BH);
+    kt = 0;
+    if (cit < nitems) {
+      nkt = item_nkt(cit);
+      bh = cit % BH;
+      q0 = item_qt(cit) * BR + qb * 32;
+    }
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
+    m = -INFINITY;
+    l = 0.f;
+  };
+
+  // Tiles this workgroup consumes: the key tiles of all its items.
+  int ntiles = 0;
+  for (int r = 0;; ++r) {
+    const int it = sched_item(sched, r, g, G, BH);
+    if (it >= nitems) break;
+    ntiles += item_nkt(it);
+  }
+  if constexpr (NST * STAGE <= 65536) {
+    for_stages<NST>(ntiles, step);
+  } else {
+    for (int pos = 0; pos < ntiles; ++pos) step(pos, pos % NST);
   }
 }
 
@@ -207,12 +334,22 @@ static hipError_t launch(const FwdArgs& a) {
   constexpr int KPW = is_bf16<E>() ? ATTN_FWD_KPW_BF16 : ATTN_FWD_KPW_F32;
   constexpr int NST = is_bf16<E>() ? ATTN_FWD_NST_BF16 : ATTN_FWD_NST_F32;
   using T = typename E::T;
+  constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>;
   constexpr int BR = 32 * (NW / NSPLIT);
   const int nqt = (a.S + BR - 1) / BR;
-  dim3 grid(a.BH, nqt);
-  hipLaunchKernelGGL((fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>), grid, dim3(NW * 64), 0,
-                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.S,
-                     a.scale * kLog2e);
+  const int nitems = a.BH * nqt;
+  const int grid = std::min(nitems, resident_workgroups<kern>(NW * 64));
+  // work of a query tile: its key tiles
+  constexpr int BK = 32 * NSPLIT * KPW;
+  std::vector<int> works(nqt);
+  for (int c = 0; c < nqt; ++c) {
+    const int qt = nqt - 1 - c;
+    const int kend = CAUSAL ? std::min(a.S, qt * BR + BR) : a.S;
+    works[c] = (kend + BK - 1) / BK;
+  }
+  const Sched sched = make_sched(grid, a.BH, works);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
+                     (const T*)a.v, (T*)a.o, a.lse, a.S, a.scale * kLog2e, a.BH, nitems, sched);
   return hipGetLastError();
 }
 

@@ -5,7 +5,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "attn_device.hpp"
 
 // Launch shapes per kernel and contract: NW waves per workgroup, NSPLIT
 // waves sharing each 32-row block (splitting its inner loop), KPW 32-row
@@ -69,7 +74,7 @@
 #define ATTN_FWD_NST_F32 2
 #endif
 #ifndef ATTN_FWD_NST_BF16
-#define ATTN_FWD_NST_BF16 3
+#define ATTN_FWD_NST_BF16 2
 #endif
 #ifndef ATTN_DQ_NST_F32
 #define ATTN_DQ_NST_F32 2
@@ -137,6 +142,78 @@ inline int resident_workgroups(int threads) {
   v = ncu * nb;
   cache[dev].store(v, std::memory_order_relaxed);
   return v;
+}
+
+// CUs per XCD of the current device (8 XCDs), cached per device.
+inline int cus_per_xcd() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || ncu < 8)
+    ncu = 8;
+  v = ncu / 8;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// The pattern of a persistent launch of G workgroups over BH heads whose
+// items fall in ncls work classes (class c has one item per head, of work
+// works[c]).  Items are placed largest first on the XCD's CU with the least
+// total work (ties: lowest CU), on that CU's least-loaded slot; slots j and
+// j + cux of an XCD share a CU (the dispatcher fills every CU once before
+// it gives any a second workgroup).  Cached per argument set; M = 0 when the
+// pattern does not apply or fit (the kernels then use the snake order).
+inline Sched make_sched(int G, int BH, const std::vector<int>& works) {
+  Sched s;
+  s.M = 0;
+  s.R = 0;
+  const int ncls = (int)works.size();
+  if (G % 8 || BH % 8 || G <= 0) return s;
+  const int M = G / 8, hx = BH / 8;
+  if (hx > 255 || ncls > 255) return s;
+  int cux = cus_per_xcd();
+  if (M % cux) cux = M;  // fewer workgroups than CUs: one per CU
+  struct Entry { int G, BH, cux; std::vector<int> works; Sched s; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.G == G && e.BH == BH && e.cux == cux && e.works == works) return e.s;
+  const int spc = M / cux;
+  std::vector<int> order(ncls);
+  for (int c = 0; c < ncls; ++c) order[c] = c;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return works[a] > works[b]; });
+  std::vector<long> load(M, 0);
+  std::vector<std::vector<uint16_t>> lists(M);
+  for (int c : order)
+    for (int u = 0; u < hx; ++u) {
+      int bcu = 0;
+      long bsum = -1;
+      for (int cu = 0; cu < cux; ++cu) {
+        long sum = 0;
+        for (int t = 0; t < spc; ++t) sum += load[cu + cux * t];
+        if (bsum < 0 || sum < bsum) { bsum = sum; bcu = cu; }
+      }
+      int bj = bcu;
+      for (int t = 1; t < spc; ++t)
+        if (load[bcu + cux * t] < load[bj]) bj = bcu + cux * t;
+      load[bj] += works[c];
+      lists[bj].push_back((uint16_t)((c << 8) | u));
+    }
+  size_t R = 0;
+  for (const auto& l : lists) R = std::max(R, l.size());
+  if (M > kSchedSlots || (R - 1) * M > (size_t)kSchedEntries) return s;
+  for (int j = 0; j < M; ++j) s.first[j] = lists[j].empty() ? 0xffff : lists[j][0];
+  for (size_t r = 1; r < R; ++r)
+    for (int j = 0; j < M; ++j) s.ent[(r - 1) * M + j] = r < lists[j].size() ? lists[j][r] : 0xffff;
+  s.M = M;
+  s.R = (int)R;
+  if (cache.size() >= 32) cache.erase(cache.begin());
+  cache.push_back(Entry{G, BH, cux, works, s});
+  return s;
 }
 
 hipError_t launch_fwd(const FwdArgs& a);
