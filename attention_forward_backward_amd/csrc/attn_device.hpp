@@ -222,17 +222,24 @@ constexpr int kSchedEntries = 1280;
 struct Sched {
   int M;  // slots per XCD, or 0
   int R;  // rounds in the table
-  uint16_t first[kSchedSlots];
-  uint16_t ent[kSchedEntries];
+  alignas(4) uint16_t first[kSchedSlots];
+  alignas(4) uint16_t ent[kSchedEntries];
 };
 
 // Item of round r of workgroup g (a value >= every item count once g has no
 // more items).
+// The 16-bit entries are read as the 32-bit words that hold them: with a
+// wave-uniform index those are scalar loads, while a 16-bit read would be a
+// vector load (and a vector-memory wait that also drains the tile loads).
+__device__ inline int sched_entry(const uint16_t* a, int i) {
+  const uint32_t v = reinterpret_cast<const uint32_t*>(a)[i >> 1];
+  return (int)((i & 1) ? v >> 16 : v & 0xffffu);
+}
 __device__ inline int sched_item(const Sched& s, int r, int g, int G, int BH) {
-  const int e0 = s.first[(g >> 3) & (kSchedSlots - 1)];
+  const int e0 = sched_entry(s.first, (g >> 3) & (kSchedSlots - 1));
   if (s.M == 0) return snake_item(r, g, G);
   if (r >= s.R) return 0x7fffffff;
-  const int e = r == 0 ? e0 : s.ent[(r - 1) * s.M + (g >> 3)];
+  const int e = r == 0 ? e0 : sched_entry(s.ent, (r - 1) * s.M + (g >> 3));
   if (e == 0xffff) return 0x7fffffff;
   return (e >> 8) * BH + 8 * (e & 255) + (g & 7);
 }

@@ -42,8 +42,13 @@ KERNEL_SYMBOL = {"attn_fwd": "fwd_kernel", "attn_bwd_prep": "bwd_prep_kernel",
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=300)
+    # The GPU reaches its sustained clock only after some tens of milliseconds
+    # of continuous load; a short warm-up times the clock ramp instead of the
+    # kernels (measured on MI355X at B8 H12 S512 D64 f32: 10 warm-up steps
+    # give 159.7 us/step, 300 give 141.5, and 2000 timed steps after those
+    # 141.2).  300 steps are about 45 ms of f32 work.
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--config", default="decoder_step")
     p.add_argument("--dtypes", default="f32,bf16", help="first one is the headline value")
     p.add_argument("--seed", type=int, default=0)
