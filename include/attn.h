@@ -15,8 +15,11 @@
  *
  * Conventions shared by every entry point:
  *  - Pointers named q, k, v, o, dout, dq, dk, dv, lse, workspace are DEVICE
- *    pointers owned by the caller.  The library never allocates, frees or
- *    keeps a pointer after the call returns; it holds no state.
+ *    pointers owned by the caller.  The library never allocates or frees
+ *    device memory and keeps no pointer after the call returns; its only
+ *    state is two host-side caches keyed by device and shape (resident
+ *    workgroups per kernel, the static work schedule), filled on first use
+ *    under a lock, so calls from several host threads are safe.
  *  - Layout: [batch, heads, seq, head_dim] contiguous row-major for Q, K, V,
  *    O, dO, dQ, dK, dV; LSE is [batch, heads, seq] float32.  Query and key
  *    length are both `seq` (self-attention).
