@@ -15,13 +15,13 @@ import re
 __all__ = ["AttnError", "lib", "attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_workspace_size", "attn_bwd_workspace_size_min",
            "attn_status_string", "attn_version",
-           "ATTN_F32", "ATTN_BF16", "STATUS", "LIB_PATH", "HEADER_PATH"]
+           "ATTN_F32", "ATTN_BF16", "ATTN_F32_BF16FWD", "STATUS", "LIB_PATH", "HEADER_PATH"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "attn.h")
 
-ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_F32, ATTN_BF16, ATTN_F32_BF16FWD = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
           3: "ATTN_ERR_WORKSPACE", 4: "ATTN_ERR_HIP"}
 
@@ -133,14 +133,25 @@ def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
 
-def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
-    """O, LSE <- attention(Q, K, V); tensors [B,H,S,D] (LSE [B,H,S] float32)."""
+def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None,
+             bf16_operands: bool = False) -> None:
+    """O, LSE <- attention(Q, K, V); tensors [B,H,S,D] (LSE [B,H,S] float32).
+
+    lse=None: inference-only forward (no LSE stored).  bf16_operands=True with
+    float32 tensors selects ATTN_F32_BF16FWD (operands rounded to bf16 inside
+    the kernel, f32 accumulation and stores)."""
     B, H, S, D = q.shape
     _check({"q": q, "k": k, "v": v, "o": o}, (B, H, S, D), q.dtype)
-    _check_f32({"lse": lse}, (B, H, S))
-    code = lib().attn_fwd(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                          o.data_ptr(), lse.data_ptr(), B, H, S, D, int(causal),
-                          float(scale), _stream(stream))
+    if lse is not None:
+        _check_f32({"lse": lse}, (B, H, S))
+    code = _dtype_code(q)
+    if bf16_operands:
+        if code != ATTN_F32:
+            raise TypeError("bf16_operands applies to float32 tensors")
+        code = ATTN_F32_BF16FWD
+    code = lib().attn_fwd(code, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          o.data_ptr(), 0 if lse is None else lse.data_ptr(), B, H, S, D,
+                          int(causal), float(scale), _stream(stream))
     _raise("attn_fwd", code)
 
 

@@ -1,8 +1,9 @@
 // attn_api.hip -- the C ABI declared in include/attn.h.
 //
 // Validates every argument on the host before anything is enqueued, then
-// hands a launch descriptor to the kernel launchers.  Stateless: nothing is
-// allocated, cached or retained between calls.
+// hands a launch descriptor to the kernel launchers.  No device memory is
+// allocated and no pointer is retained between calls (the launchers cache
+// only occupancy figures and schedule patterns, on the host).
 #include <math.h>
 #include <stdint.h>
 
@@ -15,7 +16,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 attn_status_t check_shape(attn_dtype_t dtype, int batch, int heads, int seq, int head_dim,
                           int causal, float scale, bool check_scale) {
-  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F32_BF16FWD) return ATTN_ERR_UNSUPPORTED;
   if (batch <= 0 || heads <= 0 || seq <= 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (check_scale && !(isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
@@ -84,9 +85,11 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* q, const void* k, const v
                        float scale, void* stream) {
   attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
-  if ((st = check_ptrs({q, k, v, o, lse})) != ATTN_OK) return st;
+  if ((st = check_ptrs({q, k, v, o})) != ATTN_OK) return st;
+  if (lse != nullptr && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;  // NULL: no LSE
   attn::FwdArgs a;
   a.bf16 = dtype == ATTN_BF16;
+  a.bf16_operands = dtype == ATTN_F32_BF16FWD;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.BH = batch * heads; a.S = seq; a.D = head_dim;
   a.causal = causal != 0; a.scale = scale;

@@ -59,7 +59,30 @@ struct EBF16 {
   }
 };
 
-template <class E> __host__ __device__ constexpr bool is_bf16() { return E::KL == 8; }
+// f32 storage with bf16 MFMA operands: the forward of the pages' practical
+// contract ("Meganeura", Section 4.2: eligible forward matrix and attention
+// inputs rounded locally to reduced precision, f32 accumulation, f32
+// stores).  Tiles stay f32 in LDS; Q, K and V are rounded to bf16
+// (nearest-even) as they become MFMA operands, and P as in EBF16.
+struct EF32B {
+  using T = float;
+  static constexpr int KL = 8;
+  using Frag = bf16x8;
+  __device__ static inline f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Storage (tile layout, loads, stores) is bf16.
+template <class E> __host__ __device__ constexpr bool is_bf16() { return sizeof(typename E::T) == 2; }
+// MFMA operands are bf16 (8 k-values per lane).
+template <class E> __host__ __device__ constexpr bool mma_bf16() { return E::KL == 8; }
+
+// Four floats rounded to bf16 (nearest-even) into elements 4j .. 4j+3 of v.
+__device__ inline void put_bf16x4(bf16x8& v, int j, f32x4 x) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[4 * j + e] = (__bf16)x[e];
+}
 
 // ------------------------------------------------------------------ lane maps
 __device__ inline int pi32(int m) {
@@ -102,6 +125,9 @@ template <class E, int D>
 __device__ inline void set_frag_chunk(RowFrag<E, D>& rf, int c, u32x4 x) {
   if constexpr (is_bf16<E>()) {
     rf.f[c] = __builtin_bit_cast(bf16x8, x);
+  } else if constexpr (mma_bf16<E>()) {
+    // f32 storage, bf16 operands: chunk c is half (c & 1) of fragment c / 2
+    put_bf16x4(rf.f[c >> 1], c & 1, __builtin_bit_cast(f32x4, x));
   } else {
     // bit-cast the whole vector: a bit_cast of one ext_vector element is
     // not reliable here (it read element 0 for every e)
@@ -447,6 +473,21 @@ __device__ inline f32x16 dot_tile(const char* tile, int row, int h, const RowFra
                                   f32x16 acc) {
   using TL = Tile<E, D>;
   constexpr int NCH = TL::CPR / 2;
+  if constexpr (!is_bf16<E>() && mma_bf16<E>()) {
+    // f32 tile, bf16 operands: two 16-byte chunks (8 d-values) per MFMA
+#pragma unroll
+    for (int cc = 0; cc < NCH / 2; ++cc) {
+      bf16x8 a;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int chunk = h * NCH + 2 * cc + j;
+        put_bf16x4(a, j, *reinterpret_cast<const f32x4*>(tile + row * TL::ROWB +
+                                                          ((chunk ^ TL::swz(row)) << 4)));
+      }
+      acc = E::mma(a, b.f[cc], acc);
+    }
+    return acc;
+  }
 #pragma unroll
   for (int cc = 0; cc < NCH; ++cc) {
     const int chunk = h * NCH + cc;
@@ -490,6 +531,9 @@ struct RegOperand<EBF16> {
   }
 };
 
+template <>
+struct RegOperand<EF32B> : RegOperand<EBF16> {};
+
 // acc += product over the 32 logical rows row0 .. row0+31 of an LDS tile X:
 //   REG_IS_A = true : acc[m][n] += sum_k R[m = this lane's row][k] * X[k][col0 + n]
 //   REG_IS_A = false: acc[m][n] += sum_k X[k][col0 + m] * R[k][n = this lane's column]
@@ -523,6 +567,15 @@ __device__ inline void read_kslot_operand(RegOperand<E>& X, const char* tile, in
       const s16x8 all = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
       X.v[u] = __builtin_bit_cast(bf16x8, all);
     }
+  } else if constexpr (mma_bf16<E>()) {
+    // f32 tile, bf16 operands: the 8 k-slot rows of column col0 + n, one
+    // element each, rounded
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        X.v[u][t] = (__bf16)*reinterpret_cast<const float*>(
+            tile + TL::off(row0 + 16 * u + 8 * h + t, col0 + n));
   } else {
 #pragma unroll
     for (int w = 0; w < 16; ++w)
@@ -535,7 +588,7 @@ __device__ inline f32x16 second_tile(const RegOperand<E>& R, const char* tile, i
                                      int lane, f32x16 acc) {
   RegOperand<E> X;
   read_kslot_operand<E, D>(X, tile, row0, col0, lane);
-  constexpr int NU = is_bf16<E>() ? 2 : 16;
+  constexpr int NU = 16 / E::KL;
 #pragma unroll
   for (int u = 0; u < NU; ++u) acc = REG_IS_A ? E::mma(R.v[u], X.v[u], acc) : E::mma(X.v[u], R.v[u], acc);
   return acc;

@@ -39,6 +39,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O,
     float* __restrict__ LSE, int S, float c, int BH, int nitems, const Sched sched) {
+  // LSE may be null (an inference-only forward stores no LSE).
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-query blocks per item
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
             store4<T>(orow + d, oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
                       oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
           }
-        if (h == 0) LSE[(size_t)bh * S + qi] = (m + __log2f(l)) * kLn2;
+        if (h == 0 && LSE != nullptr) LSE[(size_t)bh * S + qi] = (m + __log2f(l)) * kLn2;
       }
       // Only the O stores of a wave whose every lane stores are counted.
       if (q0 + 31 < S) vm += 4 * NDB;
@@ -369,7 +370,8 @@ static hipError_t launch_d(const FwdArgs& a) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  return a.bf16 ? launch_d<EBF16>(a) : launch_d<EF32>(a);
+  if (a.bf16) return launch_d<EBF16>(a);
+  return a.bf16_operands ? launch_d<EF32B>(a) : launch_d<EF32>(a);
 }
 
 }  // namespace attn

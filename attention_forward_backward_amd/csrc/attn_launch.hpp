@@ -97,10 +97,11 @@
 namespace attn {
 
 struct FwdArgs {
-  bool bf16;
+  bool bf16;           // bf16 storage and operands
+  bool bf16_operands;  // f32 storage, bf16 MFMA operands
   const void *q, *k, *v;
   void* o;
-  float* lse;
+  float* lse;  // null: not stored
   int BH, S, D;
   bool causal;
   float scale;

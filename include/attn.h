@@ -30,6 +30,8 @@
  *    bf16) and f32 accumulation, softmax statistics and LSE.  These are the
  *    two arithmetic contracts of the pages' Section 4.2 (strict f32 versus a
  *    reduced-input matrix path), here with bf16 in place of f16.
+ *    ATTN_F32_BF16FWD (float32 tensors, bf16-rounded forward operands,
+ *    strict f32 backward) is the pages' practical mixed contract.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *    and the call returns; outputs are valid once the caller synchronises
  *    the stream.  Faults inside a kernel surface at that synchronisation.
@@ -64,8 +66,12 @@ typedef enum {
 } attn_status_t;
 
 typedef enum {
-  ATTN_F32 = 0,  /* strict float32 contract */
-  ATTN_BF16 = 1  /* bf16 storage and MFMA operands, f32 accumulation */
+  ATTN_F32 = 0,         /* strict float32 contract */
+  ATTN_BF16 = 1,        /* bf16 storage and MFMA operands, f32 accumulation */
+  ATTN_F32_BF16FWD = 2  /* float32 storage; the forward rounds its MFMA
+                           operands (Q, K, V, P) to bf16 and accumulates and
+                           stores in f32; every backward entry point treats
+                           it as ATTN_F32 (strict) */
 } attn_dtype_t;
 
 /*
@@ -73,7 +79,14 @@ typedef enum {
  *   in : q, k, v   [B,H,S,D] dtype
  *   out: o         [B,H,S,D] dtype   softmax(scale * Q K^T, masked) V
  *        lse       [B,H,S]   float32 natural-log row normaliser, scale
- *                                    included; the backward reads it
+ *                                    included; the backward reads it.  NULL
+ *                                    skips it: an inference-only forward
+ *                                    (pages' Section 4.3, "one complete
+ *                                    no-gradient forward pass").
+ * ATTN_F32_BF16FWD is the pages' practical contract (Section 4.2: forward
+ * matrix and attention inputs rounded locally to reduced precision, f32
+ * accumulation and stores, backward kept f32): tensors as ATTN_F32, MFMA
+ * operands rounded to bf16 inside the kernel.
  * One kernel launch.
  */
 attn_status_t attn_fwd(attn_dtype_t dtype,

@@ -41,14 +41,15 @@ def _bwd(dtype=0, ptr=FAKE, ws=FAKE, wsb=1 << 20, B=1, H=1, S=8, D=64, causal=1,
 
 def test_fwd_validation():
     assert _fwd(q=None) == 1
-    assert _fwd(lse=None) == 1
+    assert _fwd(lse=MIS) == 1                      # lse may be NULL (no LSE), not misaligned
     assert _fwd(v=MIS) == 1
     assert _fwd(B=0) == 1 and _fwd(H=-1) == 1 and _fwd(S=0) == 1
     assert _fwd(causal=2) == 1
     assert _fwd(scale=math.inf) == 1 and _fwd(scale=math.nan) == 1
     assert _fwd(scale=0.0) == 1 and _fwd(scale=-0.125) == 1
     assert _fwd(D=48) == 2 and _fwd(D=256) == 2 and _fwd(D=16) == 2
-    assert _fwd(dtype=7) == 2
+    assert _fwd(dtype=7) == 2 and _fwd(dtype=3) == 2
+    assert _fwd(dtype=2, D=48) == 2 and _fwd(dtype=2, q=None) == 1   # ATTN_F32_BF16FWD is validated alike
     assert _fwd(B=1 << 16, H=1 << 16) == 1          # B*H beyond int
     assert _fwd(S=1 << 26, D=64) == 1               # S*D beyond int
 
@@ -87,6 +88,9 @@ def test_workspace_size():
     assert wfull(0, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4 + 8 * 12 * 512 * 512 * 4
     assert wfull(1, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4 + 8 * 12 * 512 * 512 * 2
     assert wfull(0, 32, 8, 197, 64, False) == r256(2 * 32 * 8 * 197 * 4) + r256(32 * 8 * 256 * 256 * 4)
+    # the practical contract (bf16 forward operands, strict f32 backward) sizes as f32
+    assert wfull(2, 8, 12, 512, 64, True) == wfull(0, 8, 12, 512, 64, True)
+    assert wmin(2, 32, 8, 197, 64, False) == wmin(0, 32, 8, 197, 64, False)
     for f in (wmin, wfull):
         assert f(0, 1, 1, 8, 48, True) == 0 and f(0, 0, 1, 8, 64, True) == 0
         assert f(5, 1, 1, 8, 64, True) == 0
