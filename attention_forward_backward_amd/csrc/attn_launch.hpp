@@ -162,27 +162,21 @@ inline int cus_per_xcd() {
 
 // The pattern of a persistent launch of G workgroups over BH heads whose
 // items fall in ncls work classes (class c has one item per head, of work
-// works[c]).  Items are placed largest first on the XCD's CU with the least
-// total work (ties: lowest CU), on that CU's least-loaded slot; slots j and
-// j + cux of an XCD share a CU (the dispatcher fills every CU once before
-// it gives any a second workgroup).  Cached per argument set; M = 0 when the
-// pattern does not apply or fit (the kernels then use the snake order).
-inline Sched make_sched(int G, int BH, const std::vector<int>& works) {
+// works[c]), for an XCD of cux CUs.  Items are placed largest first on the
+// XCD's CU with the least total work (ties: lowest CU), on that CU's
+// least-loaded slot; slots j and j + cux of an XCD share a CU (the
+// dispatcher fills every CU once before it gives any a second workgroup).
+// M = 0 when the pattern does not apply or fit (the kernels then use the
+// snake order).  Pure host function.
+inline Sched build_sched(int G, int BH, const std::vector<int>& works, int cux) {
   Sched s;
   s.M = 0;
   s.R = 0;
   const int ncls = (int)works.size();
-  if (G % 8 || BH % 8 || G <= 0) return s;
+  if (G % 8 || BH % 8 || G <= 0 || ncls <= 0) return s;
   const int M = G / 8, hx = BH / 8;
-  if (hx > 255 || ncls > 255) return s;
-  int cux = cus_per_xcd();
-  if (M % cux) cux = M;  // fewer workgroups than CUs: one per CU
-  struct Entry { int G, BH, cux; std::vector<int> works; Sched s; };
-  static std::mutex mu;
-  static std::vector<Entry> cache;
-  std::lock_guard<std::mutex> lock(mu);
-  for (const Entry& e : cache)
-    if (e.G == G && e.BH == BH && e.cux == cux && e.works == works) return e.s;
+  if (M > kSchedSlots || hx > 255 || ncls > 255) return s;
+  if (cux <= 0 || M % cux) cux = M;  // fewer workgroups than CUs: one per CU
   const int spc = M / cux;
   std::vector<int> order(ncls);
   for (int c = 0; c < ncls; ++c) order[c] = c;
@@ -206,12 +200,25 @@ inline Sched make_sched(int G, int BH, const std::vector<int>& works) {
     }
   size_t R = 0;
   for (const auto& l : lists) R = std::max(R, l.size());
-  if (M > kSchedSlots || (R - 1) * M > (size_t)kSchedEntries) return s;
+  if ((R - 1) * M > (size_t)kSchedEntries) return s;
   for (int j = 0; j < M; ++j) s.first[j] = lists[j].empty() ? 0xffff : lists[j][0];
   for (size_t r = 1; r < R; ++r)
     for (int j = 0; j < M; ++j) s.ent[(r - 1) * M + j] = r < lists[j].size() ? lists[j][r] : 0xffff;
   s.M = M;
   s.R = (int)R;
+  return s;
+}
+
+// build_sched for the current device, cached per argument set.
+inline Sched make_sched(int G, int BH, const std::vector<int>& works) {
+  const int cux = cus_per_xcd();
+  struct Entry { int G, BH, cux; std::vector<int> works; Sched s; };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.G == G && e.BH == BH && e.cux == cux && e.works == works) return e.s;
+  const Sched s = build_sched(G, BH, works, cux);
   if (cache.size() >= 32) cache.erase(cache.begin());
   cache.push_back(Entry{G, BH, cux, works, s});
   return s;
