@@ -25,9 +25,13 @@ and, for a loss L whose gradient with respect to O is dO,
     dS_ij = P_ij (dP_ij - D_i)
     dQ_i  = s sum_j dS_ij K_j ,   dK_j = s sum_i dS_ij Q_i
 
-Readings where the pages are silent: tensors are [B, H, S, D] row-major; in the
-causal case key j is visible from query i iff j <= i; the scale multiplies the
-scores before the softmax; LSE uses the natural logarithm.
+Readings where the pages are silent: tensors are [B, H, S, D] row-major
+(queries [B, H, Sq, D], keys and values [B, H, Sk, D]); batch b has L_b <= Sk
+valid keys (kv_len; all Sk when absent), and key j is visible from query i iff
+j < L_b and, in the causal case, j <= i + L_b - Sq (the causal diagonal is
+aligned with the end of the valid keys; with Sq = Sk = L_b this is j <= i); a
+query row with no visible key has O = 0, LSE = -inf and no gradient; the scale
+multiplies the scores before the softmax; LSE uses the natural logarithm.
 
 Everything is float64, one (b, h) slice at a time, with the full S x S score
 matrix: no tiling, no online softmax, no reordering beyond what numpy's matmul
@@ -38,46 +42,56 @@ from __future__ import annotations
 import numpy as np
 
 
-def _visible(seq: int, causal: bool) -> np.ndarray:
-    """Boolean S x S matrix, True where query i may attend to key j."""
+def _visible(sq: int, sk: int, causal: bool, nvalid=None) -> np.ndarray:
+    """Boolean Sq x Sk matrix, True where query i may attend to key j."""
+    L = sk if nvalid is None else int(nvalid)
+    i = np.arange(sq)[:, None]
+    j = np.arange(sk)[None, :]
+    vis = j < L
     if causal:
-        return np.tril(np.ones((seq, seq), dtype=bool))
-    return np.ones((seq, seq), dtype=bool)
+        vis = vis & (j <= i + (L - sq))
+    return vis
 
 
-def _slice_softmax(q, k, causal, scale):
-    """Scores, row LSE and probabilities for one (b, h) slice, in float64."""
+def _slice_softmax(q, k, causal, scale, nvalid=None):
+    """Scores, row LSE and probabilities for one (b, h) slice, in float64.
+    Rows with no visible key get P = 0 and LSE = -inf."""
     s = scale * (q @ k.T)
-    vis = _visible(q.shape[0], causal)
+    vis = _visible(q.shape[0], k.shape[0], causal, nvalid)
     s = np.where(vis, s, -np.inf)
-    m = s.max(axis=1, keepdims=True)  # every row has key 0 visible
-    e = np.exp(s - m)
+    any_vis = vis.any(axis=1, keepdims=True)
+    m = np.where(any_vis, s.max(axis=1, keepdims=True), 0.0)
+    e = np.where(vis, np.exp(s - m), 0.0)
     l = e.sum(axis=1, keepdims=True)
-    lse = m + np.log(l)
-    p = e / l
+    lse = np.where(any_vis, m + np.log(np.where(any_vis, l, 1.0)), -np.inf)
+    p = e / np.where(any_vis, l, 1.0)
     return s, lse[:, 0], p
+
+
+def _nvalid(kv_len, b):
+    return None if kv_len is None else int(kv_len[b])
 
 
 def _as64(*arrays):
     return [np.asarray(a, dtype=np.float64) for a in arrays]
 
 
-def attention_forward(q, k, v, causal: bool, scale: float):
-    """O [B,H,S,D] and LSE [B,H,S] in float64."""
+def attention_forward(q, k, v, causal: bool, scale: float, kv_len=None):
+    """O [B,H,Sq,D] and LSE [B,H,Sq] in float64 (kv_len: valid keys per batch)."""
     q, k, v = _as64(q, k, v)
-    bsz, nh, seq, hd = q.shape
-    o = np.empty((bsz, nh, seq, v.shape[-1]))
-    lse = np.empty((bsz, nh, seq))
+    bsz, nh, sq, hd = q.shape
+    o = np.empty((bsz, nh, sq, v.shape[-1]))
+    lse = np.empty((bsz, nh, sq))
     for b in range(bsz):
         for h in range(nh):
-            _, lse_bh, p = _slice_softmax(q[b, h], k[b, h], causal, scale)
+            _, lse_bh, p = _slice_softmax(q[b, h], k[b, h], causal, scale, _nvalid(kv_len, b))
             o[b, h] = p @ v[b, h]
             lse[b, h] = lse_bh
     return o, lse
 
 
-def attention_backward(q, k, v, do, causal: bool, scale: float):
-    """dQ, dK, dV [B,H,S,D] and D = rowsum(dO * O) [B,H,S], in float64.
+def attention_backward(q, k, v, do, causal: bool, scale: float, kv_len=None):
+    """dQ, dK, dV and D = rowsum(dO * O) [B,H,Sq], in float64.
 
     O is the oracle's own forward output (the exact O), so D is exact too.
     """
@@ -88,7 +102,7 @@ def attention_backward(q, k, v, do, causal: bool, scale: float):
     delta = np.empty(q.shape[:3])
     for b in range(q.shape[0]):
         for h in range(q.shape[1]):
-            _, _, p = _slice_softmax(q[b, h], k[b, h], causal, scale)
+            _, _, p = _slice_softmax(q[b, h], k[b, h], causal, scale, _nvalid(kv_len, b))
             o = p @ v[b, h]
             dv[b, h] = p.T @ do[b, h]
             dp = do[b, h] @ v[b, h].T
@@ -100,33 +114,40 @@ def attention_backward(q, k, v, do, causal: bool, scale: float):
     return dq, dk, dv, delta
 
 
-def attention_probs(q, k, causal: bool, scale: float):
-    """P [B,H,S,S] (float64), for pins and diagnostics on small shapes."""
+def attention_probs(q, k, causal: bool, scale: float, kv_len=None):
+    """P [B,H,Sq,Sk] (float64), for pins and diagnostics on small shapes."""
     q, k = _as64(q, k)
     p = np.empty(q.shape[:3] + (k.shape[2],))
     for b in range(q.shape[0]):
         for h in range(q.shape[1]):
-            p[b, h] = _slice_softmax(q[b, h], k[b, h], causal, scale)[2]
+            p[b, h] = _slice_softmax(q[b, h], k[b, h], causal, scale, _nvalid(kv_len, b))[2]
     return p
 
 
-def loss(q, k, v, do, causal: bool, scale: float) -> float:
+def loss(q, k, v, do, causal: bool, scale: float, kv_len=None) -> float:
     """The scalar L = sum(O * dO), whose gradient with respect to O is dO."""
-    o, _ = attention_forward(q, k, v, causal, scale)
+    o, _ = attention_forward(q, k, v, causal, scale, kv_len)
     return float((o * np.asarray(do, dtype=np.float64)).sum())
 
 
-def attention_forward_rows(q, k, v, causal: bool, scale: float, b: int, h: int, rows):
+def attention_forward_rows(q, k, v, causal: bool, scale: float, b: int, h: int, rows,
+                           kv_len=None):
     """O and LSE for selected query rows of one (b, h) slice, each row on its own.
 
     For spot checks at sizes where the full oracle is slow: row i uses only
-    its visible keys, exactly as in ``attention_forward``.
+    its visible keys (the first min(L, i + 1 + L - Sq) when causal, else the
+    first L), exactly as in ``attention_forward``.
     """
+    sq = q.shape[2]
     q, k, v = _as64(q[b, h], k[b, h], v[b, h])
-    seq = k.shape[0]
+    L = k.shape[0] if kv_len is None else int(kv_len[b])
     outs, lses = [], []
     for i in rows:
-        n_vis = i + 1 if causal else seq
+        n_vis = max(0, min(L, i + 1 + L - sq)) if causal else L
+        if n_vis == 0:
+            outs.append(np.zeros(v.shape[1]))
+            lses.append(-np.inf)
+            continue
         s = scale * (k[:n_vis] @ q[i])
         m = s.max()
         e = np.exp(s - m)

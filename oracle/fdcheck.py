@@ -17,7 +17,7 @@ from .attention import loss
 
 
 def fd_grad(q, k, v, do, causal: bool, scale: float, which: str, coords,
-            rel_step: float = 1e-6):
+            rel_step: float = 1e-6, kv_len=None):
     """Central-difference dL/d<which> at the given flat coordinates."""
     arrays = {n: np.array(a, dtype=np.float64, copy=True)
               for n, a in (("q", q), ("k", k), ("v", v))}
@@ -27,19 +27,19 @@ def fd_grad(q, k, v, do, causal: bool, scale: float, which: str, coords,
         orig = x[c]
         h = rel_step * max(1.0, abs(orig))
         x[c] = orig + h
-        lp = loss(arrays["q"], arrays["k"], arrays["v"], do, causal, scale)
+        lp = loss(arrays["q"], arrays["k"], arrays["v"], do, causal, scale, kv_len)
         x[c] = orig - h
-        lm = loss(arrays["q"], arrays["k"], arrays["v"], do, causal, scale)
+        lm = loss(arrays["q"], arrays["k"], arrays["v"], do, causal, scale, kv_len)
         x[c] = orig
         out[n] = (lp - lm) / (2.0 * h)
     return out
 
 
-def fd_full(q, k, v, do, causal: bool, scale: float, rel_step: float = 1e-6):
+def fd_full(q, k, v, do, causal: bool, scale: float, rel_step: float = 1e-6, kv_len=None):
     """Central differences over every element of Q, K and V (tiny shapes only)."""
     res = {}
     for which, a in (("q", q), ("k", k), ("v", v)):
         n = int(np.prod(np.shape(a)))
         res[which] = fd_grad(q, k, v, do, causal, scale, which, range(n),
-                             rel_step).reshape(np.shape(a))
+                             rel_step, kv_len).reshape(np.shape(a))
     return res
