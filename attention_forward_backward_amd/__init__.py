@@ -14,6 +14,8 @@ import re
 
 __all__ = ["AttnError", "lib", "attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_workspace_size", "attn_bwd_workspace_size_min",
+           "attn_fwd_cross", "attn_bwd_cross", "attn_bwd_cross_workspace_size",
+           "attn_bwd_cross_workspace_size_min",
            "attn_status_string", "attn_version",
            "ATTN_F32", "ATTN_BF16", "ATTN_F32_BF16FWD", "STATUS", "LIB_PATH", "HEADER_PATH"]
 
@@ -36,6 +38,11 @@ _lib = None
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "attn_fwd": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_fwd_cross": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _F, _P]),
+    "attn_bwd_cross": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                            _I, _I, _I, _I, _I, _P, _I, _F, _P]),
+    "attn_bwd_cross_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "attn_bwd_cross_workspace_size_min": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "attn_bwd_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "attn_bwd_workspace_size_min": (_Z, [_I, _I, _I, _I, _I, _I]),
     "attn_bwd_prep": (_I, [_I, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _P]),
@@ -129,6 +136,28 @@ def attn_bwd_workspace_size_min(dtype: int, batch: int, heads: int, seq: int, he
     return int(lib().attn_bwd_workspace_size_min(dtype, batch, heads, seq, head_dim, int(causal)))
 
 
+def attn_bwd_cross_workspace_size(dtype: int, batch: int, heads: int, seq_q: int, seq_k: int,
+                                  head_dim: int, causal: bool) -> int:
+    return int(lib().attn_bwd_cross_workspace_size(dtype, batch, heads, seq_q, seq_k, head_dim,
+                                                   int(causal)))
+
+
+def attn_bwd_cross_workspace_size_min(dtype: int, batch: int, heads: int, seq_q: int, seq_k: int,
+                                      head_dim: int, causal: bool) -> int:
+    return int(lib().attn_bwd_cross_workspace_size_min(dtype, batch, heads, seq_q, seq_k,
+                                                       head_dim, int(causal)))
+
+
+def _kv_len_ptr(kv_len, batch: int) -> int:
+    import torch
+    if kv_len is None:
+        return 0
+    if not kv_len.is_cuda or kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (batch,) \
+            or not kv_len.is_contiguous():
+        raise ValueError(f"kv_len must be a contiguous int32 device tensor of shape ({batch},)")
+    return kv_len.data_ptr()
+
+
 def _nbytes(t) -> int:
     return t.numel() * t.element_size()
 
@@ -153,6 +182,44 @@ def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None,
                           o.data_ptr(), 0 if lse is None else lse.data_ptr(), B, H, S, D,
                           int(causal), float(scale), _stream(stream))
     _raise("attn_fwd", code)
+
+
+def attn_fwd_cross(q, k, v, o, lse, kv_len, causal: bool, scale: float, stream=None,
+                   bf16_operands: bool = False) -> None:
+    """Cross-attention forward: q, o [B,H,Sq,D]; k, v [B,H,Sk,D]; lse [B,H,Sq] or
+    None; kv_len None or an int32 device tensor [B] of valid keys per batch."""
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    _check({"q": q, "o": o}, (B, H, Sq, D), q.dtype)
+    _check({"k": k, "v": v}, (B, H, Sk, D), q.dtype)
+    if lse is not None:
+        _check_f32({"lse": lse}, (B, H, Sq))
+    code = _dtype_code(q)
+    if bf16_operands:
+        if code != ATTN_F32:
+            raise TypeError("bf16_operands applies to float32 tensors")
+        code = ATTN_F32_BF16FWD
+    code = lib().attn_fwd_cross(code, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                0 if lse is None else lse.data_ptr(), B, H, Sq, Sk, D,
+                                _kv_len_ptr(kv_len, B), int(causal), float(scale),
+                                _stream(stream))
+    _raise("attn_fwd_cross", code)
+
+
+def attn_bwd_cross(q, k, v, o, dout, lse, dq, dk, dv, workspace, kv_len, causal: bool,
+                   scale: float, stream=None) -> None:
+    """Cross-attention backward (shapes as attn_fwd_cross; dq like q, dk and dv like k)."""
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    _check({"q": q, "o": o, "dout": dout, "dq": dq}, (B, H, Sq, D), q.dtype)
+    _check({"k": k, "v": v, "dk": dk, "dv": dv}, (B, H, Sk, D), q.dtype)
+    _check_f32({"lse": lse}, (B, H, Sq))
+    code = lib().attn_bwd_cross(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                                dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                                _nbytes(workspace), B, H, Sq, Sk, D, _kv_len_ptr(kv_len, B),
+                                int(causal), float(scale), _stream(stream))
+    _raise("attn_bwd_cross", code)
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,

@@ -14,10 +14,10 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-attn_status_t check_shape(attn_dtype_t dtype, int batch, int heads, int seq, int head_dim,
+attn_status_t check_shape(attn_dtype_t dtype, int batch, int heads, int sq, int sk, int head_dim,
                           int causal, float scale, bool check_scale) {
   if (dtype != ATTN_F32 && dtype != ATTN_BF16 && dtype != ATTN_F32_BF16FWD) return ATTN_ERR_UNSUPPORTED;
-  if (batch <= 0 || heads <= 0 || seq <= 0) return ATTN_ERR_INVALID_ARG;
+  if (batch <= 0 || heads <= 0 || sq <= 0 || sk <= 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (check_scale && !(isfinite(scale) && scale > 0.f)) return ATTN_ERR_INVALID_ARG;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
@@ -25,8 +25,10 @@ attn_status_t check_shape(attn_dtype_t dtype, int batch, int heads, int seq, int
   // grid's x dimension, S*D within int, and the whole tensor within int64.
   const int64_t bh = (int64_t)batch * heads;
   if (bh > 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
-  if ((int64_t)seq * head_dim > 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
-  if (bh * seq > 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
+  for (const int s : {sq, sk}) {
+    if ((int64_t)s * head_dim > 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
+    if (bh * s > 0x7fffffffLL) return ATTN_ERR_INVALID_ARG;
+  }
   return ATTN_OK;
 }
 
@@ -40,18 +42,18 @@ attn_status_t check_ptrs(std::initializer_list<const void*> ptrs) {
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Minimum workspace: D, then LSE * log2(e), one float each per query row.
-size_t ws_min_bytes(int batch, int heads, int seq) {
-  return round256(2 * (size_t)batch * heads * seq * sizeof(float));
+size_t ws_min_bytes(int batch, int heads, int sq) {
+  return round256(2 * (size_t)batch * heads * sq * sizeof(float));
 }
 
-// Row stride of the stored dS: seq rounded up to the largest key tile.
-int ds_stride(int seq) { return (seq + 127) / 128 * 128; }
+// Stride of the stored dS: a length rounded up to the largest tile.
+int ds_stride(int s) { return (s + 127) / 128 * 128; }
 
-// Full workspace: the minimum plus dS^T [B*H][ds_stride(seq)]^2 in dtype.
-size_t ws_full_bytes(attn_dtype_t dtype, int batch, int heads, int seq) {
+// Full workspace: the minimum plus dS^T [B*H][ds_stride(sk)][ds_stride(sq)] in dtype.
+size_t ws_full_bytes(attn_dtype_t dtype, int batch, int heads, int sq, int sk) {
   const size_t esize = dtype == ATTN_BF16 ? 2 : 4;
-  const size_t sp = (size_t)ds_stride(seq);
-  return ws_min_bytes(batch, heads, seq) + round256((size_t)batch * heads * sp * sp * esize);
+  return ws_min_bytes(batch, heads, sq) +
+         round256((size_t)batch * heads * ds_stride(sk) * ds_stride(sq) * esize);
 }
 
 attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
@@ -60,20 +62,62 @@ attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E
 // the full size.
 attn::BwdArgs make_bwd(attn_dtype_t dtype, const void* q, const void* k, const void* v,
                        const void* o, const void* dout, const float* lse, void* dq, void* dk,
-                       void* dv, void* ws, size_t ws_bytes, int batch, int heads, int seq,
-                       int head_dim, int causal, float scale, void* stream) {
+                       void* dv, void* ws, size_t ws_bytes, int batch, int heads, int sq, int sk,
+                       int head_dim, const int* kvlen, int causal, float scale, void* stream) {
   attn::BwdArgs a;
   a.bf16 = dtype == ATTN_BF16;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.delta = static_cast<float*>(ws);
-  const bool full = ws_bytes >= ws_full_bytes(dtype, batch, heads, seq);
-  a.ds = full ? static_cast<char*>(ws) + ws_min_bytes(batch, heads, seq) : nullptr;
-  a.SP = ds_stride(seq);
-  a.BH = batch * heads; a.S = seq; a.D = head_dim;
+  const bool full = ws_bytes >= ws_full_bytes(dtype, batch, heads, sq, sk);
+  a.ds = full ? static_cast<char*>(ws) + ws_min_bytes(batch, heads, sq) : nullptr;
+  a.SPq = ds_stride(sq); a.SPk = ds_stride(sk);
+  a.BH = batch * heads; a.H = heads; a.Sq = sq; a.Sk = sk; a.D = head_dim;
+  a.kvlen = kvlen;
+  a.cross = sq != sk || kvlen != nullptr;
   a.causal = causal != 0; a.scale = scale;
   a.stream = static_cast<hipStream_t>(stream);
   return a;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+attn_status_t fwd_impl(attn_dtype_t dtype, const void* q, const void* k, const void* v, void* o,
+                       float* lse, int batch, int heads, int sq, int sk, int head_dim,
+                       const int* kvlen, int causal, float scale, void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, sq, sk, head_dim, causal, scale, true);
+  if (st != ATTN_OK) return st;
+  if ((st = check_ptrs({q, k, v, o})) != ATTN_OK) return st;
+  if (lse != nullptr && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;  // NULL: no LSE
+  if (kvlen != nullptr && !aligned4(kvlen)) return ATTN_ERR_INVALID_ARG;
+  attn::FwdArgs a;
+  a.bf16 = dtype == ATTN_BF16;
+  a.bf16_operands = dtype == ATTN_F32_BF16FWD;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.BH = batch * heads; a.H = heads; a.Sq = sq; a.Sk = sk; a.D = head_dim;
+  a.kvlen = kvlen;
+  a.cross = sq != sk || kvlen != nullptr;
+  a.causal = causal != 0; a.scale = scale;
+  a.stream = static_cast<hipStream_t>(stream);
+  return from_hip(attn::launch_fwd(a));
+}
+
+attn_status_t bwd_impl(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                       const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                       void* dv, void* workspace, size_t workspace_bytes, int batch, int heads,
+                       int sq, int sk, int head_dim, const int* kvlen, int causal, float scale,
+                       void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, sq, sk, head_dim, causal, scale, true);
+  if (st != ATTN_OK) return st;
+  if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace})) != ATTN_OK) return st;
+  if (kvlen != nullptr && !aligned4(kvlen)) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_min_bytes(batch, heads, sq)) return ATTN_ERR_WORKSPACE;
+  const attn::BwdArgs a = make_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace,
+                                   workspace_bytes, batch, heads, sq, sk, head_dim, kvlen, causal,
+                                   scale, stream);
+  if ((st = from_hip(attn::launch_bwd_prep(a))) != ATTN_OK) return st;
+  if ((st = from_hip(attn::launch_bwd_dkdv(a))) != ATTN_OK) return st;
+  return from_hip(attn::launch_bwd_dq(a));
 }
 
 }  // namespace
@@ -83,42 +127,54 @@ extern "C" {
 attn_status_t attn_fwd(attn_dtype_t dtype, const void* q, const void* k, const void* v, void* o,
                        float* lse, int batch, int heads, int seq, int head_dim, int causal,
                        float scale, void* stream) {
-  attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, causal, scale, true);
-  if (st != ATTN_OK) return st;
-  if ((st = check_ptrs({q, k, v, o})) != ATTN_OK) return st;
-  if (lse != nullptr && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;  // NULL: no LSE
-  attn::FwdArgs a;
-  a.bf16 = dtype == ATTN_BF16;
-  a.bf16_operands = dtype == ATTN_F32_BF16FWD;
-  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.BH = batch * heads; a.S = seq; a.D = head_dim;
-  a.causal = causal != 0; a.scale = scale;
-  a.stream = static_cast<hipStream_t>(stream);
-  return from_hip(attn::launch_fwd(a));
+  return fwd_impl(dtype, q, k, v, o, lse, batch, heads, seq, seq, head_dim, nullptr, causal, scale,
+                  stream);
+}
+
+attn_status_t attn_fwd_cross(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                             void* o, float* lse, int batch, int heads, int seq_q, int seq_k,
+                             int head_dim, const int* kv_len, int causal, float scale,
+                             void* stream) {
+  return fwd_impl(dtype, q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, kv_len, causal,
+                  scale, stream);
 }
 
 size_t attn_bwd_workspace_size(attn_dtype_t dtype, int batch, int heads, int seq, int head_dim,
                                int causal) {
-  if (check_shape(dtype, batch, heads, seq, head_dim, causal, 1.f, false) != ATTN_OK) return 0;
-  return ws_full_bytes(dtype, batch, heads, seq);
+  if (check_shape(dtype, batch, heads, seq, seq, head_dim, causal, 1.f, false) != ATTN_OK) return 0;
+  return ws_full_bytes(dtype, batch, heads, seq, seq);
 }
 
 size_t attn_bwd_workspace_size_min(attn_dtype_t dtype, int batch, int heads, int seq,
                                    int head_dim, int causal) {
-  if (check_shape(dtype, batch, heads, seq, head_dim, causal, 1.f, false) != ATTN_OK) return 0;
+  if (check_shape(dtype, batch, heads, seq, seq, head_dim, causal, 1.f, false) != ATTN_OK) return 0;
   return ws_min_bytes(batch, heads, seq);
+}
+
+size_t attn_bwd_cross_workspace_size(attn_dtype_t dtype, int batch, int heads, int seq_q,
+                                     int seq_k, int head_dim, int causal) {
+  if (check_shape(dtype, batch, heads, seq_q, seq_k, head_dim, causal, 1.f, false) != ATTN_OK)
+    return 0;
+  return ws_full_bytes(dtype, batch, heads, seq_q, seq_k);
+}
+
+size_t attn_bwd_cross_workspace_size_min(attn_dtype_t dtype, int batch, int heads, int seq_q,
+                                         int seq_k, int head_dim, int causal) {
+  if (check_shape(dtype, batch, heads, seq_q, seq_k, head_dim, causal, 1.f, false) != ATTN_OK)
+    return 0;
+  return ws_min_bytes(batch, heads, seq_q);
 }
 
 attn_status_t attn_bwd_prep(attn_dtype_t dtype, const void* o, const void* dout,
                             const float* lse, void* workspace, size_t workspace_bytes, int batch,
                             int heads, int seq, int head_dim, void* stream) {
-  attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, 0, 1.f, false);
+  attn_status_t st = check_shape(dtype, batch, heads, seq, seq, head_dim, 0, 1.f, false);
   if (st != ATTN_OK) return st;
   if ((st = check_ptrs({o, dout, lse, workspace})) != ATTN_OK) return st;
   if (workspace_bytes < ws_min_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
   const attn::BwdArgs a = make_bwd(dtype, nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr,
-                                   nullptr, workspace, workspace_bytes, batch, heads, seq, head_dim,
-                                   0, 1.f, stream);
+                                   nullptr, workspace, workspace_bytes, batch, heads, seq, seq,
+                                   head_dim, nullptr, 0, 1.f, stream);
   return from_hip(attn::launch_bwd_prep(a));
 }
 
@@ -126,13 +182,13 @@ attn_status_t attn_bwd_dkdv(attn_dtype_t dtype, const void* q, const void* k, co
                             const void* dout, void* dk, void* dv, void* workspace,
                             size_t workspace_bytes, int batch, int heads, int seq, int head_dim,
                             int causal, float scale, void* stream) {
-  attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, causal, scale, true);
+  attn_status_t st = check_shape(dtype, batch, heads, seq, seq, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
   if ((st = check_ptrs({q, k, v, dout, dk, dv, workspace})) != ATTN_OK) return st;
   if (workspace_bytes < ws_min_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
   const attn::BwdArgs a = make_bwd(dtype, q, k, v, nullptr, dout, nullptr, nullptr, dk, dv,
-                                   workspace, workspace_bytes, batch, heads, seq, head_dim, causal,
-                                   scale, stream);
+                                   workspace, workspace_bytes, batch, heads, seq, seq, head_dim,
+                                   nullptr, causal, scale, stream);
   return from_hip(attn::launch_bwd_dkdv(a));
 }
 
@@ -140,13 +196,13 @@ attn_status_t attn_bwd_dq(attn_dtype_t dtype, const void* q, const void* k, cons
                           const void* dout, void* dq, const void* workspace,
                           size_t workspace_bytes, int batch, int heads, int seq, int head_dim,
                           int causal, float scale, void* stream) {
-  attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, causal, scale, true);
+  attn_status_t st = check_shape(dtype, batch, heads, seq, seq, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
   if ((st = check_ptrs({q, k, v, dout, dq, workspace})) != ATTN_OK) return st;
   if (workspace_bytes < ws_min_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
   const attn::BwdArgs a = make_bwd(dtype, q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr,
                                    const_cast<void*>(workspace), workspace_bytes, batch, heads,
-                                   seq, head_dim, causal, scale, stream);
+                                   seq, seq, head_dim, nullptr, causal, scale, stream);
   return from_hip(attn::launch_bwd_dq(a));
 }
 
@@ -154,16 +210,17 @@ attn_status_t attn_bwd(attn_dtype_t dtype, const void* q, const void* k, const v
                        const void* o, const void* dout, const float* lse, void* dq, void* dk,
                        void* dv, void* workspace, size_t workspace_bytes, int batch, int heads,
                        int seq, int head_dim, int causal, float scale, void* stream) {
-  attn_status_t st = check_shape(dtype, batch, heads, seq, head_dim, causal, scale, true);
-  if (st != ATTN_OK) return st;
-  if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace})) != ATTN_OK) return st;
-  if (workspace_bytes < ws_min_bytes(batch, heads, seq)) return ATTN_ERR_WORKSPACE;
-  const attn::BwdArgs a = make_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace,
-                                   workspace_bytes, batch, heads, seq, head_dim, causal, scale,
-                                   stream);
-  if ((st = from_hip(attn::launch_bwd_prep(a))) != ATTN_OK) return st;
-  if ((st = from_hip(attn::launch_bwd_dkdv(a))) != ATTN_OK) return st;
-  return from_hip(attn::launch_bwd_dq(a));
+  return bwd_impl(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, batch,
+                  heads, seq, seq, head_dim, nullptr, causal, scale, stream);
+}
+
+attn_status_t attn_bwd_cross(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse, void* dq,
+                             void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                             int batch, int heads, int seq_q, int seq_k, int head_dim,
+                             const int* kv_len, int causal, float scale, void* stream) {
+  return bwd_impl(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, batch,
+                  heads, seq_q, seq_k, head_dim, kv_len, causal, scale, stream);
 }
 
 const char* attn_status_string(attn_status_t s) {
@@ -177,6 +234,6 @@ const char* attn_status_string(attn_status_t s) {
   return "unknown status";
 }
 
-const char* attn_version(void) { return "0.2.0"; }
+const char* attn_version(void) { return "0.3.0"; }
 
 }  // extern "C"

@@ -34,13 +34,17 @@
 
 namespace attn {
 
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS, bool CROSS>
 __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_F32 : 1) void bwd_dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
-    typename E::T* __restrict__ dSout, int SP, int S, int L, float c, float scale, int BH,
-    int nitems, const Sched sched) {
+    typename E::T* __restrict__ dSout, int SPq, int SPk, int Sq, int Sk_, int Lws, float c,
+    float scale, int BH, int H, const int* __restrict__ kvlen, int nitems, const Sched sched) {
+  // Queries Sq, keys Sk (one length in self-attention, CROSS = false); per
+  // batch*head the first L keys exist and key j is visible from query i iff
+  // j < L and, when causal, j <= i + off (head_keys).  Lws: offset of the
+  // LSE*log2(e) vector in the workspace (B*H*Sq).
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-key blocks per item
@@ -71,33 +75,55 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int kbk = w / NSPLIT, sp = w % NSPLIT;
   const int g = blockIdx.x, G = gridDim.x;
-  const int nqt = (S + BQ - 1) / BQ;
+  const int Sk = CROSS ? Sk_ : Sq;
+  const int nqt = (Sq + BQ - 1) / BQ;
   const unsigned lane_off = LD::lane_offset(w, lane);
-  auto first_qt = [&](int kt) { return CAUSAL ? (kt * BKV) / BQ : 0; };
+  // First query tile with a query that sees a key of key tile kt (nqt: none).
+  auto first_qt = [&](int kt, int L, int off) {
+    if constexpr (!CROSS) {
+      return CAUSAL ? (kt * BKV) / BQ : 0;
+    } else {
+      if (kt * BKV >= L) return nqt;
+      return CAUSAL ? min(nqt, max(0, kt * BKV - off) / BQ) : 0;
+    }
+  };
 
   // Loader cursor: the next stream tile to issue (lqt < 0: the header of
   // item lit, whose K and V rows it stages; else query tile lqt).  Every
   // stream tile is NL loads per wave (the header also loads statistics it
   // does not use, to keep that count).
   int lr = 0, lit = sched_item(sched, 0, g, G, BH), lqt = -1, lkt = lit / BH;
-  size_t lho = (size_t)(lit % BH) * S;  // first row of the item's head
+  size_t lhq = (size_t)(lit % BH) * Sq, lhk = (size_t)(lit % BH) * Sk;  // first rows of the head
+  int lL, loff;
+  head_keys<CROSS>(kvlen, lit % BH, H, Sq, Sk, lL, loff);
   int nissued = 0;
+  auto next_item = [&]() {
+    lit = sched_item(sched, ++lr, g, G, BH);
+    lqt = -1;
+    lkt = lit / BH;
+    lhq = (size_t)(lit % BH) * Sq;
+    lhk = (size_t)(lit % BH) * Sk;
+    head_keys<CROSS>(kvlen, lit % BH, H, Sq, Sk, lL, loff);
+  };
   auto issue_next = [&]() {
     if (lit >= nitems) return;
     char* st = smem + (nissued % NST) * STAGE;
     const bool head = lqt < 0;
-    const int row0 = head ? lkt * BKV : lqt * BQ;
-    LD::issue(st, (head ? K : Q) + lho * D, (head ? V : dO) + lho * D, row0, S, w, lane, lane_off);
-    issue_stats<BQ, NW>(stats0 + (nissued % NST) * (2 * BQ), Dws + L + lho, Dws + lho,
-                        head ? 0 : row0, S, w, lane);
+    if (head) {
+      // K and V rows; past the valid keys the loads read the last valid row
+      // (finite, and masked), so padded rows are never read.
+      LD::issue(st, K + lhk * D, V + lhk * D, lkt * BKV, CROSS ? max(lL, 1) : Sk, w, lane, lane_off);
+    } else {
+      LD::issue(st, Q + lhq * D, dO + lhq * D, lqt * BQ, Sq, w, lane, lane_off);
+    }
+    issue_stats<BQ, NW>(stats0 + (nissued % NST) * (2 * BQ), Dws + Lws + lhq, Dws + lhq,
+                        head ? 0 : lqt * BQ, Sq, w, lane);
     ++nissued;
     if (head) {
-      lqt = first_qt(lkt);
+      lqt = first_qt(lkt, lL, loff);
+      if (lqt >= nqt) next_item();  // (CROSS: an item that no query sees)
     } else if (++lqt == nqt) {
-      lit = sched_item(sched, ++lr, g, G, BH);
-      lqt = -1;
-      lkt = lit / BH;
-      lho = (size_t)(lit % BH) * S;
+      next_item();
     }
   };
 
@@ -151,19 +177,19 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     int nstores = 0;
     if (sp == 0 && active) {
       // element r of acc[db]: row k0 + out_row(r, h), column db*32 + n
-      T* dk = dK + (size_t)bh * S * D;
-      T* dv = dV + (size_t)bh * S * D;
+      T* dk = dK + (size_t)bh * Sk * D;
+      T* dv = dV + (size_t)bh * Sk * D;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = k0 + out_row(r, h);
-        if (row < S) {
+        if (row < Sk) {
 #pragma unroll
           for (int db = 0; db < NDB; ++db) {
             dk[(size_t)row * D + db * 32 + n] = (T)(dkacc[db][r] * scale);
             dv[(size_t)row * D + db * 32 + n] = (T)dvacc[db][r];
           }
         }
-        if (k0 + out_row(r, 1) < S) nstores += 2 * NDB;
+        if (k0 + out_row(r, 1) < Sk) nstores += 2 * NDB;
       }
     }
     return nstores;
@@ -182,7 +208,9 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     const int kt = cit / BH, bh = cit % BH;
     const int k0 = kt * BKV + kbk * 32;
     const int kj = k0 + n;
-    const bool wave_active = k0 < S;
+    const bool wave_active = k0 < Sk;
+    int cL, coff;  // the item's valid keys and causal offset
+    head_keys<CROSS>(kvlen, bh, H, Sq, Sk, cL, coff);
 
     // Header: this wave's K, V rows into registers.
     wait_vmem_dyn(NL * (nissued - pos - 1) + NSTORE * stored + estores);
@@ -192,8 +220,8 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     issue_next();
     __builtin_amdgcn_sched_barrier(0);  // the counts above assume this issue order
     const char* hst = smem + (pos % NST) * STAGE;
-    load_row_frag_lds<E, D>(kf, hst, kbk * 32 + n, h, kj < S);
-    load_row_frag_lds<E, D>(vf, hst + TILEB, kbk * 32 + n, h, kj < S);
+    load_row_frag_lds<E, D>(kf, hst, kbk * 32 + n, h, kj < Sk);
+    load_row_frag_lds<E, D>(vf, hst + TILEB, kbk * 32 + n, h, kj < Sk);
 #pragma unroll
     for (int i = 0; i < NDB; ++i) {
       dkacc[i] = zero16();
@@ -201,7 +229,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     }
     ++pos;
 
-    for (int qt = first_qt(kt); qt < nqt; ++qt, ++pos) {
+    for (int qt = first_qt(kt, cL, coff); qt < nqt; ++qt, ++pos) {
       if (estores == 0) wait_tiles<NL, NSTORE>(nissued - pos - 1, stored);
       else wait_vmem_dyn(NL * (nissued - pos - 1) + NSTORE * stored + estores);
       stored = 0;
@@ -220,14 +248,17 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
       for (int j = 0; j < KPW; ++j) {
         const int qbl = sp + NSPLIT * j;  // query block within the tile
         const int qq0 = qt * BQ + qbl * 32;
-        if (!(qq0 < S && (!CAUSAL || qq0 + 31 >= k0))) continue;  // wave-uniform
+        if (!(qq0 < Sq && (!CAUSAL || qq0 + 31 >= k0 - coff) && (!CROSS || k0 < cL)))
+          continue;  // wave-uniform
         const int arow = qbl * 32 + pi32(n);
         f32x16 s = dot_tile<E, D>(Qt, arow, h, kf, zero16());
         f32x16 dp = dot_tile<E, D>(dOt, arow, h, vf, zero16());
-        if ((CAUSAL && qq0 < k0 + 31) || qq0 + 32 > S) {
-          // query(r) = qq0 + 8h + (16*(r/8) + r%8) sees key kj iff kj <= query < S
-          const int lo = CAUSAL ? kj - qq0 - 8 * h : -64;
-          const int hi = S - 1 - qq0 - 8 * h;
+        if ((CAUSAL && qq0 < k0 + 31 - coff) || qq0 + 32 > Sq || (CROSS && k0 + 32 > cL)) {
+          // query(r) = qq0 + 8h + (16*(r/8) + r%8) sees key kj iff
+          // kj - off <= query < Sq (and, with CROSS, kj < L)
+          int lo = CAUSAL ? kj - coff - qq0 - 8 * h : -64;
+          if (CROSS && kj >= cL) lo = 64;
+          const int hi = Sq - 1 - qq0 - 8 * h;
           // all-ones where o < lo or o > hi, built without per-element
           // compare masks (which would hold 16 scalar register pairs); the
           // whole vector is bit-cast (a bit_cast of one element of an
@@ -264,10 +295,10 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
           ++stored;
           // dS^T for the dQ GEMM, row kj: this lane's 16 values are queries
           // qq0 + 8h + {0..7} and qq0 + 16 + 8h + {0..7} (exact zeros where
-          // masked, for queries past S and for keys past S).
-          T* row = dSout + ((size_t)bh * SP + kj) * SP + qq0 + 8 * h;
-          // keys past S (only in the last key tile) store zeros
-          if (k0 + 32 > S && kj >= S) dp = zero16();
+          // masked, for queries past Sq and for keys past Sk).
+          T* row = dSout + ((size_t)bh * SPk + kj) * SPq + qq0 + 8 * h;
+          // keys past Sk (only in the last key tile) store zeros
+          if (k0 + 32 > Sk && kj >= Sk) dp = zero16();
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             if constexpr (is_bf16<E>()) {
@@ -303,34 +334,43 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   }
 }
 
-template <class E, int D, bool CAUSAL, bool WDS>
+template <class E, int D, bool CAUSAL, bool WDS, bool CROSS>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int NW = is_bf16<E>() ? ATTN_DKDV_NW_BF16 : ATTN_DKDV_NW_F32;
   constexpr int NSPLIT = is_bf16<E>() ? ATTN_DKDV_NSPLIT_BF16 : ATTN_DKDV_NSPLIT_F32;
   constexpr int KPW = is_bf16<E>() ? ATTN_DKDV_KPW_BF16 : ATTN_DKDV_KPW_F32;
   constexpr int NST = is_bf16<E>() ? ATTN_DKDV_NST_BF16 : ATTN_DKDV_NST_F32;
   using T = typename E::T;
-  constexpr auto kern = bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS>;
+  constexpr auto kern = bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS>;
   constexpr int BKV = 32 * (NW / NSPLIT);
-  const int nkt = (a.S + BKV - 1) / BKV;
+  const int nkt = (a.Sk + BKV - 1) / BKV;
   const int nitems = a.BH * nkt;
   const int grid = std::min(nitems, resident_workgroups<kern>(NW * 64));
-  // work of a key tile: its header tile and the query tiles it visits
+  // work of a key tile: its header tile and the query tiles it visits (with
+  // every key valid: the per-batch counts live on the device)
   constexpr int BQ = 32 * NSPLIT * KPW;
-  const int nqt = (a.S + BQ - 1) / BQ;
+  const int nqt = (a.Sq + BQ - 1) / BQ;
+  const int off = a.Sk - a.Sq;
   std::vector<int> works(nkt);
-  for (int kt = 0; kt < nkt; ++kt) works[kt] = 1 + nqt - (CAUSAL ? (kt * BKV) / BQ : 0);
+  for (int kt = 0; kt < nkt; ++kt)
+    works[kt] = 1 + nqt - (CAUSAL ? std::min(nqt, std::max(0, kt * BKV - off) / BQ) : 0);
   const Sched sched = make_sched(grid, a.BH, works);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SP,
-                     a.S, a.BH * a.S, a.scale * kLog2e, a.scale, a.BH, nitems, sched);
+                     (const T*)a.v, (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SPq,
+                     a.SPk, a.Sq, a.Sk, a.BH * a.Sq, a.scale * kLog2e, a.scale, a.BH, a.H, a.kvlen,
+                     nitems, sched);
   return hipGetLastError();
+}
+
+template <class E, int D, bool CAUSAL, bool WDS>
+static hipError_t launch_x(const BwdArgs& a) {
+  return a.cross ? launch<E, D, CAUSAL, WDS, true>(a) : launch<E, D, CAUSAL, WDS, false>(a);
 }
 
 template <class E, int D>
 static hipError_t launch_c(const BwdArgs& a) {
-  if (a.ds != nullptr) return a.causal ? launch<E, D, true, true>(a) : launch<E, D, false, true>(a);
-  return a.causal ? launch<E, D, true, false>(a) : launch<E, D, false, false>(a);
+  if (a.ds != nullptr) return a.causal ? launch_x<E, D, true, true>(a) : launch_x<E, D, false, true>(a);
+  return a.causal ? launch_x<E, D, true, false>(a) : launch_x<E, D, false, false>(a);
 }
 
 template <class E>

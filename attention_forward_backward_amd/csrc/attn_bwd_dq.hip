@@ -29,12 +29,15 @@
 
 namespace attn {
 
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
-    typename E::T* __restrict__ dQ, const float* __restrict__ Dws, int S, int L, float c,
-    float scale) {
+    typename E::T* __restrict__ dQ, const float* __restrict__ Dws, int Sq, int Sk_, int Lws,
+    float c, float scale, int H, const int* __restrict__ kvlen) {
+  // Queries Sq, keys Sk (one length in self-attention, CROSS = false); key j
+  // is visible from query i iff j < L and, when causal, j <= i + off
+  // (head_keys).  Lws: offset of LSE*log2(e) in the workspace (B*H*Sq).
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-query blocks per workgroup
@@ -54,34 +57,38 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   const int qb = w / NSPLIT, sp = w % NSPLIT;
   const int bh = blockIdx.x;
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
-  const size_t base = (size_t)bh * S * D;
-  const T* k = K + base;
-  const T* v = V + base;
+  const int Sk = CROSS ? Sk_ : Sq;
+  const size_t base = (size_t)bh * Sq * D;
+  const T* k = K + (size_t)bh * Sk * D;
+  const T* v = V + (size_t)bh * Sk * D;
+  int L, off;
+  head_keys<CROSS>(kvlen, bh, H, Sq, Sk, L, off);
+  const int krows = CROSS ? max(L, 1) : Sk;  // key rows the loads may read
 
   const int q0 = qt * BR + qb * 32;
   const int qi = q0 + n;
-  const bool wave_active = q0 < S;
-  const bool qvalid = qi < S;
-  const size_t qrow = base + (size_t)min(qi, S - 1) * D + h * (D / 2);
+  const bool wave_active = q0 < Sq;
+  const bool qvalid = qi < Sq;
+  const size_t qrow = base + (size_t)min(qi, Sq - 1) * D + h * (D / 2);
 
   RowFrag<E, D> qf, dof;
   load_row_frag<E, D>(qf, Q + qrow, qvalid);
   load_row_frag<E, D>(dof, dO + qrow, qvalid);
   // D_i and LSE_i*log2(e), written by the prep kernel
-  const float di = qvalid ? Dws[(size_t)bh * S + qi] : 0.f;
-  const float lse2 = qvalid ? Dws[(size_t)L + (size_t)bh * S + qi] : 0.f;
+  const float di = qvalid ? Dws[(size_t)bh * Sq + qi] : 0.f;
+  const float lse2 = qvalid ? Dws[(size_t)Lws + (size_t)bh * Sq + qi] : 0.f;
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = zero16();
 
-  const int kend = CAUSAL ? min(S, qt * BR + BR) : S;
-  const int nkt = (kend + BK - 1) / BK;
+  const int kend = CAUSAL ? min(L, qt * BR + BR + off) : L;
+  const int nkt = max((kend + BK - 1) / BK, 0);
 
   const unsigned lo = LD::lane_offset(w, lane);
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < nkt) LD::issue(smem + s * LD::BYTES, k, v, s * BK, S, w, lane, lo);
+    if (s < nkt) LD::issue(smem + s * LD::BYTES, k, v, s * BK, krows, w, lane, lo);
 
   // One staged tile of keys.  When the stages' LDS addresses fit 16-bit
   // offsets, the loop is unrolled by NST with the stage index constant.
@@ -90,7 +97,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     wait_tiles<LD::NLOADS>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1
     if (kt + NST - 1 < nkt)
-      LD::issue(smem + ((kt + NST - 1) % NST) * LD::BYTES, k, v, (kt + NST - 1) * BK, S, w, lane, lo);
+      LD::issue(smem + ((kt + NST - 1) % NST) * LD::BYTES, k, v, (kt + NST - 1) * BK, krows, w, lane, lo);
     if (!wave_active) return;
     const char* Kt = smem + si * LD::BYTES;
     const char* Vt = Kt + TILEB;
@@ -99,13 +106,13 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     for (int j = 0; j < KPW; ++j) {
       const int kb = sp + NSPLIT * j;
       const int kk0 = kt * BK + kb * 32;
-      if (!(kk0 < S && (!CAUSAL || kk0 <= q0 + 31))) continue;  // wave-uniform
+      if (!(kk0 < L && (!CAUSAL || kk0 <= q0 + 31 + off))) continue;  // wave-uniform
       const int arow = kb * 32 + pi32(n);
       f32x16 st = dot_tile<E, D>(Kt, arow, h, qf, zero16());
       f32x16 dpt = dot_tile<E, D>(Vt, arow, h, dof, zero16());
-      if (kk0 + 32 > S || (CAUSAL && kk0 + 31 > q0)) {
-        // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < S and key <= qi
-        const int lim = min(S - 1, CAUSAL ? qi : S - 1) - kk0 - 8 * h;
+      if (kk0 + 32 > L || (CAUSAL && kk0 + 31 > q0 + off)) {
+        // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < L and key <= qi + off
+        const int lim = min(L - 1, CAUSAL ? qi + off : L - 1) - kk0 - 8 * h;
         // -inf where 16*(r/8) + r%8 > lim, built arithmetically (no
         // per-element compare masks in scalar registers); the whole vector
         // is bit-cast (a bit_cast of one ext_vector element is not reliable)
@@ -119,7 +126,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(st[r], c, -lse2));  // 0 where masked
+        // 0 where masked (a row with no visible key has lse2 = 0 from the
+        // prep pass and only masked keys)
+        const float p = fast_exp2(fmaf(st[r], c, -lse2));
         st[r] = p * (dpt[r] - di);                            // dS^T
       }
       RegOperand<E> dS;
@@ -165,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = q0 + out_row(r, h);
-    if (row < S) {
+    if (row < Sq) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dq[(size_t)row * D + db * 32 + n] = (T)(acc[db][r] * scale);
     }
@@ -181,10 +190,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 // Blocks with no visible key (above the causal diagonal, or past S) are
 // skipped; the dK+dV kernel wrote exact zeros for every masked entry and
 // every key past S inside the blocks it processed.
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
     const typename E::T* __restrict__ K, const typename E::T* __restrict__ dST,
-    typename E::T* __restrict__ dQ, int S, int SP, float scale) {
+    typename E::T* __restrict__ dQ, int Sq, int Sk_, int SPq, int SPk, float scale, int H,
+    const int* __restrict__ kvlen) {
   using T = typename E::T;
   constexpr int RB = NW / NSPLIT;
   constexpr int BR = 32 * RB;
@@ -205,23 +215,27 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   const int qb = w / NSPLIT, sp = w % NSPLIT;
   const int bh = blockIdx.x;
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
-  const T* k = K + (size_t)bh * S * D;
-  const T* dst_ = dST + (size_t)bh * SP * SP;
+  const int Sk = CROSS ? Sk_ : Sq;
+  const T* k = K + (size_t)bh * Sk * D;
+  const T* dst_ = dST + (size_t)bh * SPk * SPq;
+  int L, off;  // key j is visible from query i iff j < L and (causal) j <= i + off
+  head_keys<CROSS>(kvlen, bh, H, Sq, Sk, L, off);
+  const int krows = CROSS ? max(L, 1) : Sk;  // key rows the loads may read
   const int qw0 = qt * BR;         // first query of the workgroup
   const int q0 = qw0 + qb * 32;    // first query of this wave's block
-  const bool wave_active = q0 < S;
+  const bool wave_active = q0 < Sq;
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) acc[i] = zero16();
 
-  const int kend = CAUSAL ? min(S, qw0 + BR) : S;
-  const int nkt = (kend + BK - 1) / BK;
-  const unsigned los = LDS_::lane_offset(SP, w, lane), lok = LDK::lane_offset(D, w, lane);
+  const int kend = CAUSAL ? min(L, qw0 + BR + off) : L;
+  const int nkt = max((kend + BK - 1) / BK, 0);
+  const unsigned los = LDS_::lane_offset(SPq, w, lane), lok = LDK::lane_offset(D, w, lane);
   auto issue = [&](int t) __attribute__((always_inline)) {
     char* st = smem + (t % NST) * STAGE;
-    LDS_::issue(st, dst_, SP, t * BK, SP, qw0, w, lane, los);
-    LDK::issue(st + LDS_::BYTES, k, D, t * BK, S, 0, w, lane, lok);
+    LDS_::issue(st, dst_, SPq, t * BK, SPk, qw0, w, lane, los);
+    LDK::issue(st + LDS_::BYTES, k, D, t * BK, krows, 0, w, lane, lok);
   };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
@@ -239,7 +253,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
     for (int j = 0; j < KPW; ++j) {
       const int kb = sp + NSPLIT * j;
       const int kk0 = kt * BK + kb * 32;
-      if (!(kk0 < S && (!CAUSAL || kk0 <= q0 + 31))) continue;  // wave-uniform
+      if (!(kk0 < L && (!CAUSAL || kk0 <= q0 + 31 + off))) continue;  // wave-uniform
       RegOperand<E> R;  // dS[q0 + n][keys]: k-slots from the dS^T rows
       read_kslot_operand<E, BR>(R, St, kb * 32, qb * 32, lane);
 #pragma unroll
@@ -277,31 +291,32 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
     }
   }
   if (!wave_active) return;
-  T* dq = dQ + (size_t)bh * S * D;
+  T* dq = dQ + (size_t)bh * Sq * D;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = q0 + out_row(r, h);
-    if (row < S) {
+    if (row < Sq) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) dq[(size_t)row * D + db * 32 + n] = (T)(acc[db][r] * scale);
     }
   }
 }
 
-template <class E, int D, bool CAUSAL>
+template <class E, int D, bool CAUSAL, bool CROSS>
 static hipError_t launch_gemm(const BwdArgs& a) {
   constexpr int NW = 4, NSPLIT = 2, KPW = 1;
   constexpr int NST = is_bf16<E>() ? 3 : 2;
   using T = typename E::T;
   constexpr int BR = 32 * (NW / NSPLIT);
-  const int nqt = (a.S + BR - 1) / BR;
+  const int nqt = (a.Sq + BR - 1) / BR;
   dim3 grid(a.BH, nqt);
-  hipLaunchKernelGGL((bwd_dq_gemm_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>), grid, dim3(NW * 64),
-                     0, a.stream, (const T*)a.k, (const T*)a.ds, (T*)a.dq, a.S, a.SP, a.scale);
+  hipLaunchKernelGGL((bwd_dq_gemm_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS>), grid,
+                     dim3(NW * 64), 0, a.stream, (const T*)a.k, (const T*)a.ds, (T*)a.dq, a.Sq,
+                     a.Sk, a.SPq, a.SPk, a.scale, a.H, a.kvlen);
   return hipGetLastError();
 }
 
-template <class E, int D, bool CAUSAL>
+template <class E, int D, bool CAUSAL, bool CROSS>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int NW = is_bf16<E>() ? ATTN_DQ_NW_BF16 : ATTN_DQ_NW_F32;
   constexpr int NSPLIT = is_bf16<E>() ? ATTN_DQ_NSPLIT_BF16 : ATTN_DQ_NSPLIT_F32;
@@ -309,18 +324,25 @@ static hipError_t launch(const BwdArgs& a) {
   constexpr int NST = is_bf16<E>() ? ATTN_DQ_NST_BF16 : ATTN_DQ_NST_F32;
   using T = typename E::T;
   constexpr int BR = 32 * (NW / NSPLIT);
-  const int nqt = (a.S + BR - 1) / BR;
+  const int nqt = (a.Sq + BR - 1) / BR;
   dim3 grid(a.BH, nqt);
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>), grid, dim3(NW * 64), 0,
-                     a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                     (T*)a.dq, a.delta, a.S, a.BH * a.S, a.scale * kLog2e, a.scale);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS>), grid, dim3(NW * 64),
+                     0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
+                     (T*)a.dq, a.delta, a.Sq, a.Sk, a.BH * a.Sq, a.scale * kLog2e, a.scale, a.H,
+                     a.kvlen);
   return hipGetLastError();
+}
+
+template <class E, int D, bool CAUSAL>
+static hipError_t launch_x(const BwdArgs& a) {
+  if (a.ds != nullptr)
+    return a.cross ? launch_gemm<E, D, CAUSAL, true>(a) : launch_gemm<E, D, CAUSAL, false>(a);
+  return a.cross ? launch<E, D, CAUSAL, true>(a) : launch<E, D, CAUSAL, false>(a);
 }
 
 template <class E, int D>
 static hipError_t launch_c(const BwdArgs& a) {
-  if (a.ds != nullptr) return a.causal ? launch_gemm<E, D, true>(a) : launch_gemm<E, D, false>(a);
-  return a.causal ? launch<E, D, true>(a) : launch<E, D, false>(a);
+  return a.causal ? launch_x<E, D, true>(a) : launch_x<E, D, false>(a);
 }
 
 template <class E>

@@ -54,7 +54,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __re
     for (int o = 1; o < CPR; o <<= 1) acc += __shfl_xor(acc, o);
     if (row < L && chunk == 0) {
       ws[row] = acc;
-      ws[(size_t)L + row] = LSE[row] * kLog2e;
+      // A row with no visible key (LSE = -inf; only with padded keys or
+      // more queries than keys) stores 0: its keys are all masked, so
+      // exp2(-inf - 0) = 0 is its P everywhere, where -inf - (-inf) would
+      // not be.
+      const float lse = LSE[row];
+      ws[(size_t)L + row] = lse == -INFINITY ? 0.f : lse * kLog2e;
     }
   }
 }
@@ -64,7 +69,7 @@ static hipError_t launch(const BwdArgs& a) {
   constexpr int EPC = 16 / (int)sizeof(typename E::T);
   constexpr int RPW = 64 / (D / EPC);
   constexpr int UNR = 4;
-  const int L = a.BH * a.S;
+  const int L = a.BH * a.Sq;
   const int waves = (L + RPW * UNR - 1) / (RPW * UNR);
   const int blocks = (waves + 3) / 4;
   using T = typename E::T;

@@ -232,6 +232,25 @@ __device__ inline int snake_item(int r, int g, int G) {
   return r * G + gr;
 }
 
+// Keys of batch*head bh that exist for the softmax: the first L of Sk, and
+// the causal offset off, so that key j is visible from query i iff j < L
+// and, when causal, j <= i + off (off = L - Sq aligns the causal diagonal
+// with the end of the valid keys).  Self-attention (CROSS = false): L = Sk,
+// off = 0.  kvlen (valid keys per batch, device memory) may be null; its
+// values are clamped to [0, Sk].
+template <bool CROSS>
+__device__ inline void head_keys(const int* __restrict__ kvlen, int bh, int H, int Sq, int Sk,
+                                 int& L, int& off) {
+  if constexpr (!CROSS) {
+    L = Sk;
+    off = 0;
+  } else {
+    L = Sk;
+    if (kvlen != nullptr) L = min(max(kvlen[bh / H], 0), Sk);
+    off = L - Sq;
+  }
+}
+
 // Static schedule of a persistent launch, computed on the host and passed by
 // value in the kernel arguments.  Workgroups are dispatched round-robin over
 // the 8 XCDs, so workgroup g runs on XCD g % 8 as its slot g / 8.  When the

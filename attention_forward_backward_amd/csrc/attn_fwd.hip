@@ -34,12 +34,16 @@
 
 namespace attn {
 
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O,
-    float* __restrict__ LSE, int S, float c, int BH, int nitems, const Sched sched) {
-  // LSE may be null (an inference-only forward stores no LSE).
+    float* __restrict__ LSE, int Sq, int Sk_, float c, int BH, int H,
+    const int* __restrict__ kvlen, int nitems, const Sched sched) {
+  // LSE may be null (an inference-only forward stores no LSE).  Queries Sq,
+  // keys Sk (one length in self-attention, CROSS = false); per batch*head the
+  // first L keys exist and key j is visible from query i iff j < L and, when
+  // causal, j <= i + off (head_keys).
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-query blocks per item
@@ -59,13 +63,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
   const int qb = w / NSPLIT, sp = w % NSPLIT;
   const int g = blockIdx.x, G = gridDim.x;
-  const int nqt = (S + BR - 1) / BR;
+  const int Sk = CROSS ? Sk_ : Sq;
+  const int nqt = (Sq + BR - 1) / BR;
   const unsigned lo = LD::lane_offset(w, lane);
   const unsigned qlo = QL::lane_offset(D, w, lane);
   auto item_qt = [&](int it) { return nqt - 1 - it / BH; };
+  // Key tiles of item it: those holding a key visible from one of its
+  // queries; an item none of whose queries sees a key still takes one tile
+  // (processed fully masked), so that its zero rows are stored.
   auto item_nkt = [&](int it) {
-    const int kend = CAUSAL ? min(S, item_qt(it) * BR + BR) : S;
-    return (kend + BK - 1) / BK;
+    int L, off;
+    head_keys<CROSS>(kvlen, it % BH, H, Sq, Sk, L, off);
+    const int kend = CAUSAL ? min(L, item_qt(it) * BR + BR + off) : L;
+    const int n = (kend + BK - 1) / BK;
+    return CROSS ? max(n, 1) : n;
+  };
+  // Rows a key tile may read: past them the loads read the last valid row
+  // (finite, and masked), so padded rows are never read.
+  auto key_rows = [&](int it) {
+    int L, off;
+    head_keys<CROSS>(kvlen, it % BH, H, Sq, Sk, L, off);
+    return CROSS ? max(L, 1) : Sk;
   };
   if (sched_item(sched, 0, g, G, BH) >= nitems) return;  // (the launch never makes more workgroups than items)
 
@@ -82,12 +100,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
 
   // Loader cursor: tile lkt of item lit is the next one to issue.
   int lr = 0, lit = sched_item(sched, 0, g, G, BH), lkt = 0, lnkt = item_nkt(lit);
-  size_t lbase = (size_t)(lit % BH) * S * D;
+  int lrows = key_rows(lit);
+  size_t lbase = (size_t)(lit % BH) * Sk * D;
   // While tiles remain, the tile issued at stream position pos goes to ring
   // slot (pos + NST - 1) % NST, a constant of the unrolled step.
   auto issue_next = [&](const int slot) __attribute__((always_inline)) {
     if (lit >= nitems) return;
-    LD::issue(smem + slot * STAGE, K + lbase, V + lbase, lkt * BK, S, w, lane, lo);
+    LD::issue(smem + slot * STAGE, K + lbase, V + lbase, lkt * BK, lrows, w, lane, lo);
     vm += LD::NLOADS;
 #pragma unroll
     for (int i = 0; i < NST; ++i)
@@ -97,13 +116,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
       lkt = 0;
       if (lit < nitems) {
         lnkt = item_nkt(lit);
-        lbase = (size_t)(lit % BH) * S * D;
+        lrows = key_rows(lit);
+        lbase = (size_t)(lit % BH) * Sk * D;
       }
     }
   };
-  // The Q tile of item it (rows past S read row S-1) into its LDS buffer.
+  // The Q tile of item it (rows past Sq read row Sq-1) into its LDS buffer.
   auto load_q = [&](int it) __attribute__((always_inline)) {
-    QL::issue(qtile, Q + (size_t)(it % BH) * S * D, D, item_qt(it) * BR, S, 0, w, lane, qlo);
+    QL::issue(qtile, Q + (size_t)(it % BH) * Sq * D, D, item_qt(it) * BR, Sq, 0, w, lane, qlo);
     vm += QL::NLOADS;
     qmark = vm;
   };
@@ -116,6 +136,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue_next(s);
   int bh = cit % BH, q0 = item_qt(cit) * BR + qb * 32;
+  int cL, coff;  // the current item's valid keys and causal offset
+  head_keys<CROSS>(kvlen, bh, H, Sq, Sk, cL, coff);
   f32x16 oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
@@ -159,7 +181,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
         if (sp == 0 && active) {
           if (pass == 0) {
             float mp[NSPLIT - 1], lp[NSPLIT - 1];
-            float mx = m;  // finite: split 0 always sees key 0
+            // In self-attention split 0 always sees key 0, so mx is finite;
+            // with CROSS a row may have seen no key in any split (mx = -inf:
+            // every factor is then 0 and the row stays empty).
+            float mx = m;
 #pragma unroll
             for (int p = 0; p < NSPLIT - 1; ++p) {
               const float* src = cb + ((qb * (NSPLIT - 1) + p) * nv) * 64 + lane;
@@ -167,11 +192,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
               lp[p] = src[64];
               mx = fmaxf(mx, mp[p]);
             }
-            a0 = fast_exp2(m - mx);
+            const float mxs = (CROSS && mx == -INFINITY) ? 0.f : mx;
+            a0 = fast_exp2(m - mxs);
             l *= a0;
 #pragma unroll
             for (int p = 0; p < NSPLIT - 1; ++p) {
-              ap[p] = fast_exp2(mp[p] - mx);  // 0 for a split that saw no key
+              ap[p] = fast_exp2(mp[p] - mxs);  // 0 for a split that saw no key
               l += lp[p] * ap[p];
             }
             m = mx;
@@ -217,24 +243,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);  // the counts above assume this issue order
     const int qi = q0 + n;
-    const bool wave_active = q0 < S;
+    const bool wave_active = q0 < Sq;
     if (wave_active) {
       const char* Kt = smem + si * STAGE;
       const char* Vt = Kt + TILEB;
       // This wave's 32-key blocks of the tile.  A block is skipped when no
       // key in it is visible from any of the wave's queries, and masked only
-      // when some but not all of it is (the causal diagonal, the ragged end).
-      // Every processed block has at least one visible key for every query
-      // (block starts are multiples of 32), so row maxima are finite.
+      // when some but not all of it is (the causal diagonal, the ragged end,
+      // padded keys).  In self-attention every processed block has at least
+      // one visible key for every query (block starts are multiples of 32),
+      // so row maxima are finite; with CROSS a row may see none in a block,
+      // or at all (handled where noted).
 #pragma unroll
       for (int j = 0; j < KPW; ++j) {
         const int kb = sp + NSPLIT * j;
         const int kk0 = kt * BK + kb * 32;
-        if (!(kk0 < S && (!CAUSAL || kk0 <= q0 + 31))) continue;  // wave-uniform
+        if (!(kk0 < cL && (!CAUSAL || kk0 <= q0 + 31 + coff))) continue;  // wave-uniform
         f32x16 sacc = dot_tile<E, D>(Kt, kb * 32 + pi32(n), h, qf, zero16());
-        if (kk0 + 32 > S || (CAUSAL && kk0 + 31 > q0)) {
-          // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < S and key <= qi
-          const int lim = min(S - 1, CAUSAL ? qi : S - 1) - kk0 - 8 * h;
+        if (kk0 + 32 > cL || (CAUSAL && kk0 + 31 > q0 + coff)) {
+          // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < L and key <= qi + off
+          const int lim = min(cL - 1, CAUSAL ? qi + coff : cL - 1) - kk0 - 8 * h;
           // -inf where 16*(r/8) + r%8 > lim, built arithmetically (no
           // per-element compare masks in scalar registers); the whole vector
           // is bit-cast (a bit_cast of one ext_vector element is not reliable)
@@ -256,16 +284,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
         const float mc = mx * c;
         if (__any(mc > m + 8.f)) {
           const float mnew = fmaxf(m, mc);
-          const float alpha = fast_exp2(m - mnew);
+          // (CROSS: a row with no visible key yet keeps m = mnew = -inf)
+          const float alpha = (CROSS && mnew == -INFINITY) ? 1.f : fast_exp2(m - mnew);
           m = mnew;
           l *= alpha;
 #pragma unroll
           for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
         }
+        // exponent reference: m, or 0 for a row with no visible key yet
+        // (its scores are all -inf, so every p is 0)
+        const float mref = (CROSS && m == -INFINITY) ? 0.f : m;
         float rs = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[r], c, -m));
+          const float p = fast_exp2(fmaf(sacc[r], c, -mref));
           sacc[r] = p;
           rs += p;
         }
@@ -284,9 +316,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     l += xhalf(l);
     merge(smem + si * STAGE, wave_active);
     if (sp == 0 && wave_active) {
-      const float inv = 1.f / l;
-      if (qi < S) {
-        T* orow = O + ((size_t)bh * S + qi) * D;
+      // (CROSS: a row with no visible key has l = 0: O = 0, LSE = -inf)
+      const float inv = (CROSS && !(l > 0.f)) ? 0.f : 1.f / l;
+      if (qi < Sq) {
+        T* orow = O + ((size_t)bh * Sq + qi) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -295,10 +328,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
             store4<T>(orow + d, oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv,
                       oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
           }
-        if (h == 0 && LSE != nullptr) LSE[(size_t)bh * S + qi] = (m + __log2f(l)) * kLn2;
+        if (h == 0 && LSE != nullptr) LSE[(size_t)bh * Sq + qi] = (m + __log2f(l)) * kLn2;
       }
       // Only the O stores of a wave whose every lane stores are counted.
-      if (q0 + 31 < S) vm += 4 * NDB;
+      if (q0 + 31 < Sq) vm += 4 * NDB;
     }
     // Next item.
     cit = sched_item(sched, ++cr, g, G, BH);
@@ -307,6 +340,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
       nkt = item_nkt(cit);
       bh = cit % BH;
       q0 = item_qt(cit) * BR + qb * 32;
+      head_keys<CROSS>(kvlen, bh, H, Sq, Sk, cL, coff);
     }
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[i] = zero16();
@@ -328,35 +362,38 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   }
 }
 
-template <class E, int D, bool CAUSAL>
+template <class E, int D, bool CAUSAL, bool CROSS>
 static hipError_t launch(const FwdArgs& a) {
   constexpr int NW = is_bf16<E>() ? ATTN_FWD_NW_BF16 : ATTN_FWD_NW_F32;
   constexpr int NSPLIT = is_bf16<E>() ? ATTN_FWD_NSPLIT_BF16 : ATTN_FWD_NSPLIT_F32;
   constexpr int KPW = is_bf16<E>() ? ATTN_FWD_KPW_BF16 : ATTN_FWD_KPW_F32;
   constexpr int NST = is_bf16<E>() ? ATTN_FWD_NST_BF16 : ATTN_FWD_NST_F32;
   using T = typename E::T;
-  constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL>;
+  constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS>;
   constexpr int BR = 32 * (NW / NSPLIT);
-  const int nqt = (a.S + BR - 1) / BR;
+  const int nqt = (a.Sq + BR - 1) / BR;
   const int nitems = a.BH * nqt;
   const int grid = std::min(nitems, resident_workgroups<kern>(NW * 64));
-  // work of a query tile: its key tiles
+  // work of a query tile: its key tiles (with every key valid: the per-batch
+  // counts live on the device)
   constexpr int BK = 32 * NSPLIT * KPW;
   std::vector<int> works(nqt);
   for (int c = 0; c < nqt; ++c) {
     const int qt = nqt - 1 - c;
-    const int kend = CAUSAL ? std::min(a.S, qt * BR + BR) : a.S;
-    works[c] = (kend + BK - 1) / BK;
+    const int kend = CAUSAL ? std::min(a.Sk, qt * BR + BR + a.Sk - a.Sq) : a.Sk;
+    works[c] = std::max((kend + BK - 1) / BK, 1);
   }
   const Sched sched = make_sched(grid, a.BH, works);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
-                     (const T*)a.v, (T*)a.o, a.lse, a.S, a.scale * kLog2e, a.BH, nitems, sched);
+                     (const T*)a.v, (T*)a.o, a.lse, a.Sq, a.Sk, a.scale * kLog2e, a.BH, a.H,
+                     a.kvlen, nitems, sched);
   return hipGetLastError();
 }
 
 template <class E, int D>
 static hipError_t launch_c(const FwdArgs& a) {
-  return a.causal ? launch<E, D, true>(a) : launch<E, D, false>(a);
+  if (a.cross) return a.causal ? launch<E, D, true, true>(a) : launch<E, D, false, true>(a);
+  return a.causal ? launch<E, D, true, false>(a) : launch<E, D, false, false>(a);
 }
 
 template <class E>

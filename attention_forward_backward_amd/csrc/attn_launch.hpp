@@ -102,7 +102,9 @@ struct FwdArgs {
   const void *q, *k, *v;
   void* o;
   float* lse;  // null: not stored
-  int BH, S, D;
+  int BH, H, Sq, Sk, D;
+  const int* kvlen;  // valid keys per batch (device), or null: all Sk
+  bool cross;        // Sq != Sk or kvlen given: the general (cross-attention) kernels
   bool causal;
   float scale;
   hipStream_t stream;
@@ -113,10 +115,12 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float* lse;
   void *dq, *dk, *dv;
-  float* delta;  // workspace: D [B*H*S] f32, then LSE*log2(e) [B*H*S] f32
-  void* ds;      // workspace dS^T [B*H][SP][SP] (dtype), or null: dQ recomputes
-  int SP;        // row stride of dS (S rounded up to the key tile)
-  int BH, S, D;
+  float* delta;  // workspace: D [B*H*Sq] f32, then LSE*log2(e) [B*H*Sq] f32
+  void* ds;      // workspace dS^T [B*H][SPk][SPq] (dtype), or null: dQ recomputes
+  int SPq, SPk;  // query stride and key rows per head of dS^T (rounded up to the tile)
+  int BH, H, Sq, Sk, D;
+  const int* kvlen;
+  bool cross;
   bool causal;
   float scale;
   hipStream_t stream;

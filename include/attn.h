@@ -172,6 +172,45 @@ attn_status_t attn_bwd_dq(attn_dtype_t dtype,
                           int batch, int heads, int seq, int head_dim,
                           int causal, float scale, void* stream);
 
+/*
+ * Cross-attention and padded keys (the pages' text cross-attention of the
+ * diffusion workload and the one-token minimal-latency query, Sections 10
+ * and 4.3): the forward and backward above with separate query and key
+ * lengths and optional per-batch key counts.
+ *   q, o, dout, dq  [B,H,seq_q,D] dtype      lse  [B,H,seq_q] float32
+ *   k, v, dk, dv    [B,H,seq_k,D] dtype
+ *   kv_len          NULL (every key valid) or a DEVICE array of `batch`
+ *                   int32, 4-byte aligned: batch b has L_b = kv_len[b] valid
+ *                   keys (values are clamped to [0, seq_k] on the device;
+ *                   rows of k and v at or past L_b are never read).
+ * Key j is visible from query i iff j < L_b and, when causal,
+ * j <= i + L_b - seq_q: the causal diagonal is aligned with the end of the
+ * valid keys (with seq_q = seq_k = L_b this is the self-attention rule
+ * j <= i, and a one-token query sees every valid key).  A query row with no
+ * visible key gets O = 0 and LSE = -inf, and contributes no gradient; dK and
+ * dV rows at or past L_b are written as zeros.  The workspace sizes follow
+ * from (seq_q, seq_k): D and LSE*log2(e) per query row, and for the dS path
+ * dS transposed, [B*H][ceil(seq_k/128)*128][ceil(seq_q/128)*128].  Errors as
+ * for attn_fwd / attn_bwd (seq_q, seq_k <= 0 or a misaligned kv_len:
+ * ATTN_ERR_INVALID_ARG).
+ */
+attn_status_t attn_fwd_cross(attn_dtype_t dtype,
+                             const void* q, const void* k, const void* v,
+                             void* o, float* lse,
+                             int batch, int heads, int seq_q, int seq_k, int head_dim,
+                             const int* kv_len, int causal, float scale, void* stream);
+size_t attn_bwd_cross_workspace_size(attn_dtype_t dtype, int batch, int heads,
+                                     int seq_q, int seq_k, int head_dim, int causal);
+size_t attn_bwd_cross_workspace_size_min(attn_dtype_t dtype, int batch, int heads,
+                                         int seq_q, int seq_k, int head_dim, int causal);
+attn_status_t attn_bwd_cross(attn_dtype_t dtype,
+                             const void* q, const void* k, const void* v,
+                             const void* o, const void* dout, const float* lse,
+                             void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes,
+                             int batch, int heads, int seq_q, int seq_k, int head_dim,
+                             const int* kv_len, int causal, float scale, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status_t status);
 

@@ -17,10 +17,12 @@ def test_library_loads_and_exports_header_symbols():
     declared = afb.declared_symbols()
     assert set(declared) == {"attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dq",
                              "attn_bwd_dkdv", "attn_bwd_workspace_size",
-                             "attn_bwd_workspace_size_min", "attn_status_string", "attn_version"}
+                             "attn_bwd_workspace_size_min", "attn_fwd_cross", "attn_bwd_cross",
+                             "attn_bwd_cross_workspace_size", "attn_bwd_cross_workspace_size_min",
+                             "attn_status_string", "attn_version"}
     for name in declared:
         assert hasattr(L, name), name
-    assert afb.attn_version() == "0.2.0"
+    assert afb.attn_version() == "0.3.0"
     for code in range(5):
         assert afb.attn_status_string(code) not in ("", "unknown status")
     assert afb.attn_status_string(99) == "unknown status"
@@ -107,3 +109,28 @@ def test_no_cpu_fallback_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(afb, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         afb.lib()
+
+
+def _fwdx(dtype=0, q=FAKE, lse=FAKE, B=1, H=1, Sq=8, Sk=16, D=64, kvl=None, causal=1, scale=0.125):
+    return afb.lib().attn_fwd_cross(dtype, q, FAKE, FAKE, FAKE, lse, B, H, Sq, Sk, D, kvl, causal,
+                                    scale, None)
+
+
+def test_cross_validation_and_workspace():
+    assert _fwdx(Sq=0) == 1 and _fwdx(Sk=0) == 1 and _fwdx(Sk=-3) == 1
+    assert _fwdx(q=None) == 1 and _fwdx(lse=MIS) == 1
+    assert _fwdx(kvl=FAKE + 2) == 1                      # kv_len must be 4-byte aligned
+    assert _fwdx(D=48) == 2 and _fwdx(dtype=3) == 2
+    L = afb.lib()
+    p = [FAKE] * 10
+    assert L.attn_bwd_cross(0, *p, 16, 1, 1, 8, 16, 64, None, 1, 0.1, None) == 3  # workspace
+    assert L.attn_bwd_cross(0, *p, 1 << 20, 1, 1, 8, 16, 64, FAKE + 1, 1, 0.1, None) == 1
+    assert L.attn_bwd_cross(0, *p[:9], None, 1 << 20, 1, 1, 8, 16, 64, None, 1, 0.1, None) == 1
+    wx, wxm = afb.attn_bwd_cross_workspace_size, afb.attn_bwd_cross_workspace_size_min
+    # D and LSE*log2(e) per query row; dS^T [B*H][ceil(Sk/128)*128][ceil(Sq/128)*128]
+    assert wxm(0, 2, 3, 77, 1024, 64, False) == r256(2 * 2 * 3 * 77 * 4)
+    assert wx(0, 2, 3, 77, 1024, 64, False) == r256(2 * 2 * 3 * 77 * 4) + r256(6 * 1024 * 128 * 4)
+    assert wx(1, 2, 3, 1, 512, 64, True) == r256(2 * 6 * 1 * 4) + r256(6 * 512 * 128 * 2)
+    # equal lengths: the self-attention sizes
+    assert wx(0, 8, 12, 512, 512, 64, True) == afb.attn_bwd_workspace_size(0, 8, 12, 512, 64, True)
+    assert wx(0, 1, 1, 8, 0, 64, True) == 0 and wxm(0, 1, 1, 0, 8, 64, True) == 0
