@@ -184,3 +184,55 @@ def make_inputs(shape, seed: int, dtype: str = "f32", sigma_qkv: float = 1.0,
 
 def config_inputs(cfg: AttnConfig, seed: int, dtype: str) -> dict:
     return make_inputs(cfg.shape, seed, dtype, cfg.sigma_qkv, cfg.sigma_do)
+
+
+@dataclass(frozen=True)
+class CrossWorkload:
+    """A query/key-length pair with optional per-batch valid key counts."""
+    name: str
+    batch: int
+    heads: int
+    seq_q: int
+    seq_k: int
+    head_dim: int
+    causal: bool
+    padded: bool  # per-batch valid key counts drawn by ``key_lengths``
+    min_keys: int = 1
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+# Cross-attention and one-token workloads: a 77-token text-conditioning
+# cross-attention over a 64x64 latent grid (4096 queries), and a one-token
+# query over a 512-key context, with all keys valid or with padded batches.
+CROSS_WORKLOADS = {
+    "text_cross": CrossWorkload("text_cross", 2, 8, 4096, 77, 64, False, False),
+    "decode": CrossWorkload("decode", 8, 12, 1, 512, 64, True, False),
+    "decode_padded": CrossWorkload("decode_padded", 8, 12, 1, 512, 64, True, True, 64),
+}
+
+KEY_LENGTH_TENSOR_ID = 16
+
+
+def key_lengths(seed: int, batch: int, lo: int, hi: int) -> np.ndarray:
+    """int32 [batch] of valid key counts, uniform on lo..hi inclusive, from the
+    u2 uniforms of the generator's stream KEY_LENGTH_TENSOR_ID."""
+    if not 0 <= lo <= hi:
+        raise ValueError("need 0 <= lo <= hi")
+    _, u2 = uniforms(seed, KEY_LENGTH_TENSOR_ID, 0, batch)
+    return (lo + np.floor(u2 * (hi - lo + 1))).astype(np.int32)
+
+
+def cross_inputs(shape_q, shape_k, seed: int, dtype: str = "f32") -> dict:
+    """Q and dO of shape ``shape_q``, K and V of shape ``shape_k`` (the keys
+    come from seed + 100, so they differ from a same-seed query draw)."""
+    qi = make_inputs(shape_q, seed, dtype)
+    ki = make_inputs(shape_k, seed + 100, dtype)
+    out = {n: qi[n] for n in ("q", "do")}
+    out.update({n: ki[n] for n in ("k", "v")})
+    if dtype == "bf16":
+        out.update({n + "_bits": qi[n + "_bits"] for n in ("q", "do")})
+        out.update({n + "_bits": ki[n + "_bits"] for n in ("k", "v")})
+    return out

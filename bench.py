@@ -69,6 +69,8 @@ def parse():
                    help="backward workspace: full (dS stored, dQ as a GEMM) or min (dQ recomputes)")
     p.add_argument("--only-step", action="store_true",
                    help="time only the full step (used under a profiler)")
+    p.add_argument("--no-cross", action="store_true",
+                   help="skip the cross-attention and one-token workloads")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="instead of the benchmark, run 5 plain device-to-device copies of "
                         "BYTES bytes (the reference kernel for scaling HBM byte counters)")
@@ -265,10 +267,95 @@ def main():
         line[dt] = {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                     for kk, vv in results[dt].items()}
 
+    if not args.no_cross and not args.only_step:
+        line["cross"] = cross_section(dtypes, args, stream, log)
+
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the float64 oracle on the host")
         line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def visible_pairs(w, kv_len) -> int:
+    """Visible (query, key) pairs of a cross workload: query i sees key j iff
+    j < L_b and, when causal, j <= i + L_b - Sq."""
+    total = 0
+    for L in kv_len:
+        L = int(L)
+        if w.causal:
+            per = sum(max(0, min(L, i + 1 + L - w.seq_q)) for i in range(w.seq_q))
+        else:
+            per = w.seq_q * L
+        total += per
+    return total * w.heads
+
+
+def cross_section(dtypes, args, stream, log) -> dict:
+    """fwd and fwd+bwd time of the cross-attention and one-token workloads
+    (attn_fwd_cross / attn_bwd_cross), per arithmetic contract."""
+    import torch
+    import attention_forward_backward_amd as afb
+    from attention_forward_backward_amd import synth
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    out = {}
+    for wname, w in synth.CROSS_WORKLOADS.items():
+        B, H, Sq, Sk, D = w.batch, w.heads, w.seq_q, w.seq_k, w.head_dim
+        kvl = synth.key_lengths(args.seed, B, w.min_keys, Sk) if w.padded else None
+        pairs = visible_pairs(w, kvl if kvl is not None else [Sk] * B)
+        rec = {"shape": f"B{B} H{H} Sq{Sq} Sk{Sk} D{D} {'causal' if w.causal else 'non-causal'}",
+               "kv_len": None if kvl is None else kvl.tolist(), "visible_pairs": pairs}
+        for dt in dtypes:
+            sd = "bf16" if dt == "bf16" else "f32"
+            inp = synth.cross_inputs((B, H, Sq, D), (B, H, Sk, D), args.seed, sd)
+
+            def dev(n):
+                if dt == "bf16":
+                    return torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+                return torch.from_numpy(inp[n]).cuda()
+
+            q, k, v, do = (dev(n) for n in ("q", "k", "v", "do"))
+            kv = None if kvl is None else torch.from_numpy(kvl).cuda()
+            o, dq = torch.empty_like(q), torch.empty_like(q)
+            dk, dv = torch.empty_like(k), torch.empty_like(v)
+            lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda")
+            code = {"bf16": afb.ATTN_BF16, "f32": afb.ATTN_F32,
+                    "f32_bf16fwd": afb.ATTN_F32_BF16FWD}[dt]
+            ws = torch.empty(afb.attn_bwd_cross_workspace_size(code, B, H, Sq, Sk, D, w.causal),
+                             dtype=torch.uint8, device="cuda")
+            fast = dt == "f32_bf16fwd"
+
+            def fwd():
+                afb.attn_fwd_cross(q, k, v, o, lse, kv, w.causal, w.scale, stream,
+                                   bf16_operands=fast)
+
+            def step():
+                fwd()
+                afb.attn_bwd_cross(q, k, v, o, do, lse, dq, dk, dv, ws, kv, w.causal, w.scale,
+                                   stream)
+
+            log(f"[bench] cross {wname} {rec['shape']} dtype={dt}")
+            ms_f = timed(fwd, args.steps, args.warmup)
+            ms_s = timed(step, args.steps, args.warmup)
+            rec[dt] = {"fwd_us": round(ms_f * 1e3, 2), "fwd_bwd_us": round(ms_s * 1e3, 2),
+                       "fwd_tflops": round(4 * D * pairs / (ms_f * 1e-3) / 1e12, 3),
+                       "fwd_bwd_tflops": round(14 * D * pairs / (ms_s * 1e-3) / 1e12, 3)}
+            del q, k, v, do, o, dq, dk, dv, lse, ws
+        out[wname] = rec
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(cfg, seed: int, target_s: float) -> dict:

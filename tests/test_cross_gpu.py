@@ -25,11 +25,7 @@ CASES = [
 
 
 def _inputs(B, H, Sq, Sk, D, dt, seed=0):
-    qi = synth.make_inputs((B, H, Sq, D), seed, dt)
-    ki = synth.make_inputs((B, H, Sk, D), seed + 100, dt)
-    return {"q": qi["q"], "do": qi["do"], "k": ki["k"], "v": ki["v"],
-            "q_bits": qi.get("q_bits"), "do_bits": qi.get("do_bits"),
-            "k_bits": ki.get("k_bits"), "v_bits": ki.get("v_bits")}
+    return synth.cross_inputs((B, H, Sq, D), (B, H, Sk, D), seed, dt)
 
 
 def _err_lse(got, ref):

@@ -79,3 +79,21 @@ def test_config_accounting():
     assert c.flops["fwd_bwd"] == 14 * 64 * 12607488
     e = synth.CONFIGS["ragged_encoder"]
     assert e.pairs == 32 * 8 * 197 * 197 and not e.causal and e.sigma_qkv == 0.5
+
+
+def test_key_lengths_range_and_determinism():
+    a = synth.key_lengths(0, 4096, 64, 512)
+    assert a.dtype == np.int32 and a.min() >= 64 and a.max() <= 512
+    assert a.min() == 64 and a.max() == 512  # both ends reachable
+    assert np.array_equal(a, synth.key_lengths(0, 4096, 64, 512))
+    assert not np.array_equal(a, synth.key_lengths(1, 4096, 64, 512))
+    assert np.array_equal(synth.key_lengths(3, 5, 7, 7), np.full(5, 7))
+
+
+def test_cross_inputs_shapes_and_independent_keys():
+    x = synth.cross_inputs((2, 3, 5, 32), (2, 3, 9, 32), 0, "bf16")
+    assert x["q"].shape == x["do"].shape == (2, 3, 5, 32)
+    assert x["k"].shape == x["v"].shape == (2, 3, 9, 32)
+    assert set(x) >= {"q_bits", "k_bits", "v_bits", "do_bits"}
+    same = synth.make_inputs((2, 3, 9, 32), 0, "f32")
+    assert not np.array_equal(synth.cross_inputs((2, 3, 9, 32), (2, 3, 9, 32), 0)["k"], same["k"])
