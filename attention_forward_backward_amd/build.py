@@ -34,9 +34,12 @@ HIP_FLAGS = [
 ]
 # Per-source additions.  The f32 dK+dV kernel (D <= 64) is asked to fit two
 # waves per SIMD (256 registers); LLVM's ILP-first scheduler is the one that
-# meets that bound without spilling, so its source uses it.
+# meets that bound without spilling, so its source uses it.  The few-query
+# forward needs every load of an iteration issued before the first use; the
+# default scheduler interleaves them with the arithmetic and waits for each.
 FILE_FLAGS = {
     "attn_bwd_dkdv.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attn_fwd_small.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
 }
 
 

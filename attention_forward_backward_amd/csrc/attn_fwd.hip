@@ -407,6 +407,8 @@ static hipError_t launch_d(const FwdArgs& a) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.Sq <= (a.bf16 ? ATTN_FWD_SMALL_MAXQ_BF16 : ATTN_FWD_SMALL_MAXQ_F32))
+    return launch_fwd_small(a);
   if (a.bf16) return launch_d<EBF16>(a);
   return a.bf16_operands ? launch_d<EF32B>(a) : launch_d<EF32>(a);
 }

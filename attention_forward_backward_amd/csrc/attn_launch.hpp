@@ -93,6 +93,36 @@
 #ifndef ATTN_DKDV_MINW_F32
 #define ATTN_DKDV_MINW_F32 2
 #endif
+// Forward of heads with few queries: the VALU kernel of attn_fwd_small.hip
+// takes heads of at most ATTN_FWD_SMALL_MAXQ_F32 queries with float32
+// storage and ATTN_FWD_SMALL_MAXQ_BF16 with bf16 storage; longer ones run on
+// the MFMA kernel.  One-query heads use ATTN_FWD_SMALL_NW1 waves per
+// workgroup and ATTN_FWD_SMALL_U1 keys per lane row and iteration, groups
+// of four queries ATTN_FWD_SMALL_NW4 and ATTN_FWD_SMALL_U4 (at D = 128 a
+// half and a quarter of those keys).  Measured on MI355X at B8 H12 Sk512
+// D64 causal: the VALU kernel wins at Sq = 1 in both storage types (f32
+// 4.6 us, bf16 4.8 us, against 28.7 and 9.5 on the MFMA kernel) and up to
+// Sq = 8 with float32 storage; 16 waves of 4 keys per row are best at
+// Sq = 1, 8 waves of 16 at Sq = 4 (16 waves there exceed 128 registers per
+// lane and spill).
+#ifndef ATTN_FWD_SMALL_MAXQ_F32
+#define ATTN_FWD_SMALL_MAXQ_F32 8
+#endif
+#ifndef ATTN_FWD_SMALL_MAXQ_BF16
+#define ATTN_FWD_SMALL_MAXQ_BF16 1
+#endif
+#ifndef ATTN_FWD_SMALL_NW1
+#define ATTN_FWD_SMALL_NW1 16
+#endif
+#ifndef ATTN_FWD_SMALL_U1
+#define ATTN_FWD_SMALL_U1 4
+#endif
+#ifndef ATTN_FWD_SMALL_NW4
+#define ATTN_FWD_SMALL_NW4 8
+#endif
+#ifndef ATTN_FWD_SMALL_U4
+#define ATTN_FWD_SMALL_U4 16
+#endif
 
 namespace attn {
 
@@ -229,6 +259,7 @@ inline Sched make_sched(int G, int BH, const std::vector<int>& works) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_fwd_small(const FwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_prep(const BwdArgs& a);

@@ -292,7 +292,9 @@ def visible_pairs(w, kv_len) -> int:
 
 def cross_section(dtypes, args, stream, log) -> dict:
     """fwd and fwd+bwd time of the cross-attention and one-token workloads
-    (attn_fwd_cross / attn_bwd_cross), per arithmetic contract."""
+    (attn_fwd_cross / attn_bwd_cross), per arithmetic contract: from replays
+    of a HIP graph (fwd_us, fwd_bwd_us: GPU time, the one-token calls are
+    shorter than a Python launch) and from eager calls (*_eager)."""
     import torch
     import attention_forward_backward_amd as afb
     from attention_forward_backward_amd import synth
@@ -309,6 +311,29 @@ def cross_section(dtypes, args, stream, log) -> dict:
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
+
+    def timed_graph(fn, per_graph=20, replays=30):
+        """Per-call time of fn from replays of a HIP graph of per_graph calls
+        (no host launch cost between calls)."""
+        for _ in range(per_graph):
+            fn()
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(per_graph):
+                fn()
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            gr.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del gr
+        return e0.elapsed_time(e1) / (replays * per_graph)
 
     out = {}
     for wname, w in synth.CROSS_WORKLOADS.items():
@@ -337,21 +362,34 @@ def cross_section(dtypes, args, stream, log) -> dict:
                              dtype=torch.uint8, device="cuda")
             fast = dt == "f32_bf16fwd"
 
+            # stream=None: the current stream (the capture stream in a graph)
             def fwd():
-                afb.attn_fwd_cross(q, k, v, o, lse, kv, w.causal, w.scale, stream,
+                afb.attn_fwd_cross(q, k, v, o, lse, kv, w.causal, w.scale, None,
                                    bf16_operands=fast)
 
             def step():
                 fwd()
                 afb.attn_bwd_cross(q, k, v, o, do, lse, dq, dk, dv, ws, kv, w.causal, w.scale,
-                                   stream)
+                                   None)
 
             log(f"[bench] cross {wname} {rec['shape']} dtype={dt}")
-            ms_f = timed(fwd, args.steps, args.warmup)
-            ms_s = timed(step, args.steps, args.warmup)
+            ms_fe = timed(fwd, args.steps, args.warmup)
+            ms_se = timed(step, args.steps, args.warmup)
+            ms_f = timed_graph(fwd)
+            ms_s = timed_graph(step)
+            # forward's algorithmic HBM bytes: Q and O, the valid K and V
+            # rows, the LSE
+            esz = 2 if dt == "bf16" else 4
+            nkeys = int(sum(kvl)) if kvl is not None else B * Sk
+            fbytes = (2 * B * H * Sq * D + 2 * H * nkeys * D) * esz + B * H * Sq * 4
+            gbs = fbytes / (ms_f * 1e-3) / 1e9
             rec[dt] = {"fwd_us": round(ms_f * 1e3, 2), "fwd_bwd_us": round(ms_s * 1e3, 2),
+                       "fwd_us_eager": round(ms_fe * 1e3, 2),
+                       "fwd_bwd_us_eager": round(ms_se * 1e3, 2),
                        "fwd_tflops": round(4 * D * pairs / (ms_f * 1e-3) / 1e12, 3),
-                       "fwd_bwd_tflops": round(14 * D * pairs / (ms_s * 1e-3) / 1e12, 3)}
+                       "fwd_bwd_tflops": round(14 * D * pairs / (ms_s * 1e-3) / 1e12, 3),
+                       "fwd_bytes": fbytes, "fwd_gbs": round(gbs, 1),
+                       "fwd_frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
             del q, k, v, do, o, dq, dk, dv, lse, ws
         out[wname] = rec
     torch.cuda.empty_cache()

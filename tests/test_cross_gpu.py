@@ -21,6 +21,13 @@ CASES = [
     ("more_queries_than_keys", 2, 4, 200, 130, 64, True, [130, 97]),
     ("chunked_prefill_d128", 2, 4, 96, 300, 128, True, [300, 250]),
     ("padded_self_d32", 3, 4, 197, 197, 32, True, [197, 120, 64]),
+    # few-query heads (the VALU forward for Sq <= 16): rows with no visible
+    # key (L = 3 < Sq = 5), every head_dim, one and sixteen queries
+    ("few_queries_causal", 2, 4, 5, 300, 64, True, [300, 3]),
+    ("sixteen_queries_d128", 2, 4, 16, 1000, 128, False, [1000, 777]),
+    ("decode_d32_long", 3, 4, 1, 2000, 32, True, [2000, 1, 1500]),
+    ("decode_d128_ragged", 2, 3, 1, 333, 128, False, None),
+    ("three_queries_d32", 2, 3, 3, 70, 32, True, None),
 ]
 
 
@@ -42,7 +49,7 @@ def test_cross_parity(name, B, H, Sq, Sk, D, causal, kvl, dt, ws):
     note(f"[gpu case] cross {name} B{B} H{H} Sq{Sq} Sk{Sk} D{D} causal={causal} kv_len={kvl} "
          f"dtype={dt} workspace={ws} -> attn_fwd_cross + attn_bwd_cross")
     inp = _inputs(B, H, Sq, Sk, D, dt)
-    dev = {n: to_device(inp[n], inp[n + "_bits"], dt) for n in ("q", "k", "v", "do")}
+    dev = {n: to_device(inp[n], inp.get(n + "_bits"), dt) for n in ("q", "k", "v", "do")}
     kv_len = None if kvl is None else torch.tensor(kvl, dtype=torch.int32, device="cuda")
     if kvl is not None:  # padded rows are never read: poison them
         for b, L in enumerate(kvl):
@@ -106,3 +113,38 @@ def test_cross_equal_lengths_match_self_attention():
         outs.append([to_host(t) for t in (o, lse, *g)])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("Sq,Sk,D,causal,kvl", [(1, 512, 64, True, [512, 200]),
+                                               (5, 300, 128, True, [300, 4]),
+                                               (16, 257, 32, False, None)])
+def test_few_query_practical_contract(Sq, Sk, D, causal, kvl):
+    """The practical contract (float32 tensors, bf16-rounded forward
+    operands) on the few-query forward: against the oracle on the rounded
+    operands at the reduced-precision gate, and visibly different from the
+    strict forward."""
+    import torch
+    B, H = 2, 3
+    note(f"[gpu case] few-query practical B{B} H{H} Sq{Sq} Sk{Sk} D{D} causal={causal} "
+         f"kv_len={kvl} -> attn_fwd_cross(bf16_operands)")
+    inp = _inputs(B, H, Sq, Sk, D, "f32", seed=4)
+    rnd = _inputs(B, H, Sq, Sk, D, "bf16", seed=4)
+    dev = {n: to_device(inp[n], None, "f32") for n in ("q", "k", "v")}
+    kv_len = None if kvl is None else torch.tensor(kvl, dtype=torch.int32, device="cuda")
+    o = torch.full((B, H, Sq, D), float("nan"), device="cuda")
+    o_s = torch.full((B, H, Sq, D), float("nan"), device="cuda")
+    lse = torch.full((B, H, Sq), float("nan"), device="cuda")
+    scale = 1.0 / np.sqrt(D)
+    afb.attn_fwd_cross(dev["q"], dev["k"], dev["v"], o, lse, kv_len, causal, scale,
+                       bf16_operands=True)
+    afb.attn_fwd_cross(dev["q"], dev["k"], dev["v"], o_s, None, kv_len, causal, scale)
+    torch.cuda.synchronize()
+    kvn = None if kvl is None else np.array(kvl)
+    o_r, lse_r = oracle.attention_forward(rnd["q"], rnd["k"], rnd["v"], causal, scale, kvn)
+    o_f, _ = oracle.attention_forward(inp["q"], inp["k"], inp["v"], causal, scale, kvn)
+    ho, hl, hs = to_host(o), to_host(lse), to_host(o_s)
+    e = {"o": max_rel_err(ho, o_r), "lse": _err_lse(hl, lse_r), "o_strict": max_rel_err(hs, o_f)}
+    diff = np.abs(ho - hs).max() / np.abs(hs).max()
+    note("  errors " + ", ".join(f"{k}={v:.2e}" for k, v in e.items()) + f"; |O - O_strict| {diff:.2e}")
+    assert e["o"] <= TOL["bf16"] and e["lse"] <= TOL["bf16"] and e["o_strict"] <= TOL["f32"]
+    assert diff > TOL["f32"], diff

@@ -31,7 +31,7 @@ def test_config_parity(name, dtype, seed, ws):
     assert max_rel_err(host["lse2"], ref["lse"] * np.log2(np.e)) <= TOL[dtype]
 
 
-MICRO = [(S, D, causal) for S in (1, 17, 33, 67, 130, 197) for D in (32, 64, 128)
+MICRO = [(S, D, causal) for S in (1, 5, 16, 17, 33, 67, 130, 197) for D in (32, 64, 128)
          for causal in (True, False)]
 
 

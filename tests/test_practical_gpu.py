@@ -67,7 +67,7 @@ def test_practical_contract(name, ws):
 
 @pytest.mark.parametrize("mode", ["f32", "bf16", "f32_bf16fwd"])
 @pytest.mark.parametrize("S,D,causal", [(197, 64, False), (130, 128, True), (64, 32, True),
-                                        (512, 64, True)])
+                                        (512, 64, True), (1, 64, True), (16, 128, False)])
 def test_forward_without_lse(mode, S, D, causal):
     """lse = NULL stores no LSE and leaves O bit-identical."""
     import torch
