@@ -56,10 +56,26 @@ size_t ws_full_bytes(attn_dtype_t dtype, int batch, int heads, int sq, int sk) {
          round256((size_t)batch * heads * ds_stride(sk) * ds_stride(sq) * esize);
 }
 
+// dK, dV partials of the query-chunk split, [2][nqs][B*H][Sk][D] f32 (none
+// when the shape needs no split; the backward arithmetic is f32 unless the
+// tensors are bf16).
+size_t ws_part_bytes(attn_dtype_t dtype, int batch, int heads, int sq, int sk, int head_dim) {
+  const int nqs = attn::dkdv_query_chunks(dtype == ATTN_BF16, (long long)batch * heads, sq, sk);
+  return nqs > 1 ? round256(2 * (size_t)nqs * batch * heads * sk * head_dim * sizeof(float)) : 0;
+}
+
+// Recommended workspace: the dS path plus, for shapes with few key tiles per
+// head, room for the dK, dV partials.
+size_t ws_rec_bytes(attn_dtype_t dtype, int batch, int heads, int sq, int sk, int head_dim) {
+  return ws_full_bytes(dtype, batch, heads, sq, sk) +
+         ws_part_bytes(dtype, batch, heads, sq, sk, head_dim);
+}
+
 attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
-// Backward launch descriptor; the dS path is taken iff the workspace holds
-// the full size.
+// Backward launch descriptor.  The dS path is taken iff the workspace holds
+// the minimum plus dS^T; the dK+dV query split iff it also holds the
+// partials (after dS^T, or after the minimum without the dS path).
 attn::BwdArgs make_bwd(attn_dtype_t dtype, const void* q, const void* k, const void* v,
                        const void* o, const void* dout, const float* lse, void* dq, void* dk,
                        void* dv, void* ws, size_t ws_bytes, int batch, int heads, int sq, int sk,
@@ -69,8 +85,16 @@ attn::BwdArgs make_bwd(attn_dtype_t dtype, const void* q, const void* k, const v
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.delta = static_cast<float*>(ws);
-  const bool full = ws_bytes >= ws_full_bytes(dtype, batch, heads, sq, sk);
-  a.ds = full ? static_cast<char*>(ws) + ws_min_bytes(batch, heads, sq) : nullptr;
+  const size_t wmin = ws_min_bytes(batch, heads, sq);
+  const size_t wfull = ws_full_bytes(dtype, batch, heads, sq, sk);
+  const size_t wpart = ws_part_bytes(dtype, batch, heads, sq, sk, head_dim);
+  const bool full = ws_bytes >= wfull;
+  const bool split = wpart > 0 && ws_bytes >= (full ? wfull : wmin) + wpart;
+  a.ds = full ? static_cast<char*>(ws) + wmin : nullptr;
+  a.part = split ? reinterpret_cast<float*>(static_cast<char*>(ws) + (full ? wfull : wmin))
+                 : nullptr;
+  a.nqs = split ? attn::dkdv_query_chunks(dtype == ATTN_BF16, (long long)batch * heads, sq, sk)
+                : 1;
   a.SPq = ds_stride(sq); a.SPk = ds_stride(sk);
   a.BH = batch * heads; a.H = heads; a.Sq = sq; a.Sk = sk; a.D = head_dim;
   a.kvlen = kvlen;
@@ -142,7 +166,7 @@ attn_status_t attn_fwd_cross(attn_dtype_t dtype, const void* q, const void* k, c
 size_t attn_bwd_workspace_size(attn_dtype_t dtype, int batch, int heads, int seq, int head_dim,
                                int causal) {
   if (check_shape(dtype, batch, heads, seq, seq, head_dim, causal, 1.f, false) != ATTN_OK) return 0;
-  return ws_full_bytes(dtype, batch, heads, seq, seq);
+  return ws_rec_bytes(dtype, batch, heads, seq, seq, head_dim);
 }
 
 size_t attn_bwd_workspace_size_min(attn_dtype_t dtype, int batch, int heads, int seq,
@@ -155,7 +179,7 @@ size_t attn_bwd_cross_workspace_size(attn_dtype_t dtype, int batch, int heads, i
                                      int seq_k, int head_dim, int causal) {
   if (check_shape(dtype, batch, heads, seq_q, seq_k, head_dim, causal, 1.f, false) != ATTN_OK)
     return 0;
-  return ws_full_bytes(dtype, batch, heads, seq_q, seq_k);
+  return ws_rec_bytes(dtype, batch, heads, seq_q, seq_k, head_dim);
 }
 
 size_t attn_bwd_cross_workspace_size_min(attn_dtype_t dtype, int batch, int heads, int seq_q,

@@ -34,17 +34,24 @@
 
 namespace attn {
 
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS, bool CROSS>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS, bool CROSS,
+          bool QSPLIT>
 __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_F32 : 1) void bwd_dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
     typename E::T* __restrict__ dSout, int SPq, int SPk, int Sq, int Sk_, int Lws, float c,
-    float scale, int BH, int H, const int* __restrict__ kvlen, int nitems, const Sched sched) {
+    float scale, int BH, int H, const int* __restrict__ kvlen, float* __restrict__ part, int nqs_,
+    int qpc_, int nitems, const Sched sched) {
   // Queries Sq, keys Sk (one length in self-attention, CROSS = false); per
   // batch*head the first L keys exist and key j is visible from query i iff
   // j < L and, when causal, j <= i + off (head_keys).  Lws: offset of the
   // LSE*log2(e) vector in the workspace (B*H*Sq).
+  // Query chunks: item (class c, head bh) is key tile c / nqs over query
+  // tiles [(c % nqs) * qpc, (c % nqs + 1) * qpc); with nqs > 1 it stores
+  // its dK (scaled) and dV sums as float32 partials, part[qc][bh][Sk][D]
+  // then part[nqs + qc][bh][Sk][D], which a second kernel adds up.  Without
+  // QSPLIT there is one chunk of every query tile and dK, dV are stored.
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-key blocks per item
@@ -77,6 +84,8 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   const int g = blockIdx.x, G = gridDim.x;
   const int Sk = CROSS ? Sk_ : Sq;
   const int nqt = (Sq + BQ - 1) / BQ;
+  const int nqs = QSPLIT ? nqs_ : 1;
+  const int qpc = QSPLIT ? qpc_ : nqt;
   const unsigned lane_off = LD::lane_offset(w, lane);
   // First query tile with a query that sees a key of key tile kt (nqt: none).
   auto first_qt = [&](int kt, int L, int off) {
@@ -92,7 +101,8 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   // item lit, whose K and V rows it stages; else query tile lqt).  Every
   // stream tile is NL loads per wave (the header also loads statistics it
   // does not use, to keep that count).
-  int lr = 0, lit = sched_item(sched, 0, g, G, BH), lqt = -1, lkt = lit / BH;
+  int lr = 0, lit = sched_item(sched, 0, g, G, BH), lqt = -1, lkt = lit / BH / nqs;
+  int lqc = lit / BH % nqs, lqend = nqt;
   size_t lhq = (size_t)(lit % BH) * Sq, lhk = (size_t)(lit % BH) * Sk;  // first rows of the head
   int lL, loff;
   head_keys<CROSS>(kvlen, lit % BH, H, Sq, Sk, lL, loff);
@@ -100,7 +110,8 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   auto next_item = [&]() {
     lit = sched_item(sched, ++lr, g, G, BH);
     lqt = -1;
-    lkt = lit / BH;
+    lkt = lit / BH / nqs;
+    lqc = lit / BH % nqs;
     lhq = (size_t)(lit % BH) * Sq;
     lhk = (size_t)(lit % BH) * Sk;
     head_keys<CROSS>(kvlen, lit % BH, H, Sq, Sk, lL, loff);
@@ -121,8 +132,12 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     ++nissued;
     if (head) {
       lqt = first_qt(lkt, lL, loff);
-      if (lqt >= nqt) next_item();  // (CROSS: an item that no query sees)
-    } else if (++lqt == nqt) {
+      if constexpr (QSPLIT) {
+        lqt = max(lqt, lqc * qpc);
+        lqend = min(nqt, (lqc + 1) * qpc);
+      }
+      if (lqt >= (QSPLIT ? lqend : nqt)) next_item();  // (an item that no query of its chunk sees)
+    } else if (++lqt == (QSPLIT ? lqend : nqt)) {
       next_item();
     }
   };
@@ -139,7 +154,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   // `buf` (an LDS stage no load targets), then store dK and dV.
   // Returns the store instructions counted for the tile waits: only rows that
   // every lane writes, so the count never exceeds the instructions issued.
-  auto merge_store = [&](char* buf, int bh, int k0, bool active) -> int {
+  auto merge_store = [&](char* buf, int bh, int qc, int k0, bool active) -> int {
     if constexpr (NSPLIT > 1) {
       float* cb = reinterpret_cast<float*>(buf);
       constexpr int PER = (NPASS == 1 ? 2 : 1) * 16 * NDB;  // floats per lane per helper wave
@@ -177,20 +192,38 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     int nstores = 0;
     if (sp == 0 && active) {
       // element r of acc[db]: row k0 + out_row(r, h), column db*32 + n
-      T* dk = dK + (size_t)bh * Sk * D;
-      T* dv = dV + (size_t)bh * Sk * D;
+      if constexpr (!QSPLIT) {
+        T* dk = dK + (size_t)bh * Sk * D;
+        T* dv = dV + (size_t)bh * Sk * D;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = k0 + out_row(r, h);
-        if (row < Sk) {
+        for (int r = 0; r < 16; ++r) {
+          const int row = k0 + out_row(r, h);
+          if (row < Sk) {
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dk[(size_t)row * D + db * 32 + n] = (T)(dkacc[db][r] * scale);
-            dv[(size_t)row * D + db * 32 + n] = (T)dvacc[db][r];
+            for (int db = 0; db < NDB; ++db) {
+              dk[(size_t)row * D + db * 32 + n] = (T)(dkacc[db][r] * scale);
+              dv[(size_t)row * D + db * 32 + n] = (T)dvacc[db][r];
+            }
           }
         }
-        if (k0 + out_row(r, 1) < Sk) nstores += 2 * NDB;
+      } else {
+        float* pk = part + ((size_t)qc * BH + bh) * Sk * D;
+        float* pv = part + ((size_t)(nqs + qc) * BH + bh) * Sk * D;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = k0 + out_row(r, h);
+          if (row < Sk) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+              pk[(size_t)row * D + db * 32 + n] = dkacc[db][r] * scale;
+              pv[(size_t)row * D + db * 32 + n] = dvacc[db][r];
+            }
+          }
+        }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (k0 + out_row(r, 1) < Sk) nstores += 2 * NDB;
     }
     return nstores;
   };
@@ -205,7 +238,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   for (int cr = 0;; ++cr) {
     const int cit = sched_item(sched, cr, g, G, BH);
     if (cit >= nitems) break;
-    const int kt = cit / BH, bh = cit % BH;
+    const int kt = cit / BH / nqs, qc = cit / BH % nqs, bh = cit % BH;
     const int k0 = kt * BKV + kbk * 32;
     const int kj = k0 + n;
     const bool wave_active = k0 < Sk;
@@ -229,7 +262,9 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     }
     ++pos;
 
-    for (int qt = first_qt(kt, cL, coff); qt < nqt; ++qt, ++pos) {
+    const int qbeg = QSPLIT ? max(first_qt(kt, cL, coff), qc * qpc) : first_qt(kt, cL, coff);
+    const int qend = QSPLIT ? min(nqt, (qc + 1) * qpc) : nqt;
+    for (int qt = qbeg; qt < qend; ++qt, ++pos) {
       if (estores == 0) wait_tiles<NL, NSTORE>(nissued - pos - 1, stored);
       else wait_vmem_dyn(NL * (nissued - pos - 1) + NSTORE * stored + estores);
       stored = 0;
@@ -330,41 +365,85 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
 
     // The item is done: merge through the stage of its last tile (the tiles
     // in flight are the next NST-1, so no load targets it).
-    estores = merge_store(smem + ((pos - 1) % NST) * STAGE, bh, k0, wave_active);
+    estores = merge_store(smem + ((pos - 1) % NST) * STAGE, bh, qc, k0, wave_active);
   }
 }
 
-template <class E, int D, bool CAUSAL, bool WDS, bool CROSS>
+// dK = sum over the query chunks of the float32 partials, and dV likewise,
+// in chunk order (deterministic); four elements per thread.
+template <class T>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ part,
+                                                              T* __restrict__ dK,
+                                                              T* __restrict__ dV, int nqs,
+                                                              long long nel4) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nel4) return;
+  const f32x4* pk = reinterpret_cast<const f32x4*>(part) + i;
+  const f32x4* pv = pk + (size_t)nqs * nel4;
+  f32x4 ak = pk[0], av = pv[0];
+  for (int qc = 1; qc < nqs; ++qc) {
+    const f32x4 xk = pk[(size_t)qc * nel4], xv = pv[(size_t)qc * nel4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ak[e] += xk[e];
+      av[e] += xv[e];
+    }
+  }
+  store4<T>(dK + 4 * i, ak[0], ak[1], ak[2], ak[3]);
+  store4<T>(dV + 4 * i, av[0], av[1], av[2], av[3]);
+}
+
+template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool QSPLIT>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int NW = is_bf16<E>() ? ATTN_DKDV_NW_BF16 : ATTN_DKDV_NW_F32;
   constexpr int NSPLIT = is_bf16<E>() ? ATTN_DKDV_NSPLIT_BF16 : ATTN_DKDV_NSPLIT_F32;
   constexpr int KPW = is_bf16<E>() ? ATTN_DKDV_KPW_BF16 : ATTN_DKDV_KPW_F32;
   constexpr int NST = is_bf16<E>() ? ATTN_DKDV_NST_BF16 : ATTN_DKDV_NST_F32;
   using T = typename E::T;
-  constexpr auto kern = bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS>;
+  constexpr auto kern = bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS, QSPLIT>;
   constexpr int BKV = 32 * (NW / NSPLIT);
-  const int nkt = (a.Sk + BKV - 1) / BKV;
-  const int nitems = a.BH * nkt;
-  const int grid = std::min(nitems, resident_workgroups<kern>(NW * 64));
-  // work of a key tile: its header tile and the query tiles it visits (with
-  // every key valid: the per-batch counts live on the device)
   constexpr int BQ = 32 * NSPLIT * KPW;
+  static_assert(BKV == dkdv_key_tile(is_bf16<E>()) && BQ == dkdv_query_tile(is_bf16<E>()),
+                "tile sizes of the query-chunk choice");
+  const int nkt = (a.Sk + BKV - 1) / BKV;
   const int nqt = (a.Sq + BQ - 1) / BQ;
+  const int nqs = QSPLIT ? a.nqs : 1;
+  const int qpc = (nqt + nqs - 1) / nqs;
+  const int nitems = a.BH * nkt * nqs;
+  const int grid = std::min(nitems, resident_workgroups<kern>(NW * 64));
+  // work of class c = (key tile c / nqs, query chunk c % nqs): its header
+  // tile and the query tiles it visits (with every key valid: the per-batch
+  // counts live on the device)
   const int off = a.Sk - a.Sq;
-  std::vector<int> works(nkt);
-  for (int kt = 0; kt < nkt; ++kt)
-    works[kt] = 1 + nqt - (CAUSAL ? std::min(nqt, std::max(0, kt * BKV - off) / BQ) : 0);
+  std::vector<int> works(nkt * nqs);
+  for (int c = 0; c < nkt * nqs; ++c) {
+    const int kt = c / nqs, qc = c % nqs;
+    const int fq = CAUSAL ? std::min(nqt, std::max(0, kt * BKV - off) / BQ) : 0;
+    const int lo = std::max(fq, qc * qpc), hi = std::min(nqt, (qc + 1) * qpc);
+    works[c] = 1 + std::max(0, hi - lo);
+  }
   const Sched sched = make_sched(grid, a.BH, works);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SPq,
                      a.SPk, a.Sq, a.Sk, a.BH * a.Sq, a.scale * kLog2e, a.scale, a.BH, a.H, a.kvlen,
-                     nitems, sched);
+                     QSPLIT ? a.part : nullptr, nqs, qpc, nitems, sched);
+  if (QSPLIT) {
+    const long long nel4 = (long long)a.BH * a.Sk * D / 4;
+    hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<T>, dim3((unsigned)((nel4 + 255) / 256)), dim3(256),
+                       0, a.stream, a.part, (T*)a.dk, (T*)a.dv, nqs, nel4);
+  }
   return hipGetLastError();
+}
+
+template <class E, int D, bool CAUSAL, bool WDS, bool CROSS>
+static hipError_t launch_s(const BwdArgs& a) {
+  if (a.part != nullptr && a.nqs > 1) return launch<E, D, CAUSAL, WDS, CROSS, true>(a);
+  return launch<E, D, CAUSAL, WDS, CROSS, false>(a);
 }
 
 template <class E, int D, bool CAUSAL, bool WDS>
 static hipError_t launch_x(const BwdArgs& a) {
-  return a.cross ? launch<E, D, CAUSAL, WDS, true>(a) : launch<E, D, CAUSAL, WDS, false>(a);
+  return a.cross ? launch_s<E, D, CAUSAL, WDS, true>(a) : launch_s<E, D, CAUSAL, WDS, false>(a);
 }
 
 template <class E, int D>

@@ -93,6 +93,16 @@
 #ifndef ATTN_DKDV_MINW_F32
 #define ATTN_DKDV_MINW_F32 2
 #endif
+// Query-chunk split of the dK+dV pass (dkdv_query_chunks).
+#ifndef ATTN_DKDV_SPLIT_BELOW
+#define ATTN_DKDV_SPLIT_BELOW 256
+#endif
+#ifndef ATTN_DKDV_SPLIT_TARGET
+#define ATTN_DKDV_SPLIT_TARGET 512
+#endif
+#ifndef ATTN_DKDV_QCHUNK_MIN
+#define ATTN_DKDV_QCHUNK_MIN 4
+#endif
 // Forward of heads with few queries: the VALU kernel of attn_fwd_small.hip
 // takes heads of at most ATTN_FWD_SMALL_MAXQ_F32 queries with float32
 // storage and ATTN_FWD_SMALL_MAXQ_BF16 with bf16 storage; longer ones run on
@@ -147,6 +157,8 @@ struct BwdArgs {
   void *dq, *dk, *dv;
   float* delta;  // workspace: D [B*H*Sq] f32, then LSE*log2(e) [B*H*Sq] f32
   void* ds;      // workspace dS^T [B*H][SPk][SPq] (dtype), or null: dQ recomputes
+  float* part;   // workspace dK, dV partials [2][nqs][B*H][Sk][D] f32, or null
+  int nqs;       // query chunks of the dK+dV pass (1: no partials)
   int SPq, SPk;  // query stride and key rows per head of dS^T (rounded up to the tile)
   int BH, H, Sq, Sk, D;
   const int* kvlen;
@@ -256,6 +268,36 @@ inline Sched make_sched(int G, int BH, const std::vector<int>& works) {
   if (cache.size() >= 32) cache.erase(cache.begin());
   cache.push_back(Entry{G, BH, cux, works, s});
   return s;
+}
+
+// Tiles of the dK+dV kernel: keys per item, queries per staged tile.
+constexpr int dkdv_key_tile(bool bf16) {
+  return bf16 ? 32 * (ATTN_DKDV_NW_BF16 / ATTN_DKDV_NSPLIT_BF16)
+              : 32 * (ATTN_DKDV_NW_F32 / ATTN_DKDV_NSPLIT_F32);
+}
+constexpr int dkdv_query_tile(bool bf16) {
+  return bf16 ? 32 * ATTN_DKDV_NSPLIT_BF16 * ATTN_DKDV_KPW_BF16
+              : 32 * ATTN_DKDV_NSPLIT_F32 * ATTN_DKDV_KPW_F32;
+}
+
+// Query chunks of the dK+dV pass for a shape (a function of the shape
+// alone, so that workspace sizes and launches agree).  With fewer than
+// ATTN_DKDV_SPLIT_BELOW (key tile, head) items the chip would idle (many
+// queries over few keys: the text cross-attention); the query tiles are then
+// cut into chunks of at least ATTN_DKDV_QCHUNK_MIN tiles, towards
+// ATTN_DKDV_SPLIT_TARGET items, and the chunks' partial sums are added up
+// afterwards.
+inline int dkdv_query_chunks(bool bf16, long long BH, int Sq, int Sk) {
+  const long long nkt = (Sk + dkdv_key_tile(bf16) - 1) / dkdv_key_tile(bf16);
+  const int nqt = (Sq + dkdv_query_tile(bf16) - 1) / dkdv_query_tile(bf16);
+  const long long items = BH * nkt;
+  if (items >= ATTN_DKDV_SPLIT_BELOW) return 1;
+  long long n = (ATTN_DKDV_SPLIT_TARGET + items - 1) / items;
+  n = std::min<long long>(n, nqt / ATTN_DKDV_QCHUNK_MIN);
+  n = std::min<long long>(n, 64);
+  if (n <= 1) return 1;
+  const int qpc = (int)((nqt + n - 1) / n);
+  return (nqt + qpc - 1) / qpc;  // no empty chunk
 }
 
 hipError_t launch_fwd(const FwdArgs& a);

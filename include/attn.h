@@ -97,17 +97,23 @@ attn_status_t attn_fwd(attn_dtype_t dtype,
 
 /*
  * Workspace of the backward, in bytes (pure host functions; 0 for arguments
- * attn_bwd would reject).  The workspace holds, for every query row,
- * D_i = sum_d dO_id O_id and LSE_i * log2(e) (two [B,H,S] float32 vectors,
- * rounded up to 256 bytes: the minimum), and -- only in the full size --
- * dS transposed, [B*H][Sp][Sp] with Sp = ceil(S/128)*128, in the element
- * type, which lets dQ be computed as one GEMM dS K instead of recomputing the
- * scores.
- *   attn_bwd_workspace_size      recommended size (the dS path)
- *   attn_bwd_workspace_size_min  minimum size (dQ recomputes P and dP)
- * The backward takes the dS path iff workspace_bytes >= the recommended
- * size; the recommended size grows as S^2, so very long sequences can use
- * the minimum instead.
+ * attn_bwd would reject).  The workspace holds, in this order:
+ *   1. for every query row, D_i = sum_d dO_id O_id and LSE_i * log2(e) (two
+ *      [B,H,S] float32 vectors, rounded up to 256 bytes): the minimum;
+ *   2. dS transposed, [B*H][Sp][Sp] with Sp = ceil(S/128)*128, in the
+ *      element type, which lets dQ be computed as one GEMM dS K instead of
+ *      recomputing the scores (the dS path);
+ *   3. only for shapes with few (key tile, head) pairs -- fewer than 256,
+ *      e.g. many queries over few keys -- float32 partial sums of dK and dV
+ *      over chunks of the queries, [2][C][B*H][S][D] with C chunks chosen
+ *      from the shape alone (each chunk is then its own work item and the
+ *      chunks are added up in a fixed order, so results stay deterministic).
+ *   attn_bwd_workspace_size      recommended size: 1 + 2 + 3
+ *   attn_bwd_workspace_size_min  minimum size: 1 (dQ recomputes P and dP)
+ * The backward takes the dS path iff workspace_bytes >= the size of 1 + 2,
+ * and the query-chunk split iff the partials fit as well (after 2 on the dS
+ * path, else after 1).  The recommended size grows as S^2, so very long
+ * sequences can use the minimum instead.
  */
 size_t attn_bwd_workspace_size(attn_dtype_t dtype, int batch, int heads,
                                int seq, int head_dim, int causal);
@@ -189,8 +195,11 @@ attn_status_t attn_bwd_dq(attn_dtype_t dtype,
  * j <= i, and a one-token query sees every valid key).  A query row with no
  * visible key gets O = 0 and LSE = -inf, and contributes no gradient; dK and
  * dV rows at or past L_b are written as zeros.  The workspace sizes follow
- * from (seq_q, seq_k): D and LSE*log2(e) per query row, and for the dS path
- * dS transposed, [B*H][ceil(seq_k/128)*128][ceil(seq_q/128)*128].  Errors as
+ * from (seq_q, seq_k): D and LSE*log2(e) per query row, for the dS path
+ * dS transposed, [B*H][ceil(seq_k/128)*128][ceil(seq_q/128)*128], and for
+ * the query-chunk split the dK, dV partials [2][C][B*H][seq_k][D] float32
+ * (the 77-key text cross-attention over 4096 queries is such a shape), in
+ * the order and with the rules of attn_bwd_workspace_size.  Errors as
  * for attn_fwd / attn_bwd (seq_q, seq_k <= 0 or a misaligned kv_len:
  * ATTN_ERR_INVALID_ARG).
  */

@@ -131,6 +131,14 @@ def test_cross_validation_and_workspace():
     assert wxm(0, 2, 3, 77, 1024, 64, False) == r256(2 * 2 * 3 * 77 * 4)
     assert wx(0, 2, 3, 77, 1024, 64, False) == r256(2 * 2 * 3 * 77 * 4) + r256(6 * 1024 * 128 * 4)
     assert wx(1, 2, 3, 1, 512, 64, True) == r256(2 * 6 * 1 * 4) + r256(6 * 512 * 128 * 2)
+    # many queries over few keys: plus the dK, dV partials of the query split,
+    # [2][C][B*H][Sk][D] f32; B2 H8 Sq4096 Sk77: 32 (key tile, head) pairs,
+    # 64 query tiles of 64 -> C = 16 chunks of 4 tiles
+    assert wx(0, 2, 8, 4096, 77, 64, False) == (r256(2 * 16 * 4096 * 4) + r256(16 * 128 * 4096 * 4)
+                                                + r256(2 * 16 * 16 * 77 * 64 * 4))
+    assert wx(1, 2, 8, 4096, 77, 64, False) == (r256(2 * 16 * 4096 * 4) + r256(16 * 128 * 4096 * 2)
+                                                + r256(2 * 16 * 16 * 77 * 64 * 4))
+    assert wxm(0, 2, 8, 4096, 77, 64, False) == r256(2 * 16 * 4096 * 4)
     # equal lengths: the self-attention sizes
     assert wx(0, 8, 12, 512, 512, 64, True) == afb.attn_bwd_workspace_size(0, 8, 12, 512, 64, True)
     assert wx(0, 1, 1, 8, 0, 64, True) == 0 and wxm(0, 1, 1, 0, 8, 64, True) == 0

@@ -28,7 +28,31 @@ CASES = [
     ("decode_d32_long", 3, 4, 1, 2000, 32, True, [2000, 1, 1500]),
     ("decode_d128_ragged", 2, 3, 1, 333, 128, False, None),
     ("three_queries_d32", 2, 3, 3, 70, 32, True, None),
+    # many queries over few keys: the dK+dV pass splits the queries into
+    # chunks and adds their partial sums (with causal rows that see nothing)
+    ("long_queries_77", 1, 2, 2048, 77, 64, False, None),
+    ("long_queries_causal_split", 1, 2, 1024, 200, 64, True, [150]),
+    ("long_queries_d128_padded", 2, 1, 1536, 100, 128, False, [100, 61]),
 ]
+
+
+def _ds_bytes(B, H, Sq, Sk, dt):
+    """dS^T of the dS path: [B*H][ceil(Sk/128)*128][ceil(Sq/128)*128]."""
+    r = lambda n: (n + 127) // 128 * 128
+    b = B * H * r(Sk) * r(Sq) * (2 if dt == "bf16" else 4)
+    return (b + 255) // 256 * 256
+
+
+def _ws_bytes(mode, code, dt, B, H, Sq, Sk, D, causal):
+    """Workspace for a mode: full (recommended), min, or split (the minimum
+    and the dK, dV partials, no dS^T: the query split with dQ recomputed)."""
+    rec = afb.attn_bwd_cross_workspace_size(code, B, H, Sq, Sk, D, causal)
+    mn = afb.attn_bwd_cross_workspace_size_min(code, B, H, Sq, Sk, D, causal)
+    if mode == "full":
+        return rec
+    if mode == "min":
+        return mn
+    return mn + (rec - mn - _ds_bytes(B, H, Sq, Sk, dt))
 
 
 def _inputs(B, H, Sq, Sk, D, dt, seed=0):
@@ -41,7 +65,7 @@ def _err_lse(got, ref):
     return max_rel_err(got[fin], ref[fin]) if fin.any() else 0.0
 
 
-@pytest.mark.parametrize("ws", ["full", "min"])
+@pytest.mark.parametrize("ws", ["full", "min", "split"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("name,B,H,Sq,Sk,D,causal,kvl", CASES)
 def test_cross_parity(name, B, H, Sq, Sk, D, causal, kvl, dt, ws):
@@ -63,8 +87,7 @@ def test_cross_parity(name, B, H, Sq, Sk, D, causal, kvl, dt, ws):
     dk = torch.full((B, H, Sk, D), nan, dtype=tdt, device="cuda")
     dv = torch.full((B, H, Sk, D), nan, dtype=tdt, device="cuda")
     code = afb.ATTN_BF16 if dt == "bf16" else afb.ATTN_F32
-    wsf = afb.attn_bwd_cross_workspace_size if ws == "full" else afb.attn_bwd_cross_workspace_size_min
-    wsb = torch.full((wsf(code, B, H, Sq, Sk, D, causal) // 4,), nan, device="cuda")
+    wsb = torch.full((_ws_bytes(ws, code, dt, B, H, Sq, Sk, D, causal) // 4,), nan, device="cuda")
     scale = 1.0 / np.sqrt(D)
     afb.attn_fwd_cross(dev["q"], dev["k"], dev["v"], o, lse, kv_len, causal, scale)
     afb.attn_bwd_cross(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, dq, dk, dv, wsb, kv_len,
@@ -148,3 +171,28 @@ def test_few_query_practical_contract(Sq, Sk, D, causal, kvl):
     note("  errors " + ", ".join(f"{k}={v:.2e}" for k, v in e.items()) + f"; |O - O_strict| {diff:.2e}")
     assert e["o"] <= TOL["bf16"] and e["lse"] <= TOL["bf16"] and e["o_strict"] <= TOL["f32"]
     assert diff > TOL["f32"], diff
+
+
+def test_query_split_deterministic():
+    """The split dK+dV pass (partials added in a fixed order) gives bitwise
+    the same gradients on every run."""
+    import torch
+    B, H, Sq, Sk, D = 1, 2, 2048, 77, 64
+    note(f"[gpu case] query split determinism B{B} H{H} Sq{Sq} Sk{Sk} D{D}")
+    inp = _inputs(B, H, Sq, Sk, D, "f32", seed=2)
+    dev = {n: to_device(inp[n], None, "f32") for n in ("q", "k", "v", "do")}
+    ws = torch.empty(afb.attn_bwd_cross_workspace_size(0, B, H, Sq, Sk, D, False),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty((B, H, Sq), device="cuda")
+    afb.attn_fwd_cross(dev["q"], dev["k"], dev["v"], o, lse, None, False, 0.125)
+    runs = []
+    for _ in range(3):
+        g = [torch.empty_like(dev["q"]), torch.empty_like(dev["k"]), torch.empty_like(dev["v"])]
+        afb.attn_bwd_cross(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, *g, ws, None, False,
+                           0.125)
+        torch.cuda.synchronize()
+        runs.append([to_host(t) for t in g])
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert np.array_equal(a, b)
