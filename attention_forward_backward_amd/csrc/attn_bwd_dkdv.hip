@@ -370,23 +370,36 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
 }
 
 // dK = sum over the query chunks of the float32 partials, and dV likewise,
-// in chunk order (deterministic); four elements per thread.
+// in chunk order (deterministic); four elements per thread, 64 threads per
+// workgroup (a small tensor spread over the CUs), the loads of eight chunks
+// issued before their sums.
 template <class T>
-__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ part,
-                                                              T* __restrict__ dK,
-                                                              T* __restrict__ dV, int nqs,
-                                                              long long nel4) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(64) void bwd_dkdv_reduce_kernel(const float* __restrict__ part,
+                                                             T* __restrict__ dK,
+                                                             T* __restrict__ dV, int nqs,
+                                                             long long nel4) {
+  const long long i = (long long)blockIdx.x * 64 + threadIdx.x;
   if (i >= nel4) return;
   const f32x4* pk = reinterpret_cast<const f32x4*>(part) + i;
   const f32x4* pv = pk + (size_t)nqs * nel4;
-  f32x4 ak = pk[0], av = pv[0];
-  for (int qc = 1; qc < nqs; ++qc) {
-    const f32x4 xk = pk[(size_t)qc * nel4], xv = pv[(size_t)qc * nel4];
+  f32x4 ak = {0.f, 0.f, 0.f, 0.f}, av = {0.f, 0.f, 0.f, 0.f};
+  for (int q0 = 0; q0 < nqs; q0 += 8) {
+    f32x4 xk[8], xv[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ak[e] += xk[e];
-      av[e] += xv[e];
+    for (int u = 0; u < 8; ++u) {
+      const int qc = min(q0 + u, nqs - 1);  // (past the last chunk: loaded, not added)
+      xk[u] = pk[(size_t)qc * nel4];
+      xv[u] = pv[(size_t)qc * nel4];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (q0 + u < nqs) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ak[e] += xk[u][e];
+          av[e] += xv[u][e];
+        }
+      }
     }
   }
   store4<T>(dK + 4 * i, ak[0], ak[1], ak[2], ak[3]);
@@ -429,7 +442,7 @@ static hipError_t launch(const BwdArgs& a) {
                      QSPLIT ? a.part : nullptr, nqs, qpc, nitems, sched);
   if (QSPLIT) {
     const long long nel4 = (long long)a.BH * a.Sk * D / 4;
-    hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<T>, dim3((unsigned)((nel4 + 255) / 256)), dim3(256),
+    hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<T>, dim3((unsigned)((nel4 + 63) / 64)), dim3(64),
                        0, a.stream, a.part, (T*)a.dk, (T*)a.dv, nqs, nel4);
   }
   return hipGetLastError();

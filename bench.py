@@ -71,6 +71,9 @@ def parse():
                    help="time only the full step (used under a profiler)")
     p.add_argument("--no-cross", action="store_true",
                    help="skip the cross-attention and one-token workloads")
+    p.add_argument("--cross-only", action="store_true",
+                   help="run only the cross-attention and one-token workloads (prints their "
+                        "section alone; used under a profiler)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="instead of the benchmark, run 5 plain device-to-device copies of "
                         "BYTES bytes (the reference kernel for scaling HBM byte counters)")
@@ -139,6 +142,10 @@ def main():
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
+
+    if args.cross_only:
+        print(json.dumps({"cross": cross_section(dtypes, args, stream, log)}), flush=True)
+        return
 
     results = {}
     for dt in dtypes:
