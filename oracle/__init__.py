@@ -6,3 +6,5 @@ and the benchmark's CPU-baseline leg, never by the library.
 from .attention import (attention_backward, attention_forward,  # noqa: F401
                         attention_forward_rows, attention_probs, loss)
 from .fdcheck import fd_full, fd_grad  # noqa: F401
+from .rope import (gather_rows, rope, rope_angles_1d, rope_angles_axial,  # noqa: F401
+                   rope_transpose, scatter_rows)
