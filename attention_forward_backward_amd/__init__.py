@@ -50,6 +50,9 @@ _SIGS = {
                       _I, _I, _I, _I, _I, _F, _P]),
     "attn_bwd_dq": (_I, [_I, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _P]),
     "attn_bwd_dkdv": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_rope_copy": (_I, [_I, _P, ctypes.POINTER(ctypes.c_longlong), _P,
+                            ctypes.POINTER(ctypes.c_longlong), _P, _P, _I, _I, _I, _I, _I, _I,
+                            _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_version": (ctypes.c_char_p, []),
 }
@@ -267,3 +270,68 @@ def attn_bwd_dq(q, k, v, dout, dq, workspace, causal: bool, scale: float, stream
                              _nbytes(workspace), B, H, S, D, int(causal), float(scale),
                              _stream(stream))
     _raise("attn_bwd_dq", code)
+
+
+# ---------------------------------------------------------------- layouts, RoPE
+def strides_bhsd(heads: int, seq: int, head_dim: int) -> tuple:
+    """Element strides (batch, head, row) of a [B, H, S, D] row-major tensor."""
+    return (heads * seq * head_dim, seq * head_dim, head_dim)
+
+
+def strides_bshd(heads: int, seq: int, head_dim: int) -> tuple:
+    """Element strides (batch, head, row) of a [B, S, H, D] row-major tensor."""
+    return (seq * heads * head_dim, head_dim, heads * head_dim)
+
+
+def packed_qkv(heads: int, seq: int, head_dim: int) -> tuple:
+    """(offsets of Q, K, V, strides) inside a packed [B, S, 3, H, D] tensor."""
+    hd = heads * head_dim
+    return (0, hd, 2 * hd), (seq * 3 * hd, head_dim, 3 * hd)
+
+
+def _max_row_start(shape, offset: int, strides) -> int:
+    B, H, S, _ = shape
+    return offset + sum(st * (n - 1) for st, n in zip(strides, (B, H, S)))
+
+
+def attn_rope_copy(src, src_offset: int, src_strides, dst, dst_offset: int, dst_strides, shape,
+                   cos=None, sin=None, pos_offset: int = 0, transpose: bool = False,
+                   stream=None) -> None:
+    """Rows (b, h, s) of src -> rows of dst, each head_dim contiguous elements
+    at offset + b*strides[0] + h*strides[1] + s*strides[2] of the flat tensor;
+    rotated by the [P, head_dim/2] float32 cos/sin tables (table row
+    pos_offset + s), by their transpose with transpose=True, or copied when
+    no tables are given.  Every addressed row is checked to lie inside its
+    tensor before the call."""
+    import torch
+    B, H, S, D = (int(x) for x in shape)
+    for name, t, off, st in (("src", src, src_offset, src_strides),
+                             ("dst", dst, dst_offset, dst_strides)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if off < 0 or min(st) < 0:
+            raise ValueError(f"{name}: negative offset or stride")
+        if _max_row_start((B, H, S, D), off, st) + D > t.numel():
+            raise ValueError(f"{name}: rows reach past the end of the tensor")
+    if src.dtype != dst.dtype:
+        raise ValueError("src and dst must have the same dtype")
+    code = _dtype_code(src)
+    rows = 0
+    cp = sp = 0
+    if (cos is None) != (sin is None):
+        raise ValueError("give both tables or neither")
+    if cos is not None:
+        for name, t in (("cos", cos), ("sin", sin)):
+            if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() \
+                    or t.dim() != 2 or t.shape[1] != D // 2:
+                raise ValueError(f"{name} must be a contiguous float32 device tensor [P, {D // 2}]")
+        if cos.shape != sin.shape:
+            raise ValueError("cos and sin tables differ in shape")
+        rows, cp, sp = int(cos.shape[0]), cos.data_ptr(), sin.data_ptr()
+    LL3 = ctypes.c_longlong * 3
+    esz = src.element_size()
+    code = lib().attn_rope_copy(code, src.data_ptr() + src_offset * esz, LL3(*src_strides),
+                                dst.data_ptr() + dst_offset * esz, LL3(*dst_strides), cp, sp,
+                                rows, int(pos_offset), B, H, S, D, int(bool(transpose)),
+                                _stream(stream))
+    _raise("attn_rope_copy", code)

@@ -247,6 +247,49 @@ attn_status_t attn_bwd_cross(attn_dtype_t dtype, const void* q, const void* k, c
                   heads, seq_q, seq_k, head_dim, kv_len, causal, scale, stream);
 }
 
+attn_status_t attn_rope_copy(attn_dtype_t dtype, const void* src, const long long* src_strides,
+                             void* dst, const long long* dst_strides, const float* cos_table,
+                             const float* sin_table, int table_rows, int pos_offset, int batch,
+                             int heads, int seq, int head_dim, int transpose, void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, seq, seq, head_dim, 0, 1.f, false);
+  if (st != ATTN_OK) return st;
+  if ((st = check_ptrs({src, dst})) != ATTN_OK) return st;
+  if (src_strides == nullptr || dst_strides == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (transpose != 0 && transpose != 1) return ATTN_ERR_INVALID_ARG;
+  if ((cos_table == nullptr) != (sin_table == nullptr)) return ATTN_ERR_INVALID_ARG;
+  if (cos_table != nullptr) {
+    if (!aligned16(cos_table) || !aligned16(sin_table)) return ATTN_ERR_INVALID_ARG;
+    if (pos_offset < 0 || table_rows < 0 || (int64_t)pos_offset + seq > table_rows)
+      return ATTN_ERR_INVALID_ARG;
+  }
+  // strides in elements: non-negative multiples of 8 (16-byte accesses),
+  // and the farthest element within int64
+  const int dims[3] = {batch, heads, seq};
+  for (const long long* str : {src_strides, dst_strides}) {
+    double far = head_dim;
+    for (int i = 0; i < 3; ++i) {
+      if (str[i] < 0 || str[i] % 8 != 0 || str[i] > (1LL << 48)) return ATTN_ERR_INVALID_ARG;
+      far += (double)str[i] * (dims[i] - 1);
+    }
+    if (far > 4.0e18) return ATTN_ERR_INVALID_ARG;
+  }
+  attn::RopeArgs a;
+  a.bf16 = dtype == ATTN_BF16;
+  a.src = src;
+  a.dst = dst;
+  for (int i = 0; i < 3; ++i) {
+    a.ss[i] = src_strides[i];
+    a.ds[i] = dst_strides[i];
+  }
+  a.cos = cos_table;
+  a.sin = sin_table;
+  a.pos_offset = cos_table != nullptr ? pos_offset : 0;
+  a.B = batch; a.H = heads; a.S = seq; a.D = head_dim;
+  a.transpose = transpose != 0;
+  a.stream = static_cast<hipStream_t>(stream);
+  return from_hip(attn::launch_rope(a));
+}
+
 const char* attn_status_string(attn_status_t s) {
   switch (s) {
     case ATTN_OK: return "ok";
@@ -258,6 +301,6 @@ const char* attn_status_string(attn_status_t s) {
   return "unknown status";
 }
 
-const char* attn_version(void) { return "0.3.0"; }
+const char* attn_version(void) { return "0.4.0"; }
 
 }  // extern "C"

@@ -168,6 +168,23 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+// Rotary embedding / layout pass: dst rows = R(src rows) (or R^T, or a plain
+// copy without tables); element (b, h, s, d) of a tensor at
+// b*strides[0] + h*strides[1] + s*strides[2] + d.
+struct RopeArgs {
+  bool bf16;
+  const void* src;
+  long long ss[3];
+  void* dst;
+  long long ds[3];
+  const float* cos;  // [rows][D/2] f32, or null: no rotation
+  const float* sin;
+  int pos_offset;    // table row of sequence position 0
+  int B, H, S, D;
+  bool transpose;
+  hipStream_t stream;
+};
+
 // Workgroups of kernel Kern (launched with `threads` threads and no dynamic
 // LDS) that the current device holds at once: CUs x resident workgroups per
 // CU.  Persistent kernels launch this many (or fewer) workgroups.  Queried
@@ -301,6 +318,7 @@ inline int dkdv_query_chunks(bool bf16, long long BH, int Sq, int Sk) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_rope(const RopeArgs& a);
 hipError_t launch_fwd_small(const FwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);

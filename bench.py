@@ -71,6 +71,8 @@ def parse():
                    help="time only the full step (used under a profiler)")
     p.add_argument("--no-cross", action="store_true",
                    help="skip the cross-attention and one-token workloads")
+    p.add_argument("--no-rope", action="store_true",
+                   help="skip the packed-QKV + RoPE layout pass measurement")
     p.add_argument("--cross-only", action="store_true",
                    help="run only the cross-attention and one-token workloads (prints their "
                         "section alone; used under a profiler)")
@@ -276,6 +278,8 @@ def main():
 
     if not args.no_cross and not args.only_step:
         line["cross"] = cross_section(dtypes, args, stream, log)
+    if not args.no_rope and not args.only_step:
+        line["rope_packed"] = rope_section(cfg, dtypes, args, stream, log)
 
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the float64 oracle on the host")
@@ -399,6 +403,98 @@ def cross_section(dtypes, args, stream, log) -> dict:
                        "fwd_frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}
             del q, k, v, do, o, dq, dk, dv, lse, ws
         out[wname] = rec
+    torch.cuda.empty_cache()
+    return out
+
+
+def graph_time(fn, per_graph=20, replays=30) -> float:
+    """ms per call of fn from replays of a HIP graph of per_graph calls."""
+    import torch
+    for _ in range(per_graph):
+        fn()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(per_graph):
+            fn()
+    for _ in range(3):
+        gr.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del gr
+    return e0.elapsed_time(e1) / (replays * per_graph)
+
+
+def rope_section(cfg, dtypes, args, stream, log) -> dict:
+    """The workload's step on a packed [B, S, 3, H, D] projection with 1-D
+    RoPE on Q and K: attn_rope_copy brings Q, K (rotated) and V into
+    [B, H, S, D] and dO from [B, S, H, D], and takes O to [B, S, H, D] and
+    dQ, dK (transposed rotation) and dV back into the packed gradient.  Each
+    pass reads and writes one [B, H, S, D] tensor (plus table rows): HBM-bound,
+    timed from HIP graph replays."""
+    import torch
+    import attention_forward_backward_amd as afb
+    from attention_forward_backward_amd import synth
+    B, H, S, D = cfg.shape
+    shp = (B, H, S, D)
+    # 1-D rotary angles p * 10000^(-2i/D) (the input tables of the pass)
+    ang = np.arange(S)[:, None] * 10000.0 ** (-2.0 * np.arange(D // 2) / D)
+    ct = torch.from_numpy(np.cos(ang).astype(np.float32)).cuda()
+    st = torch.from_numpy(np.sin(ang).astype(np.float32)).cuda()
+    offs, pst = afb.packed_qkv(H, S, D)
+    bhsd, bshd = afb.strides_bhsd(H, S, D), afb.strides_bshd(H, S, D)
+    out = {"layout": "packed [B,S,3,H,D] QKV, dO and O in [B,S,H,D]", "rope": "1-D, base 10000"}
+    for dt in dtypes:
+        if dt == "f32_bf16fwd":
+            continue
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        pk = torch.from_numpy(synth.normal_f32(args.seed, 0, (B, S, 3, H, D))).cuda().to(tdt)
+        dOt = torch.from_numpy(synth.normal_f32(args.seed, 3, (B, S, H, D))).cuda().to(tdt)
+        q, k, v, o, do, dq, dk, dv = (torch.empty(shp, dtype=tdt, device="cuda") for _ in range(8))
+        o_s = torch.empty((B, S, H, D), dtype=tdt, device="cuda")
+        dpk = torch.empty_like(pk)
+        lse = torch.empty((B, H, S), device="cuda")
+        code = afb.ATTN_BF16 if dt == "bf16" else afb.ATTN_F32
+        ws = torch.empty(afb.attn_bwd_workspace_size(code, B, H, S, D, cfg.causal),
+                         dtype=torch.uint8, device="cuda")
+
+        def prologue():
+            afb.attn_rope_copy(pk, offs[0], pst, q, 0, bhsd, shp, ct, st)
+            afb.attn_rope_copy(pk, offs[1], pst, k, 0, bhsd, shp, ct, st)
+            afb.attn_rope_copy(pk, offs[2], pst, v, 0, bhsd, shp)
+
+        def epilogue():
+            afb.attn_rope_copy(o, 0, bhsd, o_s, 0, bshd, shp)
+            afb.attn_rope_copy(dOt, 0, bshd, do, 0, bhsd, shp)
+            afb.attn_rope_copy(dq, 0, bhsd, dpk, offs[0], pst, shp, ct, st, transpose=True)
+            afb.attn_rope_copy(dk, 0, bhsd, dpk, offs[1], pst, shp, ct, st, transpose=True)
+            afb.attn_rope_copy(dv, 0, bhsd, dpk, offs[2], pst, shp)
+
+        def step():
+            prologue()
+            afb.attn_fwd(q, k, v, o, lse, cfg.causal, cfg.scale)
+            epilogue()
+            afb.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, cfg.causal, cfg.scale)
+
+        log(f"[bench] packed QKV + RoPE {shp} dtype={dt}")
+        esz = 2 if dt == "bf16" else 4
+        tb = B * H * S * D * esz
+        rot = lambda: afb.attn_rope_copy(pk, offs[0], pst, q, 0, bhsd, shp, ct, st)
+        ms_rot = graph_time(rot)
+        bytes_rot = 2 * tb + 2 * S * (D // 2) * 4
+        ms_pro, ms_epi, ms_step = graph_time(prologue), graph_time(epilogue), graph_time(step)
+        gbs = bytes_rot / (ms_rot * 1e-3) / 1e9
+        out[dt] = {"rotate_us": round(ms_rot * 1e3, 2), "rotate_bytes": bytes_rot,
+                   "rotate_gbs": round(gbs, 1), "rotate_frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                   "prologue_us": round(ms_pro * 1e3, 2), "epilogue_us": round(ms_epi * 1e3, 2),
+                   "step_us": round(ms_step * 1e3, 2)}
+        del pk, dOt, q, k, v, o, do, dq, dk, dv, o_s, dpk, lse, ws
     torch.cuda.empty_cache()
     return out
 

@@ -220,6 +220,39 @@ attn_status_t attn_bwd_cross(attn_dtype_t dtype,
                              int batch, int heads, int seq_q, int seq_k, int head_dim,
                              const int* kv_len, int causal, float scale, void* stream);
 
+/*
+ * Rotary position embedding and row-layout change, one memory-bound pass
+ * (the pages' axial RoPE in front of attention, Section 5.2, and their
+ * packed projection forms, Section 3.2).  For every (b, h, s) < (batch,
+ * heads, seq) it reads row s of head h of batch b of src and writes row
+ * (b, h, s) of dst, each row head_dim contiguous elements at
+ *   b*strides[0] + h*strides[1] + s*strides[2]      (elements, not bytes).
+ * [B,H,S,D] row-major is strides {H*S*D, S*D, D}; [B,S,H,D] is
+ * {S*H*D, D, H*D}; a packed [B,S,3,H,D] projection holds Q, K, V at element
+ * offsets 0, H*D, 2*H*D (src = base + offset) with strides {S*3*H*D, D, 3*H*D}.
+ *   cos_table, sin_table  NULL (a plain copy) or DEVICE float32 tables
+ *                          [table_rows][head_dim/2]; row s uses table row
+ *                          pos_offset + s, which must be < table_rows
+ *   transpose = 0: y_i = x_i c - x_{i+D/2} s, y_{i+D/2} = x_{i+D/2} c + x_i s
+ *               (pair (i, i + D/2) turned by the angle of cosine c, sine s:
+ *               the rotate-half RoPE; 1-D and axial positions differ only
+ *               in the tables);
+ *   transpose = 1: the transposed rotation (angle negated), which maps the
+ *               gradient with respect to the rotated rows back to the rows.
+ * dtype: ATTN_F32 and ATTN_F32_BF16FWD (float32 tensors, arithmetic in
+ * float32) or ATTN_BF16 (bf16 tensors, rotation in float32, one rounding to
+ * bf16 per output).  src and dst are 16-byte aligned device pointers; strides
+ * are non-negative multiples of 8 elements.  The rows written must not
+ * overlap each other; dst may equal src with the same strides (in place).
+ * Errors: ATTN_ERR_INVALID_ARG (null or misaligned pointers, bad strides,
+ * only one table, a table too short, transpose not 0/1, sizes <= 0),
+ * ATTN_ERR_UNSUPPORTED (dtype, head_dim), ATTN_ERR_HIP (launch failure).
+ */
+attn_status_t attn_rope_copy(attn_dtype_t dtype, const void* src, const long long* src_strides,
+                             void* dst, const long long* dst_strides, const float* cos_table,
+                             const float* sin_table, int table_rows, int pos_offset, int batch,
+                             int heads, int seq, int head_dim, int transpose, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status_t status);
 

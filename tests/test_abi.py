@@ -19,10 +19,10 @@ def test_library_loads_and_exports_header_symbols():
                              "attn_bwd_dkdv", "attn_bwd_workspace_size",
                              "attn_bwd_workspace_size_min", "attn_fwd_cross", "attn_bwd_cross",
                              "attn_bwd_cross_workspace_size", "attn_bwd_cross_workspace_size_min",
-                             "attn_status_string", "attn_version"}
+                             "attn_rope_copy", "attn_status_string", "attn_version"}
     for name in declared:
         assert hasattr(L, name), name
-    assert afb.attn_version() == "0.3.0"
+    assert afb.attn_version() == "0.4.0"
     for code in range(5):
         assert afb.attn_status_string(code) not in ("", "unknown status")
     assert afb.attn_status_string(99) == "unknown status"
@@ -142,3 +142,26 @@ def test_cross_validation_and_workspace():
     # equal lengths: the self-attention sizes
     assert wx(0, 8, 12, 512, 512, 64, True) == afb.attn_bwd_workspace_size(0, 8, 12, 512, 64, True)
     assert wx(0, 1, 1, 8, 0, 64, True) == 0 and wxm(0, 1, 1, 0, 8, 64, True) == 0
+
+
+def _rope(dtype=0, src=FAKE, ss=(64 * 8, 64 * 8, 64), dst=FAKE, ds=(64 * 8, 64 * 8, 64),
+          cos=FAKE, sin=FAKE, rows=8, pos=0, B=1, H=1, S=8, D=64, tr=0):
+    LL3 = ctypes.c_longlong * 3
+    return afb.lib().attn_rope_copy(dtype, src, None if ss is None else LL3(*ss), dst,
+                                    None if ds is None else LL3(*ds), cos, sin, rows, pos, B, H,
+                                    S, D, tr, None)
+
+
+def test_rope_copy_validation():
+    assert _rope(src=None) == 1 and _rope(dst=MIS) == 1
+    assert _rope(ss=None) == 1 and _rope(ds=None) == 1
+    assert _rope(ss=(512, 512, 60)) == 1                 # stride not a multiple of 8
+    assert _rope(ds=(-512, 512, 64)) == 1                # negative stride
+    assert _rope(ss=(1 << 50, 8, 8)) == 1                # beyond the index range
+    assert _rope(cos=None) == 1 and _rope(sin=None) == 1  # one table only
+    assert _rope(cos=MIS) == 1
+    assert _rope(rows=7) == 1 and _rope(pos=1) == 1      # table too short for the rows used
+    assert _rope(pos=-1, rows=100) == 1
+    assert _rope(tr=2) == 1
+    assert _rope(B=0) == 1 and _rope(S=0) == 1
+    assert _rope(D=48) == 2 and _rope(dtype=5) == 2
