@@ -73,6 +73,11 @@ def parse():
                    help="skip the cross-attention and one-token workloads")
     p.add_argument("--no-rope", action="store_true",
                    help="skip the packed-QKV + RoPE layout pass measurement")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time the cross and RoPE sections from eager calls only, no HIP graphs "
+                        "(for counter runs under a profiler)")
+    p.add_argument("--rope-only", action="store_true",
+                   help="run only the packed-QKV + RoPE measurement (used under a profiler)")
     p.add_argument("--cross-only", action="store_true",
                    help="run only the cross-attention and one-token workloads (prints their "
                         "section alone; used under a profiler)")
@@ -147,6 +152,9 @@ def main():
 
     if args.cross_only:
         print(json.dumps({"cross": cross_section(dtypes, args, stream, log)}), flush=True)
+        return
+    if args.rope_only:
+        print(json.dumps({"rope_packed": rope_section(cfg, dtypes, args, stream, log)}), flush=True)
         return
 
     results = {}
@@ -386,8 +394,8 @@ def cross_section(dtypes, args, stream, log) -> dict:
             log(f"[bench] cross {wname} {rec['shape']} dtype={dt}")
             ms_fe = timed(fwd, args.steps, args.warmup)
             ms_se = timed(step, args.steps, args.warmup)
-            ms_f = timed_graph(fwd)
-            ms_s = timed_graph(step)
+            ms_f = ms_fe if args.no_graph else timed_graph(fwd)
+            ms_s = ms_se if args.no_graph else timed_graph(step)
             # forward's algorithmic HBM bytes: Q and O, the valid K and V
             # rows, the LSE
             esz = 2 if dt == "bf16" else 4
@@ -405,6 +413,22 @@ def cross_section(dtypes, args, stream, log) -> dict:
         out[wname] = rec
     torch.cuda.empty_cache()
     return out
+
+
+def eager_time(fn, steps: int) -> float:
+    """ms per call of fn over `steps` eager calls after as many warm-up calls."""
+    import torch
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def graph_time(fn, per_graph=20, replays=30) -> float:
@@ -486,9 +510,10 @@ def rope_section(cfg, dtypes, args, stream, log) -> dict:
         esz = 2 if dt == "bf16" else 4
         tb = B * H * S * D * esz
         rot = lambda: afb.attn_rope_copy(pk, offs[0], pst, q, 0, bhsd, shp, ct, st)
-        ms_rot = graph_time(rot)
+        tf = (lambda fn: eager_time(fn, args.steps)) if args.no_graph else graph_time
+        ms_rot = tf(rot)
         bytes_rot = 2 * tb + 2 * S * (D // 2) * 4
-        ms_pro, ms_epi, ms_step = graph_time(prologue), graph_time(epilogue), graph_time(step)
+        ms_pro, ms_epi, ms_step = tf(prologue), tf(epilogue), tf(step)
         gbs = bytes_rot / (ms_rot * 1e-3) / 1e9
         out[dt] = {"rotate_us": round(ms_rot * 1e3, 2), "rotate_bytes": bytes_rot,
                    "rotate_gbs": round(gbs, 1), "rotate_frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
