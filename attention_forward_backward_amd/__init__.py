@@ -50,6 +50,10 @@ _SIGS = {
                       _I, _I, _I, _I, _I, _F, _P]),
     "attn_bwd_dq": (_I, [_I, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _P]),
     "attn_bwd_dkdv": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_fwd_strided": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P,
+                              ctypes.POINTER(ctypes.c_longlong), _I, _F, _P]),
+    "attn_bwd_strided": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I,
+                              _I, _P, ctypes.POINTER(ctypes.c_longlong), _I, _F, _P]),
     "attn_rope_copy": (_I, [_I, _P, ctypes.POINTER(ctypes.c_longlong), _P,
                             ctypes.POINTER(ctypes.c_longlong), _P, _P, _I, _I, _I, _I, _I, _I,
                             _I, _P]),
@@ -223,6 +227,69 @@ def attn_bwd_cross(q, k, v, o, dout, lse, dq, dk, dv, workspace, kv_len, causal:
                                 _nbytes(workspace), B, H, Sq, Sk, D, _kv_len_ptr(kv_len, B),
                                 int(causal), float(scale), _stream(stream))
     _raise("attn_bwd_cross", code)
+
+
+def _view_strides(tensors: dict, shape, dtype) -> list:
+    """(batch, head, row) element strides of [B,H,S,D] views whose last
+    dimension is contiguous (any view torch can make lies inside its
+    storage, so the strides address only the tensor's own memory)."""
+    out = []
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous")
+        out.extend(int(x) for x in t.stride()[:3])
+    return out
+
+
+def attn_fwd_strided(q, k, v, o, lse, kv_len, causal: bool, scale: float, stream=None,
+                     bf16_operands: bool = False) -> None:
+    """attn_fwd_cross on [B,H,S,D] views of any layout with a contiguous head
+    dimension (e.g. slices of a packed [B,S,3,H,D] projection, permuted
+    [B,S,H,D] tensors); lse [B,H,Sq] contiguous float32 or None."""
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    st = _view_strides({"q": q}, (B, H, Sq, D), q.dtype) + \
+        _view_strides({"k": k, "v": v}, (B, H, Sk, D), q.dtype) + \
+        _view_strides({"o": o}, (B, H, Sq, D), q.dtype)
+    if lse is not None:
+        _check_f32({"lse": lse}, (B, H, Sq))
+    code = _dtype_code(q)
+    if bf16_operands:
+        if code != ATTN_F32:
+            raise TypeError("bf16_operands applies to float32 tensors")
+        code = ATTN_F32_BF16FWD
+    code = lib().attn_fwd_strided(code, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  0 if lse is None else lse.data_ptr(), B, H, Sq, Sk, D,
+                                  _kv_len_ptr(kv_len, B), (ctypes.c_longlong * 12)(*st),
+                                  int(causal), float(scale), _stream(stream))
+    _raise("attn_fwd_strided", code)
+
+
+def attn_bwd_strided(q, k, v, o, dout, lse, dq, dk, dv, workspace, kv_len, causal: bool,
+                     scale: float, stream=None) -> None:
+    """attn_bwd_cross on [B,H,S,D] views (as attn_fwd_strided); the
+    workspace is contiguous, sized by attn_bwd_cross_workspace_size."""
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    qs, ks = (B, H, Sq, D), (B, H, Sk, D)
+    st = []
+    for name, t, shp in (("q", q, qs), ("k", k, ks), ("v", v, ks), ("o", o, qs),
+                         ("dout", dout, qs), ("dq", dq, qs), ("dk", dk, ks), ("dv", dv, ks)):
+        st += _view_strides({name: t}, shp, q.dtype)
+    _check_f32({"lse": lse}, (B, H, Sq))
+    code = lib().attn_bwd_strided(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                                  dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                                  _nbytes(workspace), B, H, Sq, Sk, D, _kv_len_ptr(kv_len, B),
+                                  (ctypes.c_longlong * 24)(*st), int(causal), float(scale),
+                                  _stream(stream))
+    _raise("attn_bwd_strided", code)
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,

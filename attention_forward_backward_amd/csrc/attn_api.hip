@@ -5,6 +5,8 @@
 // allocated and no pointer is retained between calls (the launchers cache
 // only occupancy figures and schedule patterns, on the host).
 #include <math.h>
+
+#include <utility>
 #include <stdint.h>
 
 #include "../../include/attn.h"
@@ -79,7 +81,8 @@ attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_E
 attn::BwdArgs make_bwd(attn_dtype_t dtype, const void* q, const void* k, const void* v,
                        const void* o, const void* dout, const float* lse, void* dq, void* dk,
                        void* dv, void* ws, size_t ws_bytes, int batch, int heads, int sq, int sk,
-                       int head_dim, const int* kvlen, int causal, float scale, void* stream) {
+                       int head_dim, const int* kvlen, int causal, float scale, void* stream,
+                       const attn::Layout* layout = nullptr) {
   attn::BwdArgs a;
   a.bf16 = dtype == ATTN_BF16;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
@@ -98,17 +101,54 @@ attn::BwdArgs make_bwd(attn_dtype_t dtype, const void* q, const void* k, const v
   a.SPq = ds_stride(sq); a.SPk = ds_stride(sk);
   a.BH = batch * heads; a.H = heads; a.Sq = sq; a.Sk = sk; a.D = head_dim;
   a.kvlen = kvlen;
-  a.cross = sq != sk || kvlen != nullptr;
+  a.cross = sq != sk || kvlen != nullptr || layout != nullptr;
   a.causal = causal != 0; a.scale = scale;
   a.stream = static_cast<hipStream_t>(stream);
+  a.layout = layout;
   return a;
 }
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// Strides (batch, head, row) of one tensor of extents (B, H, S) x D:
+// non-negative multiples of 8 elements (16-byte rows), below 2^31 (the
+// kernels hold them in 32 bits), a row stride of at most 2^24 (their 32-bit
+// lane offsets), and the farthest element within int64.
+// Outputs must also not overlap themselves: sorted by stride, each stride is
+// at least the span of the dimensions below it (the D elements of a row
+// first).
+bool check_strides(const long long* st, int B, int H, int S, int D, bool output) {
+  const int ext[3] = {B, H, S};
+  double far = D;
+  for (int i = 0; i < 3; ++i) {
+    if (st[i] < 0 || st[i] % 8 != 0) return false;
+    far += (double)st[i] * (ext[i] - 1);
+  }
+  if (st[0] > 0x7fffffffLL || st[1] > 0x7fffffffLL || st[2] > (1LL << 24) || far > 4.0e18)
+    return false;
+  if (!output) return true;
+  int ord[3] = {0, 1, 2};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (st[ord[j]] < st[ord[i]]) std::swap(ord[i], ord[j]);
+  long long span = D;
+  for (int i = 0; i < 3; ++i) {
+    const int d = ord[i];
+    if (ext[d] == 1) continue;
+    if (st[d] < span) return false;
+    span = st[d] * ext[d];
+  }
+  return true;
+}
+
+attn::Str3 str3(const long long* st) {
+  return attn::Str3{(int)st[0], (int)st[1], (int)st[2]};
+}
+
 attn_status_t fwd_impl(attn_dtype_t dtype, const void* q, const void* k, const void* v, void* o,
                        float* lse, int batch, int heads, int sq, int sk, int head_dim,
-                       const int* kvlen, int causal, float scale, void* stream) {
+                       const int* kvlen, int causal, float scale, void* stream,
+                       const attn::Layout* layout = nullptr) {
   attn_status_t st = check_shape(dtype, batch, heads, sq, sk, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
   if ((st = check_ptrs({q, k, v, o})) != ATTN_OK) return st;
@@ -120,9 +160,10 @@ attn_status_t fwd_impl(attn_dtype_t dtype, const void* q, const void* k, const v
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.BH = batch * heads; a.H = heads; a.Sq = sq; a.Sk = sk; a.D = head_dim;
   a.kvlen = kvlen;
-  a.cross = sq != sk || kvlen != nullptr;
+  a.cross = sq != sk || kvlen != nullptr || layout != nullptr;
   a.causal = causal != 0; a.scale = scale;
   a.stream = static_cast<hipStream_t>(stream);
+  a.layout = layout;
   return from_hip(attn::launch_fwd(a));
 }
 
@@ -130,7 +171,7 @@ attn_status_t bwd_impl(attn_dtype_t dtype, const void* q, const void* k, const v
                        const void* o, const void* dout, const float* lse, void* dq, void* dk,
                        void* dv, void* workspace, size_t workspace_bytes, int batch, int heads,
                        int sq, int sk, int head_dim, const int* kvlen, int causal, float scale,
-                       void* stream) {
+                       void* stream, const attn::Layout* layout = nullptr) {
   attn_status_t st = check_shape(dtype, batch, heads, sq, sk, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
   if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace})) != ATTN_OK) return st;
@@ -138,7 +179,7 @@ attn_status_t bwd_impl(attn_dtype_t dtype, const void* q, const void* k, const v
   if (workspace_bytes < ws_min_bytes(batch, heads, sq)) return ATTN_ERR_WORKSPACE;
   const attn::BwdArgs a = make_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace,
                                    workspace_bytes, batch, heads, sq, sk, head_dim, kvlen, causal,
-                                   scale, stream);
+                                   scale, stream, layout);
   if ((st = from_hip(attn::launch_bwd_prep(a))) != ATTN_OK) return st;
   if ((st = from_hip(attn::launch_bwd_dkdv(a))) != ATTN_OK) return st;
   return from_hip(attn::launch_bwd_dq(a));
@@ -247,6 +288,53 @@ attn_status_t attn_bwd_cross(attn_dtype_t dtype, const void* q, const void* k, c
                   heads, seq_q, seq_k, head_dim, kv_len, causal, scale, stream);
 }
 
+attn_status_t attn_fwd_strided(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                               void* o, float* lse, int batch, int heads, int seq_q, int seq_k,
+                               int head_dim, const int* kv_len, const long long* strides,
+                               int causal, float scale, void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, seq_q, seq_k, head_dim, causal, scale, true);
+  if (st != ATTN_OK) return st;
+  if (strides == nullptr) return ATTN_ERR_INVALID_ARG;
+  const int rows[4] = {seq_q, seq_k, seq_k, seq_q};
+  for (int t = 0; t < 4; ++t)
+    if (!check_strides(strides + 3 * t, batch, heads, rows[t], head_dim, t == 3))
+      return ATTN_ERR_INVALID_ARG;
+  attn::Layout lay{};
+  lay.q = str3(strides);
+  lay.k = str3(strides + 3);
+  lay.v = str3(strides + 6);
+  lay.o = str3(strides + 9);
+  return fwd_impl(dtype, q, k, v, o, lse, batch, heads, seq_q, seq_k, head_dim, kv_len, causal,
+                  scale, stream, &lay);
+}
+
+attn_status_t attn_bwd_strided(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                               const void* o, const void* dout, const float* lse, void* dq,
+                               void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                               int batch, int heads, int seq_q, int seq_k, int head_dim,
+                               const int* kv_len, const long long* strides, int causal,
+                               float scale, void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, seq_q, seq_k, head_dim, causal, scale, true);
+  if (st != ATTN_OK) return st;
+  if (strides == nullptr) return ATTN_ERR_INVALID_ARG;
+  // q, k, v, o, dout, dq, dk, dv
+  const int rows[8] = {seq_q, seq_k, seq_k, seq_q, seq_q, seq_q, seq_k, seq_k};
+  for (int t = 0; t < 8; ++t)
+    if (!check_strides(strides + 3 * t, batch, heads, rows[t], head_dim, t >= 5))
+      return ATTN_ERR_INVALID_ARG;
+  attn::Layout lay{};
+  lay.q = str3(strides);
+  lay.k = str3(strides + 3);
+  lay.v = str3(strides + 6);
+  lay.o = str3(strides + 9);
+  lay.dout = str3(strides + 12);
+  lay.dq = str3(strides + 15);
+  lay.dk = str3(strides + 18);
+  lay.dv = str3(strides + 21);
+  return bwd_impl(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, batch,
+                  heads, seq_q, seq_k, head_dim, kv_len, causal, scale, stream, &lay);
+}
+
 attn_status_t attn_rope_copy(attn_dtype_t dtype, const void* src, const long long* src_strides,
                              void* dst, const long long* dst_strides, const float* cos_table,
                              const float* sin_table, int table_rows, int pos_offset, int batch,
@@ -301,6 +389,6 @@ const char* attn_status_string(attn_status_t s) {
   return "unknown status";
 }
 
-const char* attn_version(void) { return "0.4.0"; }
+const char* attn_version(void) { return "0.5.0"; }
 
 }  // extern "C"

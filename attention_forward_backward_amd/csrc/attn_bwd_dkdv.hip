@@ -35,14 +35,14 @@
 namespace attn {
 
 template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS, bool CROSS,
-          bool QSPLIT>
+          bool QSPLIT, bool STR>
 __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_F32 : 1) void bwd_dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
     typename E::T* __restrict__ dSout, int SPq, int SPk, int Sq, int Sk_, int Lws, float c,
     float scale, int BH, int H, const int* __restrict__ kvlen, float* __restrict__ part, int nqs_,
-    int qpc_, int nitems, const Sched sched) {
+    int qpc_, int nitems, const Sched sched, const Layout lay) {
   // Queries Sq, keys Sk (one length in self-attention, CROSS = false); per
   // batch*head the first L keys exist and key j is visible from query i iff
   // j < L and, when causal, j <= i + off (head_keys).  Lws: offset of the
@@ -52,6 +52,8 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   // its dK (scaled) and dV sums as float32 partials, part[qc][bh][Sk][D]
   // then part[nqs + qc][bh][Sk][D], which a second kernel adds up.  Without
   // QSPLIT there is one chunk of every query tile and dK, dV are stored.
+  // STR: Q, K, V, dO, dK, dV are laid out by `lay` (else [B, H, S, D]
+  // row-major; the workspace is always packed).
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-key blocks per item
@@ -86,7 +88,9 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   const int nqt = (Sq + BQ - 1) / BQ;
   const int nqs = QSPLIT ? nqs_ : 1;
   const int qpc = QSPLIT ? qpc_ : nqt;
-  const unsigned lane_off = LD::lane_offset(w, lane);
+  const unsigned lane_off = STR ? 0u : LD::lane_offset(w, lane);
+  const int ldq = row_ld<STR, D>(lay.q), ldk = row_ld<STR, D>(lay.k);
+  const int ldv = row_ld<STR, D>(lay.v), lddo = row_ld<STR, D>(lay.dout);
   // First query tile with a query that sees a key of key tile kt (nqt: none).
   auto first_qt = [&](int kt, int L, int off) {
     if constexpr (!CROSS) {
@@ -123,9 +127,23 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     if (head) {
       // K and V rows; past the valid keys the loads read the last valid row
       // (finite, and masked), so padded rows are never read.
-      LD::issue(st, K + lhk * D, V + lhk * D, lkt * BKV, CROSS ? max(lL, 1) : Sk, w, lane, lane_off);
+      if constexpr (STR) {
+        const int bhl = lit % BH;
+        LD::issue_ld(st, K + head_off<STR, D>(lay.k, bhl, H, Sk), ldk,
+                     V + head_off<STR, D>(lay.v, bhl, H, Sk), ldv, lkt * BKV,
+                     CROSS ? max(lL, 1) : Sk, w, lane);
+      } else {
+        LD::issue(st, K + lhk * D, V + lhk * D, lkt * BKV, CROSS ? max(lL, 1) : Sk, w, lane,
+                  lane_off);
+      }
     } else {
-      LD::issue(st, Q + lhq * D, dO + lhq * D, lqt * BQ, Sq, w, lane, lane_off);
+      if constexpr (STR) {
+        const int bhl = lit % BH;
+        LD::issue_ld(st, Q + head_off<STR, D>(lay.q, bhl, H, Sq), ldq,
+                     dO + head_off<STR, D>(lay.dout, bhl, H, Sq), lddo, lqt * BQ, Sq, w, lane);
+      } else {
+        LD::issue(st, Q + lhq * D, dO + lhq * D, lqt * BQ, Sq, w, lane, lane_off);
+      }
     }
     issue_stats<BQ, NW>(stats0 + (nissued % NST) * (2 * BQ), Dws + Lws + lhq, Dws + lhq,
                         head ? 0 : lqt * BQ, Sq, w, lane);
@@ -193,16 +211,17 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     if (sp == 0 && active) {
       // element r of acc[db]: row k0 + out_row(r, h), column db*32 + n
       if constexpr (!QSPLIT) {
-        T* dk = dK + (size_t)bh * Sk * D;
-        T* dv = dV + (size_t)bh * Sk * D;
+        T* dk = dK + head_off<STR, D>(lay.dk, bh, H, Sk);
+        T* dv = dV + head_off<STR, D>(lay.dv, bh, H, Sk);
+        const int lddk = row_ld<STR, D>(lay.dk), lddv = row_ld<STR, D>(lay.dv);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = k0 + out_row(r, h);
           if (row < Sk) {
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-              dk[(size_t)row * D + db * 32 + n] = (T)(dkacc[db][r] * scale);
-              dv[(size_t)row * D + db * 32 + n] = (T)dvacc[db][r];
+              dk[(size_t)row * lddk + db * 32 + n] = (T)(dkacc[db][r] * scale);
+              dv[(size_t)row * lddv + db * 32 + n] = (T)dvacc[db][r];
             }
           }
         }
@@ -373,11 +392,13 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
 // in chunk order (deterministic); four elements per thread, 64 threads per
 // workgroup (a small tensor spread over the CUs), the loads of eight chunks
 // issued before their sums.
-template <class T>
+template <class T, int D, bool STR>
 __global__ __launch_bounds__(64) void bwd_dkdv_reduce_kernel(const float* __restrict__ part,
                                                              T* __restrict__ dK,
                                                              T* __restrict__ dV, int nqs,
-                                                             long long nel4) {
+                                                             long long nel4, int Sk, int H,
+                                                             const Layout lay) {
+  // (partials are [B*H][Sk][D] packed; STR: dK, dV are laid out by `lay`)
   const long long i = (long long)blockIdx.x * 64 + threadIdx.x;
   if (i >= nel4) return;
   const f32x4* pk = reinterpret_cast<const f32x4*>(part) + i;
@@ -402,18 +423,31 @@ __global__ __launch_bounds__(64) void bwd_dkdv_reduce_kernel(const float* __rest
       }
     }
   }
-  store4<T>(dK + 4 * i, ak[0], ak[1], ak[2], ak[3]);
-  store4<T>(dV + 4 * i, av[0], av[1], av[2], av[3]);
+  if constexpr (STR) {
+    const long long e = 4 * i;
+    const int bh = (int)(e / ((long long)Sk * D));
+    const int rem = (int)(e - (long long)bh * Sk * D);
+    const int row = rem / D, d = rem % D;
+    store4<T>(dK + head_off<STR, D>(lay.dk, bh, H, Sk) + (size_t)row * lay.dk.s + d, ak[0], ak[1],
+              ak[2], ak[3]);
+    store4<T>(dV + head_off<STR, D>(lay.dv, bh, H, Sk) + (size_t)row * lay.dv.s + d, av[0], av[1],
+              av[2], av[3]);
+  } else {
+    store4<T>(dK + 4 * i, ak[0], ak[1], ak[2], ak[3]);
+    store4<T>(dV + 4 * i, av[0], av[1], av[2], av[3]);
+  }
 }
 
-template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool QSPLIT>
+template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool QSPLIT, bool STR>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int NW = is_bf16<E>() ? ATTN_DKDV_NW_BF16 : ATTN_DKDV_NW_F32;
   constexpr int NSPLIT = is_bf16<E>() ? ATTN_DKDV_NSPLIT_BF16 : ATTN_DKDV_NSPLIT_F32;
   constexpr int KPW = is_bf16<E>() ? ATTN_DKDV_KPW_BF16 : ATTN_DKDV_KPW_F32;
   constexpr int NST = is_bf16<E>() ? ATTN_DKDV_NST_BF16 : ATTN_DKDV_NST_F32;
   using T = typename E::T;
-  constexpr auto kern = bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS, QSPLIT>;
+  constexpr auto kern =
+      bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS, QSPLIT, STR>;
+  const Layout lay = a.layout != nullptr ? *a.layout : Layout{};
   constexpr int BKV = 32 * (NW / NSPLIT);
   constexpr int BQ = 32 * NSPLIT * KPW;
   static_assert(BKV == dkdv_key_tile(is_bf16<E>()) && BQ == dkdv_query_tile(is_bf16<E>()),
@@ -439,24 +473,28 @@ static hipError_t launch(const BwdArgs& a) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SPq,
                      a.SPk, a.Sq, a.Sk, a.BH * a.Sq, a.scale * kLog2e, a.scale, a.BH, a.H, a.kvlen,
-                     QSPLIT ? a.part : nullptr, nqs, qpc, nitems, sched);
+                     QSPLIT ? a.part : nullptr, nqs, qpc, nitems, sched, lay);
   if (QSPLIT) {
     const long long nel4 = (long long)a.BH * a.Sk * D / 4;
-    hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<T>, dim3((unsigned)((nel4 + 63) / 64)), dim3(64),
-                       0, a.stream, a.part, (T*)a.dk, (T*)a.dv, nqs, nel4);
+    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T, D, STR>), dim3((unsigned)((nel4 + 63) / 64)),
+                       dim3(64), 0, a.stream, a.part, (T*)a.dk, (T*)a.dv, nqs, nel4, a.Sk, a.H,
+                       lay);
   }
   return hipGetLastError();
 }
 
-template <class E, int D, bool CAUSAL, bool WDS, bool CROSS>
+template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool STR>
 static hipError_t launch_s(const BwdArgs& a) {
-  if (a.part != nullptr && a.nqs > 1) return launch<E, D, CAUSAL, WDS, CROSS, true>(a);
-  return launch<E, D, CAUSAL, WDS, CROSS, false>(a);
+  if (a.part != nullptr && a.nqs > 1) return launch<E, D, CAUSAL, WDS, CROSS, true, STR>(a);
+  return launch<E, D, CAUSAL, WDS, CROSS, false, STR>(a);
 }
 
+// (strided layouts run the cross-attention instantiation)
 template <class E, int D, bool CAUSAL, bool WDS>
 static hipError_t launch_x(const BwdArgs& a) {
-  return a.cross ? launch_s<E, D, CAUSAL, WDS, true>(a) : launch_s<E, D, CAUSAL, WDS, false>(a);
+  if (a.layout != nullptr) return launch_s<E, D, CAUSAL, WDS, true, true>(a);
+  return a.cross ? launch_s<E, D, CAUSAL, WDS, true, false>(a)
+                 : launch_s<E, D, CAUSAL, WDS, false, false>(a);
 }
 
 template <class E, int D>

@@ -29,12 +29,13 @@
 
 namespace attn {
 
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS, bool STR>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     typename E::T* __restrict__ dQ, const float* __restrict__ Dws, int Sq, int Sk_, int Lws,
-    float c, float scale, int H, const int* __restrict__ kvlen) {
+    float c, float scale, int H, const int* __restrict__ kvlen, const Layout lay) {
+  // STR: Q, K, V, dO, dQ are laid out by `lay` (else [B, H, S, D] row-major).
   // Queries Sq, keys Sk (one length in self-attention, CROSS = false); key j
   // is visible from query i iff j < L and, when causal, j <= i + off
   // (head_keys).  Lws: offset of LSE*log2(e) in the workspace (B*H*Sq).
@@ -59,8 +60,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
   const int Sk = CROSS ? Sk_ : Sq;
   const size_t base = (size_t)bh * Sq * D;
-  const T* k = K + (size_t)bh * Sk * D;
-  const T* v = V + (size_t)bh * Sk * D;
+  const T* k = K + head_off<STR, D>(lay.k, bh, H, Sk);
+  const T* v = V + head_off<STR, D>(lay.v, bh, H, Sk);
+  const int ldk = row_ld<STR, D>(lay.k), ldv = row_ld<STR, D>(lay.v);
   int L, off;
   head_keys<CROSS>(kvlen, bh, H, Sq, Sk, L, off);
   const int krows = CROSS ? max(L, 1) : Sk;  // key rows the loads may read
@@ -72,8 +74,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   const size_t qrow = base + (size_t)min(qi, Sq - 1) * D + h * (D / 2);
 
   RowFrag<E, D> qf, dof;
-  load_row_frag<E, D>(qf, Q + qrow, qvalid);
-  load_row_frag<E, D>(dof, dO + qrow, qvalid);
+  if constexpr (STR) {
+    const size_t r = (size_t)min(qi, Sq - 1);
+    load_row_frag<E, D>(qf, Q + head_off<STR, D>(lay.q, bh, H, Sq) + r * lay.q.s + h * (D / 2),
+                        qvalid);
+    load_row_frag<E, D>(dof,
+                        dO + head_off<STR, D>(lay.dout, bh, H, Sq) + r * lay.dout.s + h * (D / 2),
+                        qvalid);
+  } else {
+    load_row_frag<E, D>(qf, Q + qrow, qvalid);
+    load_row_frag<E, D>(dof, dO + qrow, qvalid);
+  }
   // D_i and LSE_i*log2(e), written by the prep kernel
   const float di = qvalid ? Dws[(size_t)bh * Sq + qi] : 0.f;
   const float lse2 = qvalid ? Dws[(size_t)Lws + (size_t)bh * Sq + qi] : 0.f;
@@ -85,10 +96,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   const int kend = CAUSAL ? min(L, qt * BR + BR + off) : L;
   const int nkt = max((kend + BK - 1) / BK, 0);
 
-  const unsigned lo = LD::lane_offset(w, lane);
+  const unsigned lo = STR ? 0u : LD::lane_offset(w, lane);
+  auto issue_kv = [&](char* st, int row0) __attribute__((always_inline)) {
+    if constexpr (STR)
+      LD::issue_ld(st, k, ldk, v, ldv, row0, krows, w, lane);
+    else
+      LD::issue(st, k, v, row0, krows, w, lane, lo);
+  };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
-    if (s < nkt) LD::issue(smem + s * LD::BYTES, k, v, s * BK, krows, w, lane, lo);
+    if (s < nkt) issue_kv(smem + s * LD::BYTES, s * BK);
 
   // One staged tile of keys.  When the stages' LDS addresses fit 16-bit
   // offsets, the loop is unrolled by NST with the stage index constant.
@@ -96,8 +113,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const int si = sc;  // kt % NST
     wait_tiles<LD::NLOADS>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();  // tile kt is in LDS; every wave is done with tile kt-1
-    if (kt + NST - 1 < nkt)
-      LD::issue(smem + ((kt + NST - 1) % NST) * LD::BYTES, k, v, (kt + NST - 1) * BK, krows, w, lane, lo);
+    if (kt + NST - 1 < nkt) issue_kv(smem + ((kt + NST - 1) % NST) * LD::BYTES, (kt + NST - 1) * BK);
     if (!wave_active) return;
     const char* Kt = smem + si * LD::BYTES;
     const char* Vt = Kt + TILEB;
@@ -170,13 +186,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   }
   if (!wave_active) return;
   // acc[db] element r: dQ[q0 + out_row(r, h)][db*32 + n]
-  T* dq = dQ + base;
+  T* dq = STR ? dQ + head_off<STR, D>(lay.dq, bh, H, Sq) : dQ + base;
+  const int lddq = row_ld<STR, D>(lay.dq);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = q0 + out_row(r, h);
     if (row < Sq) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) dq[(size_t)row * D + db * 32 + n] = (T)(acc[db][r] * scale);
+      for (int db = 0; db < NDB; ++db)
+        dq[(size_t)row * lddq + db * 32 + n] = (T)(acc[db][r] * scale);
     }
   }
 }
@@ -190,11 +208,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 // Blocks with no visible key (above the causal diagonal, or past S) are
 // skipped; the dK+dV kernel wrote exact zeros for every masked entry and
 // every key past S inside the blocks it processed.
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS, bool STR>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
     const typename E::T* __restrict__ K, const typename E::T* __restrict__ dST,
     typename E::T* __restrict__ dQ, int Sq, int Sk_, int SPq, int SPk, float scale, int H,
-    const int* __restrict__ kvlen) {
+    const int* __restrict__ kvlen, const Layout lay) {
+  // STR: K and dQ are laid out by `lay` (dS^T is the packed workspace).
   using T = typename E::T;
   constexpr int RB = NW / NSPLIT;
   constexpr int BR = 32 * RB;
@@ -216,7 +235,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   const int bh = blockIdx.x;
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
   const int Sk = CROSS ? Sk_ : Sq;
-  const T* k = K + (size_t)bh * Sk * D;
+  const T* k = K + head_off<STR, D>(lay.k, bh, H, Sk);
+  const int ldk = row_ld<STR, D>(lay.k);
   const T* dst_ = dST + (size_t)bh * SPk * SPq;
   int L, off;  // key j is visible from query i iff j < L and (causal) j <= i + off
   head_keys<CROSS>(kvlen, bh, H, Sq, Sk, L, off);
@@ -231,11 +251,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
 
   const int kend = CAUSAL ? min(L, qw0 + BR + off) : L;
   const int nkt = max((kend + BK - 1) / BK, 0);
-  const unsigned los = LDS_::lane_offset(SPq, w, lane), lok = LDK::lane_offset(D, w, lane);
+  const unsigned los = LDS_::lane_offset(SPq, w, lane), lok = LDK::lane_offset(ldk, w, lane);
   auto issue = [&](int t) __attribute__((always_inline)) {
     char* st = smem + (t % NST) * STAGE;
     LDS_::issue(st, dst_, SPq, t * BK, SPk, qw0, w, lane, los);
-    LDK::issue(st + LDS_::BYTES, k, D, t * BK, krows, 0, w, lane, lok);
+    LDK::issue(st + LDS_::BYTES, k, ldk, t * BK, krows, 0, w, lane, lok);
   };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
@@ -291,18 +311,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
     }
   }
   if (!wave_active) return;
-  T* dq = dQ + (size_t)bh * Sq * D;
+  T* dq = dQ + head_off<STR, D>(lay.dq, bh, H, Sq);
+  const int lddq = row_ld<STR, D>(lay.dq);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = q0 + out_row(r, h);
     if (row < Sq) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) dq[(size_t)row * D + db * 32 + n] = (T)(acc[db][r] * scale);
+      for (int db = 0; db < NDB; ++db)
+        dq[(size_t)row * lddq + db * 32 + n] = (T)(acc[db][r] * scale);
     }
   }
 }
 
-template <class E, int D, bool CAUSAL, bool CROSS>
+template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
 static hipError_t launch_gemm(const BwdArgs& a) {
   constexpr int NW = 4, NSPLIT = 2, KPW = 1;
   constexpr int NST = is_bf16<E>() ? 3 : 2;
@@ -310,13 +332,14 @@ static hipError_t launch_gemm(const BwdArgs& a) {
   constexpr int BR = 32 * (NW / NSPLIT);
   const int nqt = (a.Sq + BR - 1) / BR;
   dim3 grid(a.BH, nqt);
-  hipLaunchKernelGGL((bwd_dq_gemm_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS>), grid,
+  hipLaunchKernelGGL((bwd_dq_gemm_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR>), grid,
                      dim3(NW * 64), 0, a.stream, (const T*)a.k, (const T*)a.ds, (T*)a.dq, a.Sq,
-                     a.Sk, a.SPq, a.SPk, a.scale, a.H, a.kvlen);
+                     a.Sk, a.SPq, a.SPk, a.scale, a.H, a.kvlen,
+                     a.layout != nullptr ? *a.layout : Layout{});
   return hipGetLastError();
 }
 
-template <class E, int D, bool CAUSAL, bool CROSS>
+template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int NW = is_bf16<E>() ? ATTN_DQ_NW_BF16 : ATTN_DQ_NW_F32;
   constexpr int NSPLIT = is_bf16<E>() ? ATTN_DQ_NSPLIT_BF16 : ATTN_DQ_NSPLIT_F32;
@@ -326,18 +349,24 @@ static hipError_t launch(const BwdArgs& a) {
   constexpr int BR = 32 * (NW / NSPLIT);
   const int nqt = (a.Sq + BR - 1) / BR;
   dim3 grid(a.BH, nqt);
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS>), grid, dim3(NW * 64),
-                     0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
-                     (T*)a.dq, a.delta, a.Sq, a.Sk, a.BH * a.Sq, a.scale * kLog2e, a.scale, a.H,
-                     a.kvlen);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR>), grid,
+                     dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                     (const T*)a.dout, (T*)a.dq, a.delta, a.Sq, a.Sk, a.BH * a.Sq,
+                     a.scale * kLog2e, a.scale, a.H, a.kvlen,
+                     a.layout != nullptr ? *a.layout : Layout{});
   return hipGetLastError();
 }
 
+// (strided layouts run the cross-attention instantiation)
 template <class E, int D, bool CAUSAL>
 static hipError_t launch_x(const BwdArgs& a) {
-  if (a.ds != nullptr)
-    return a.cross ? launch_gemm<E, D, CAUSAL, true>(a) : launch_gemm<E, D, CAUSAL, false>(a);
-  return a.cross ? launch<E, D, CAUSAL, true>(a) : launch<E, D, CAUSAL, false>(a);
+  if (a.ds != nullptr) {
+    if (a.layout != nullptr) return launch_gemm<E, D, CAUSAL, true, true>(a);
+    return a.cross ? launch_gemm<E, D, CAUSAL, true, false>(a)
+                   : launch_gemm<E, D, CAUSAL, false, false>(a);
+  }
+  if (a.layout != nullptr) return launch<E, D, CAUSAL, true, true>(a);
+  return a.cross ? launch<E, D, CAUSAL, true, false>(a) : launch<E, D, CAUSAL, false, false>(a);
 }
 
 template <class E, int D>

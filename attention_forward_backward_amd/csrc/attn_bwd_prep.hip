@@ -17,11 +17,14 @@
 
 namespace attn {
 
-template <class E, int D, int UNR>
+template <class E, int D, int UNR, bool STR>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __restrict__ O,
                                                         const typename E::T* __restrict__ dO,
                                                         const float* __restrict__ LSE,
-                                                        float* __restrict__ ws, int L) {
+                                                        float* __restrict__ ws, int L, int Sq,
+                                                        int H, const Layout lay) {
+  // Rows are the B*H*Sq query rows in [B, H, Sq] order; STR: O and dO are
+  // laid out by `lay`.
   using T = typename E::T;
   constexpr int EPC = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / EPC;              // chunks per row (<= 32)
@@ -33,8 +36,16 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __re
 #pragma unroll
   for (int i = 0; i < UNR; ++i) {  // all loads first, then the arithmetic
     const int row = min((wave * UNR + i) * RPW + lane / CPR, L - 1);
-    a[i] = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + chunk * EPC);
-    b[i] = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + chunk * EPC);
+    if constexpr (STR) {
+      const int bh = row / Sq, s = row % Sq;
+      a[i] = *reinterpret_cast<const u32x4*>(O + head_off<STR, D>(lay.o, bh, H, Sq) +
+                                              (size_t)s * lay.o.s + chunk * EPC);
+      b[i] = *reinterpret_cast<const u32x4*>(dO + head_off<STR, D>(lay.dout, bh, H, Sq) +
+                                              (size_t)s * lay.dout.s + chunk * EPC);
+    } else {
+      a[i] = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + chunk * EPC);
+      b[i] = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + chunk * EPC);
+    }
   }
 #pragma unroll
   for (int i = 0; i < UNR; ++i) {
@@ -64,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const typename E::T* __re
   }
 }
 
-template <class E, int D>
+template <class E, int D, bool STR>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int EPC = 16 / (int)sizeof(typename E::T);
   constexpr int RPW = 64 / (D / EPC);
@@ -73,17 +84,18 @@ static hipError_t launch(const BwdArgs& a) {
   const int waves = (L + RPW * UNR - 1) / (RPW * UNR);
   const int blocks = (waves + 3) / 4;
   using T = typename E::T;
-  hipLaunchKernelGGL((bwd_prep_kernel<E, D, UNR>), dim3(blocks), dim3(256), 0, a.stream,
-                     (const T*)a.o, (const T*)a.dout, a.lse, a.delta, L);
+  hipLaunchKernelGGL((bwd_prep_kernel<E, D, UNR, STR>), dim3(blocks), dim3(256), 0, a.stream,
+                     (const T*)a.o, (const T*)a.dout, a.lse, a.delta, L, a.Sq, a.H,
+                     a.layout != nullptr ? *a.layout : Layout{});
   return hipGetLastError();
 }
 
 template <class E>
 static hipError_t launch_d(const BwdArgs& a) {
   switch (a.D) {
-    case 32: return launch<E, 32>(a);
-    case 64: return launch<E, 64>(a);
-    case 128: return launch<E, 128>(a);
+    case 32: return a.layout ? launch<E, 32, true>(a) : launch<E, 32, false>(a);
+    case 64: return a.layout ? launch<E, 64, true>(a) : launch<E, 64, false>(a);
+    case 128: return a.layout ? launch<E, 128, true>(a) : launch<E, 128, false>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -251,6 +251,34 @@ __device__ inline void head_keys(const int* __restrict__ kvlen, int bh, int H, i
   }
 }
 
+// Element strides (batch, head, row) of a tensor indexed [B, H, S, D] whose
+// head dimension is contiguous, and the layout of every tensor of a call
+// (strided entry points; the other entry points use [B, H, S, D] row-major).
+struct Str3 {
+  int b, h, s;  // (the host checks each is below 2^31)
+};
+struct Layout {
+  Str3 q, k, v, o, dout, dq, dk, dv;
+};
+
+// First element of head bh's rows: with STR from the strides, else in the
+// row-major [B, H, rows, D] layout.
+template <bool STR, int D>
+__device__ inline size_t head_off(const Str3& st, int bh, int H, int rows) {
+  if constexpr (STR)
+    return (size_t)(bh / H) * (unsigned)st.b + (size_t)(bh % H) * (unsigned)st.h;
+  else
+    return (size_t)bh * rows * D;
+}
+// Elements between consecutive rows.
+template <bool STR, int D>
+__device__ inline int row_ld(const Str3& st) {
+  if constexpr (STR)
+    return (int)st.s;
+  else
+    return D;
+}
+
 // Static schedule of a persistent launch, computed on the host and passed by
 // value in the kernel arguments.  Workgroups are dispatched round-robin over
 // the 8 XCDs, so workgroup g runs on XCD g % 8 as its slot g / 8.  When the
@@ -412,6 +440,42 @@ struct StageLoader {
       const int logical = (pc % TL::CPR) ^ TL::swz(row);
       const T* src = (mat == 0 ? src0 : src1) + (size_t)min(row0 + row, S - 1) * D + logical * TL::EPC;
       __builtin_amdgcn_global_load_lds(src, stage + slot * 1024, 16, 0, 0);
+    }
+  }
+
+  // The same loads from matrices whose rows are ld0 and ld1 elements apart
+  // (strided layouts).  A lane keeps only its row in the wave's first load
+  // and its chunk's byte column (with FAST both hold for every load) and
+  // forms each address from them; rows past S read row S-1.
+  __device__ static inline void issue_ld(char* stage, const T* src0, int ld0, const T* src1,
+                                         int ld1, int row0, int S, int w, int lane) {
+    if constexpr (FAST) {
+      const int lrow = w * RPS + lane / TL::CPR;
+      const int lcolb = ((lane % TL::CPR) ^ TL::swz(lrow)) * TL::EPC * (int)sizeof(T);
+      const int lim = row0 + BT <= S ? 0x7fffffff : S - 1;
+#pragma unroll
+      for (int i = 0; i < NLOADS; ++i) {
+        const int slot = i * NW + w;
+        const int mat = slot * 64 / CH_PER;  // wave-uniform
+        const size_t grow = (size_t)min(row0 + i * RS - mat * BT + lrow, lim);
+        const char* src = mat == 0
+                              ? reinterpret_cast<const char*>(src0) + grow * ld0 * sizeof(T)
+                              : reinterpret_cast<const char*>(src1) + grow * ld1 * sizeof(T);
+        __builtin_amdgcn_global_load_lds(src + lcolb, stage + slot * 1024, 16, 0, 0);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NLOADS; ++i) {
+      const int slot = i * NW + w;
+      const int chunk = slot * 64 + lane;
+      const int mat = chunk / CH_PER;
+      const int pc = chunk - mat * CH_PER;
+      const int row = pc / TL::CPR;
+      const int logical = (pc % TL::CPR) ^ TL::swz(row);
+      const size_t r = (size_t)min(row0 + row, S - 1);
+      const T* src = mat == 0 ? src0 + r * ld0 : src1 + r * ld1;
+      __builtin_amdgcn_global_load_lds(src + logical * TL::EPC, stage + slot * 1024, 16, 0, 0);
     }
   }
 };

@@ -34,16 +34,18 @@
 
 namespace attn {
 
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS,
+          bool STR>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O,
     float* __restrict__ LSE, int Sq, int Sk_, float c, int BH, int H,
-    const int* __restrict__ kvlen, int nitems, const Sched sched) {
+    const int* __restrict__ kvlen, int nitems, const Sched sched, const Layout lay) {
   // LSE may be null (an inference-only forward stores no LSE).  Queries Sq,
   // keys Sk (one length in self-attention, CROSS = false); per batch*head the
   // first L keys exist and key j is visible from query i iff j < L and, when
-  // causal, j <= i + off (head_keys).
+  // causal, j <= i + off (head_keys).  STR: Q, K, V, O are laid out by `lay`
+  // (else [B, H, S, D] row-major).
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-query blocks per item
@@ -65,8 +67,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   const int g = blockIdx.x, G = gridDim.x;
   const int Sk = CROSS ? Sk_ : Sq;
   const int nqt = (Sq + BR - 1) / BR;
-  const unsigned lo = LD::lane_offset(w, lane);
-  const unsigned qlo = QL::lane_offset(D, w, lane);
+  const int ldk = row_ld<STR, D>(lay.k), ldv = row_ld<STR, D>(lay.v);
+  const int ldq = row_ld<STR, D>(lay.q), ldo = row_ld<STR, D>(lay.o);
+  const unsigned lo = STR ? 0u : LD::lane_offset(w, lane);
+  const unsigned qlo = QL::lane_offset(ldq, w, lane);
   auto item_qt = [&](int it) { return nqt - 1 - it / BH; };
   // Key tiles of item it: those holding a key visible from one of its
   // queries; an item none of whose queries sees a key still takes one tile
@@ -101,12 +105,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   // Loader cursor: tile lkt of item lit is the next one to issue.
   int lr = 0, lit = sched_item(sched, 0, g, G, BH), lkt = 0, lnkt = item_nkt(lit);
   int lrows = key_rows(lit);
-  size_t lbase = (size_t)(lit % BH) * Sk * D;
+  size_t kbase = head_off<STR, D>(lay.k, lit % BH, H, Sk);
+  size_t vbase = head_off<STR, D>(lay.v, lit % BH, H, Sk);
   // While tiles remain, the tile issued at stream position pos goes to ring
   // slot (pos + NST - 1) % NST, a constant of the unrolled step.
   auto issue_next = [&](const int slot) __attribute__((always_inline)) {
     if (lit >= nitems) return;
-    LD::issue(smem + slot * STAGE, K + lbase, V + lbase, lkt * BK, lrows, w, lane, lo);
+    if constexpr (STR)
+      LD::issue_ld(smem + slot * STAGE, K + kbase, ldk, V + vbase, ldv, lkt * BK, lrows, w, lane);
+    else
+      LD::issue(smem + slot * STAGE, K + kbase, V + vbase, lkt * BK, lrows, w, lane, lo);
     vm += LD::NLOADS;
 #pragma unroll
     for (int i = 0; i < NST; ++i)
@@ -117,13 +125,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
       if (lit < nitems) {
         lnkt = item_nkt(lit);
         lrows = key_rows(lit);
-        lbase = (size_t)(lit % BH) * Sk * D;
+        kbase = head_off<STR, D>(lay.k, lit % BH, H, Sk);
+        vbase = head_off<STR, D>(lay.v, lit % BH, H, Sk);
       }
     }
   };
   // The Q tile of item it (rows past Sq read row Sq-1) into its LDS buffer.
   auto load_q = [&](int it) __attribute__((always_inline)) {
-    QL::issue(qtile, Q + (size_t)(it % BH) * Sq * D, D, item_qt(it) * BR, Sq, 0, w, lane, qlo);
+    QL::issue(qtile, Q + head_off<STR, D>(lay.q, it % BH, H, Sq), ldq, item_qt(it) * BR, Sq, 0, w,
+              lane, qlo);
     vm += QL::NLOADS;
     qmark = vm;
   };
@@ -319,7 +329,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
       // (CROSS: a row with no visible key has l = 0: O = 0, LSE = -inf)
       const float inv = (CROSS && !(l > 0.f)) ? 0.f : 1.f / l;
       if (qi < Sq) {
-        T* orow = O + ((size_t)bh * Sq + qi) * D;
+        T* orow;
+        if constexpr (STR)
+          orow = O + head_off<STR, D>(lay.o, bh, H, Sq) + (size_t)qi * ldo;
+        else
+          orow = O + ((size_t)bh * Sq + qi) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -362,14 +376,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   }
 }
 
-template <class E, int D, bool CAUSAL, bool CROSS>
+template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
 static hipError_t launch(const FwdArgs& a) {
   constexpr int NW = is_bf16<E>() ? ATTN_FWD_NW_BF16 : ATTN_FWD_NW_F32;
   constexpr int NSPLIT = is_bf16<E>() ? ATTN_FWD_NSPLIT_BF16 : ATTN_FWD_NSPLIT_F32;
   constexpr int KPW = is_bf16<E>() ? ATTN_FWD_KPW_BF16 : ATTN_FWD_KPW_F32;
   constexpr int NST = is_bf16<E>() ? ATTN_FWD_NST_BF16 : ATTN_FWD_NST_F32;
   using T = typename E::T;
-  constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS>;
+  constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR>;
   constexpr int BR = 32 * (NW / NSPLIT);
   const int nqt = (a.Sq + BR - 1) / BR;
   const int nitems = a.BH * nqt;
@@ -386,14 +400,19 @@ static hipError_t launch(const FwdArgs& a) {
   const Sched sched = make_sched(grid, a.BH, works);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.o, a.lse, a.Sq, a.Sk, a.scale * kLog2e, a.BH, a.H,
-                     a.kvlen, nitems, sched);
+                     a.kvlen, nitems, sched, a.layout != nullptr ? *a.layout : Layout{});
   return hipGetLastError();
 }
 
+// (strided layouts run the cross-attention instantiation, which handles any
+// lengths)
 template <class E, int D>
 static hipError_t launch_c(const FwdArgs& a) {
-  if (a.cross) return a.causal ? launch<E, D, true, true>(a) : launch<E, D, false, true>(a);
-  return a.causal ? launch<E, D, true, false>(a) : launch<E, D, false, false>(a);
+  if (a.layout != nullptr)
+    return a.causal ? launch<E, D, true, true, true>(a) : launch<E, D, false, true, true>(a);
+  if (a.cross)
+    return a.causal ? launch<E, D, true, true, false>(a) : launch<E, D, false, true, false>(a);
+  return a.causal ? launch<E, D, true, false, false>(a) : launch<E, D, false, false, false>(a);
 }
 
 template <class E>

@@ -78,11 +78,12 @@ __device__ inline float row16_sum(float x) {
   return x;
 }
 
-template <class E, int D, int NW, int QG, int U, bool CAUSAL, bool CROSS>
+template <class E, int D, int NW, int QG, int U, bool CAUSAL, bool CROSS, bool STR>
 __global__ __launch_bounds__(NW * 64) void fwd_small_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O, float* __restrict__ LSE,
-    int Sq, int Sk, float c, int BH, int H, const int* __restrict__ kvlen, int nqg) {
+    int Sq, int Sk, float c, int BH, int H, const int* __restrict__ kvlen, int nqg,
+    const Layout lay) {
   using T = typename E::T;
   constexpr int DV = D / 16;
   constexpr int KB = 4 * U;
@@ -112,7 +113,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_small_kernel(
 #pragma unroll
   for (int i = 0; i < QG; ++i) {
     if (q0 + i < Sq) {
-      load_slice<T, DV>(Q + ((size_t)bh * Sq + q0 + i) * D + cc * DV, q[i]);
+      load_slice<T, DV>(Q + head_off<STR, D>(lay.q, bh, H, Sq) +
+                            (size_t)(q0 + i) * row_ld<STR, D>(lay.q) + cc * DV,
+                        q[i]);
     } else {
 #pragma unroll
       for (int e = 0; e < DV; ++e) q[i][e] = 0.f;
@@ -130,8 +133,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_small_kernel(
     for (int e = 0; e < DV; ++e) o[i][e] = 0.f;
   }
 
-  const T* Kh = K + (size_t)bh * Sk * D + cc * DV;
-  const T* Vh = V + (size_t)bh * Sk * D + cc * DV;
+  const T* Kh = K + head_off<STR, D>(lay.k, bh, H, Sk) + cc * DV;
+  const T* Vh = V + head_off<STR, D>(lay.v, bh, H, Sk) + cc * DV;
+  const int ldk = row_ld<STR, D>(lay.k), ldv = row_ld<STR, D>(lay.v);
   for (int base = w * KB; base < kend; base += NW * KB) {
     float kr[U][DV], vr[U][DV];
 #pragma unroll
@@ -139,12 +143,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_small_kernel(
       // rows past kend are clamped to the last one the group may see (their
       // scores are masked): no row at or past the valid keys is read
       const int row = min(base + 4 * u + rg, kend - 1);
-      load_slice<T, DV>(Kh + (size_t)row * D, kr[u]);
+      load_slice<T, DV>(Kh + (size_t)row * ldk, kr[u]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = min(base + 4 * u + rg, kend - 1);
-      load_slice<T, DV>(Vh + (size_t)row * D, vr[u]);
+      load_slice<T, DV>(Vh + (size_t)row * ldv, vr[u]);
     }
     if constexpr (RQKV) {
 #pragma unroll
@@ -239,13 +243,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_small_kernel(
       acc = fmaf(os[v][i][d], a, acc);
     }
     const float inv = (lsum > 0.f) ? 1.f / lsum : 0.f;
-    O[((size_t)bh * Sq + qi) * D + d] = (T)(acc * inv);
+    O[head_off<STR, D>(lay.o, bh, H, Sq) + (size_t)qi * row_ld<STR, D>(lay.o) + d] =
+        (T)(acc * inv);
     if (d == 0 && LSE != nullptr)
       LSE[(size_t)bh * Sq + qi] = (lsum > 0.f) ? (M + __log2f(lsum)) * kLn2 : -INFINITY;
   }
 }
 
-template <class E, int D, int QG, bool CAUSAL, bool CROSS>
+template <class E, int D, int QG, bool CAUSAL, bool CROSS, bool STR>
 static hipError_t launch_small(const FwdArgs& a) {
   constexpr int NW = QG == 1 ? ATTN_FWD_SMALL_NW1 : ATTN_FWD_SMALL_NW4;
   constexpr int U0 = QG == 1 ? ATTN_FWD_SMALL_U1 : ATTN_FWD_SMALL_U4;
@@ -258,22 +263,28 @@ static hipError_t launch_small(const FwdArgs& a) {
   // heads in blocks of 8 (one per XCD), then query groups, then the block
   const long long grid = (long long)((a.BH + 7) / 8) * 8 * nqg;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fwd_small_kernel<E, D, NW, QG, U, CAUSAL, CROSS>), dim3((unsigned)grid),
-                     dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     (T*)a.o, a.lse, a.Sq, a.Sk, a.scale * kLog2e, a.BH, a.H, a.kvlen, nqg);
+  hipLaunchKernelGGL((fwd_small_kernel<E, D, NW, QG, U, CAUSAL, CROSS, STR>),
+                     dim3((unsigned)grid), dim3(NW * 64), 0, a.stream, (const T*)a.q,
+                     (const T*)a.k, (const T*)a.v, (T*)a.o, a.lse, a.Sq, a.Sk, a.scale * kLog2e,
+                     a.BH, a.H, a.kvlen, nqg, a.layout != nullptr ? *a.layout : Layout{});
   return hipGetLastError();
+}
+
+template <class E, int D, int QG>
+static hipError_t launch_small_g(const FwdArgs& a) {
+  if (a.layout != nullptr)  // (strided: the cross-attention instantiation)
+    return a.causal ? launch_small<E, D, QG, true, true, true>(a)
+                    : launch_small<E, D, QG, false, true, true>(a);
+  if (a.cross)
+    return a.causal ? launch_small<E, D, QG, true, true, false>(a)
+                    : launch_small<E, D, QG, false, true, false>(a);
+  return a.causal ? launch_small<E, D, QG, true, false, false>(a)
+                  : launch_small<E, D, QG, false, false, false>(a);
 }
 
 template <class E, int D>
 static hipError_t launch_small_q(const FwdArgs& a) {
-  if (a.Sq == 1) {
-    if (a.cross) return a.causal ? launch_small<E, D, 1, true, true>(a)
-                                 : launch_small<E, D, 1, false, true>(a);
-    return a.causal ? launch_small<E, D, 1, true, false>(a) : launch_small<E, D, 1, false, false>(a);
-  }
-  if (a.cross) return a.causal ? launch_small<E, D, 4, true, true>(a)
-                               : launch_small<E, D, 4, false, true>(a);
-  return a.causal ? launch_small<E, D, 4, true, false>(a) : launch_small<E, D, 4, false, false>(a);
+  return a.Sq == 1 ? launch_small_g<E, D, 1>(a) : launch_small_g<E, D, 4>(a);
 }
 
 template <class E>

@@ -148,6 +148,7 @@ struct FwdArgs {
   bool causal;
   float scale;
   hipStream_t stream;
+  const Layout* layout = nullptr;  // strides of q, k, v, o; null: [B, H, S, D] row-major
 };
 
 struct BwdArgs {
@@ -159,6 +160,7 @@ struct BwdArgs {
   void* ds;      // workspace dS^T [B*H][SPk][SPq] (dtype), or null: dQ recomputes
   float* part;   // workspace dK, dV partials [2][nqs][B*H][Sk][D] f32, or null
   int nqs;       // query chunks of the dK+dV pass (1: no partials)
+  const Layout* layout = nullptr;  // strides of every tensor; null: [B, H, S, D] row-major
   int SPq, SPk;  // query stride and key rows per head of dS^T (rounded up to the tile)
   int BH, H, Sq, Sk, D;
   const int* kvlen;

@@ -457,11 +457,12 @@ def graph_time(fn, per_graph=20, replays=30) -> float:
 
 def rope_section(cfg, dtypes, args, stream, log) -> dict:
     """The workload's step on a packed [B, S, 3, H, D] projection with 1-D
-    RoPE on Q and K: attn_rope_copy brings Q, K (rotated) and V into
-    [B, H, S, D] and dO from [B, S, H, D], and takes O to [B, S, H, D] and
-    dQ, dK (transposed rotation) and dV back into the packed gradient.  Each
-    pass reads and writes one [B, H, S, D] tensor (plus table rows): HBM-bound,
-    timed from HIP graph replays."""
+    RoPE on Q and K, O and dO in [B, S, H, D]: attn_rope_copy writes the
+    rotated Q and K ([B, H, S, D]) and takes dQ, dK back through the
+    transposed rotation into the packed gradient; the strided entry points
+    read V and dO and write O and dV in place.  A rotation pass reads and
+    writes one [B, H, S, D] tensor (plus table rows): HBM-bound.  Timed from
+    HIP graph replays."""
     import torch
     import attention_forward_backward_amd as afb
     from attention_forward_backward_amd import synth
@@ -480,31 +481,46 @@ def rope_section(cfg, dtypes, args, stream, log) -> dict:
         tdt = torch.bfloat16 if dt == "bf16" else torch.float32
         pk = torch.from_numpy(synth.normal_f32(args.seed, 0, (B, S, 3, H, D))).cuda().to(tdt)
         dOt = torch.from_numpy(synth.normal_f32(args.seed, 3, (B, S, H, D))).cuda().to(tdt)
-        q, k, v, o, do, dq, dk, dv = (torch.empty(shp, dtype=tdt, device="cuda") for _ in range(8))
+        q, k, dq, dk = (torch.empty(shp, dtype=tdt, device="cuda") for _ in range(4))
         o_s = torch.empty((B, S, H, D), dtype=tdt, device="cuda")
         dpk = torch.empty_like(pk)
         lse = torch.empty((B, H, S), device="cuda")
         code = afb.ATTN_BF16 if dt == "bf16" else afb.ATTN_F32
-        ws = torch.empty(afb.attn_bwd_workspace_size(code, B, H, S, D, cfg.causal),
+        ws = torch.empty(afb.attn_bwd_cross_workspace_size(code, B, H, S, S, D, cfg.causal),
                          dtype=torch.uint8, device="cuda")
+
+        # the strided kernels read V straight from the packed projection and
+        # dO from [B,S,H,D], and write O to [B,S,H,D] and dV into the packed
+        # gradient; only the rotated Q, K and the gradients through the
+        # rotation (dQ, dK) take a pass
+        v_view = pk[:, :, 2].permute(0, 2, 1, 3)
+        o_view = o_s.permute(0, 2, 1, 3)
+        do_view = dOt.permute(0, 2, 1, 3)
+        dv_view = dpk[:, :, 2].permute(0, 2, 1, 3)
 
         def prologue():
             afb.attn_rope_copy(pk, offs[0], pst, q, 0, bhsd, shp, ct, st)
             afb.attn_rope_copy(pk, offs[1], pst, k, 0, bhsd, shp, ct, st)
-            afb.attn_rope_copy(pk, offs[2], pst, v, 0, bhsd, shp)
 
         def epilogue():
-            afb.attn_rope_copy(o, 0, bhsd, o_s, 0, bshd, shp)
-            afb.attn_rope_copy(dOt, 0, bshd, do, 0, bhsd, shp)
             afb.attn_rope_copy(dq, 0, bhsd, dpk, offs[0], pst, shp, ct, st, transpose=True)
             afb.attn_rope_copy(dk, 0, bhsd, dpk, offs[1], pst, shp, ct, st, transpose=True)
-            afb.attn_rope_copy(dv, 0, bhsd, dpk, offs[2], pst, shp)
 
         def step():
             prologue()
-            afb.attn_fwd(q, k, v, o, lse, cfg.causal, cfg.scale)
+            afb.attn_fwd_strided(q, k, v_view, o_view, lse, None, cfg.causal, cfg.scale)
+            afb.attn_bwd_strided(q, k, v_view, o_view, do_view, lse, dq, dk, dv_view, ws, None,
+                                 cfg.causal, cfg.scale)
             epilogue()
-            afb.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, cfg.causal, cfg.scale)
+
+        # the same step without RoPE: every tensor read and written in place
+        q_view, k_view = pk[:, :, 0].permute(0, 2, 1, 3), pk[:, :, 1].permute(0, 2, 1, 3)
+        dq_view, dk_view = dpk[:, :, 0].permute(0, 2, 1, 3), dpk[:, :, 1].permute(0, 2, 1, 3)
+
+        def step_plain():
+            afb.attn_fwd_strided(q_view, k_view, v_view, o_view, lse, None, cfg.causal, cfg.scale)
+            afb.attn_bwd_strided(q_view, k_view, v_view, o_view, do_view, lse, dq_view, dk_view,
+                                 dv_view, ws, None, cfg.causal, cfg.scale)
 
         log(f"[bench] packed QKV + RoPE {shp} dtype={dt}")
         esz = 2 if dt == "bf16" else 4
@@ -514,12 +530,14 @@ def rope_section(cfg, dtypes, args, stream, log) -> dict:
         ms_rot = tf(rot)
         bytes_rot = 2 * tb + 2 * S * (D // 2) * 4
         ms_pro, ms_epi, ms_step = tf(prologue), tf(epilogue), tf(step)
+        ms_plain = tf(step_plain)
         gbs = bytes_rot / (ms_rot * 1e-3) / 1e9
         out[dt] = {"rotate_us": round(ms_rot * 1e3, 2), "rotate_bytes": bytes_rot,
                    "rotate_gbs": round(gbs, 1), "rotate_frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
                    "prologue_us": round(ms_pro * 1e3, 2), "epilogue_us": round(ms_epi * 1e3, 2),
-                   "step_us": round(ms_step * 1e3, 2)}
-        del pk, dOt, q, k, v, o, do, dq, dk, dv, o_s, dpk, lse, ws
+                   "step_us": round(ms_step * 1e3, 2),
+                   "packed_step_no_rope_us": round(ms_plain * 1e3, 2)}
+        del pk, dOt, q, k, dq, dk, o_s, dpk, lse, ws
     torch.cuda.empty_cache()
     return out
 

@@ -221,6 +221,37 @@ attn_status_t attn_bwd_cross(attn_dtype_t dtype,
                              const int* kv_len, int causal, float scale, void* stream);
 
 /*
+ * Strided layouts (the pages' packed projection forms, Section 3.2): the
+ * cross-attention forward and backward above, with every tensor given as a
+ * base pointer plus element strides (batch, head, row) of its [B,H,S,D]
+ * indexing; the head dimension is contiguous.
+ *   strides  HOST array of int64: attn_fwd_strided 12 values, (batch, head,
+ *            row) for q, k, v, o in that order; attn_bwd_strided 24 values,
+ *            for q, k, v, o, dout, dq, dk, dv.
+ * Examples: [B,H,S,D] row-major {H*S*D, S*D, D}; [B,S,H,D] {S*H*D, D, H*D};
+ * Q, K, V of a packed [B,S,3,H,D] projection at element offsets 0, H*D,
+ * 2*H*D with {S*3*H*D, D, 3*H*D}; one K, V head shared by all query heads
+ * (multi-query attention) with head stride 0 on k and v.  lse stays
+ * [B,H,seq_q] float32 and the workspace keeps its layout and sizes
+ * (attn_bwd_cross_workspace_size).  Strides are non-negative multiples of
+ * 8 elements below 2^31, row strides at most 2^24; input rows may overlap (a shared
+ * head), output rows (o, dq, dk, dv) may not (checked: sorted by stride,
+ * each stride covers the span of the dimensions below it).  Pointers as
+ * for attn_fwd_cross / attn_bwd_cross.  Errors as there, and
+ * ATTN_ERR_INVALID_ARG for a null, misaligned or overlapping stride set.
+ */
+attn_status_t attn_fwd_strided(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                               void* o, float* lse, int batch, int heads, int seq_q, int seq_k,
+                               int head_dim, const int* kv_len, const long long* strides,
+                               int causal, float scale, void* stream);
+attn_status_t attn_bwd_strided(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                               const void* o, const void* dout, const float* lse, void* dq,
+                               void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                               int batch, int heads, int seq_q, int seq_k, int head_dim,
+                               const int* kv_len, const long long* strides, int causal,
+                               float scale, void* stream);
+
+/*
  * Rotary position embedding and row-layout change, one memory-bound pass
  * (the pages' axial RoPE in front of attention, Section 5.2, and their
  * packed projection forms, Section 3.2).  For every (b, h, s) < (batch,

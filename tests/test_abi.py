@@ -19,10 +19,11 @@ def test_library_loads_and_exports_header_symbols():
                              "attn_bwd_dkdv", "attn_bwd_workspace_size",
                              "attn_bwd_workspace_size_min", "attn_fwd_cross", "attn_bwd_cross",
                              "attn_bwd_cross_workspace_size", "attn_bwd_cross_workspace_size_min",
-                             "attn_rope_copy", "attn_status_string", "attn_version"}
+                             "attn_rope_copy", "attn_fwd_strided", "attn_bwd_strided",
+                             "attn_status_string", "attn_version"}
     for name in declared:
         assert hasattr(L, name), name
-    assert afb.attn_version() == "0.4.0"
+    assert afb.attn_version() == "0.5.0"
     for code in range(5):
         assert afb.attn_status_string(code) not in ("", "unknown status")
     assert afb.attn_status_string(99) == "unknown status"
@@ -165,3 +166,33 @@ def test_rope_copy_validation():
     assert _rope(tr=2) == 1
     assert _rope(B=0) == 1 and _rope(S=0) == 1
     assert _rope(D=48) == 2 and _rope(dtype=5) == 2
+
+
+def _fwds(strides, B=2, H=3, Sq=8, Sk=8, D=64, dtype=0, q=FAKE):
+    LL = ctypes.c_longlong * 12
+    return afb.lib().attn_fwd_strided(dtype, q, FAKE, FAKE, FAKE, FAKE, B, H, Sq, Sk, D, None,
+                                      None if strides is None else LL(*strides), 1, 0.125, None)
+
+
+def _bwds(strides, B=2, H=3, S=8, D=64, wsb=1 << 20):
+    LL = ctypes.c_longlong * 24
+    return afb.lib().attn_bwd_strided(0, *([FAKE] * 9), FAKE, wsb, B, H, S, S, D, None,
+                                      None if strides is None else LL(*strides), 1, 0.125, None)
+
+
+def test_strided_validation():
+    B, H, S, D = 2, 3, 8, 64
+    bhsd = [H * S * D, S * D, D]
+    bshd = [S * H * D, D, H * D]
+    assert _fwds(None) == 1
+    assert _fwds(bhsd * 3 + [H * S * D, S * D, D + 4]) == 1        # row stride not a multiple of 8
+    assert _fwds(bhsd * 3 + [-8, S * D, D]) == 1                   # negative
+    assert _fwds(bhsd * 3 + [H * S * D, S * D, 1 << 25]) == 1      # row stride beyond 2^24
+    assert _fwds(bhsd * 3 + [H * S * D, 0, D]) == 1                # output heads overlap
+    assert _fwds(bhsd * 3 + [H * S * D, S * D, 32]) == 1           # output rows overlap (32 < D)
+    assert _fwds(bhsd * 3 + bhsd, q=None) == 1
+    assert _fwds(bhsd * 3 + bhsd, D=48) == 2
+    # shared K, V head (head stride 0) is a valid input; overlapping dK is not
+    mq = bhsd + [S * D, 0, D] * 2
+    assert _bwds(mq + bhsd * 2 + bshd + [S * D, 0, D] * 2) == 1
+    assert _bwds(mq + bhsd * 5, wsb=16) == 3                       # workspace still checked
