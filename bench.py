@@ -124,7 +124,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the attention "
-              "path here is single-GPU; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "path here is single-GPU (every (batch, head) slice is independent, so a "
+              "multi-GPU split would give each GPU its own slices).", file=sys.stderr)
         sys.exit(2)
 
     import torch
