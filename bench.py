@@ -81,6 +81,10 @@ def parse():
     p.add_argument("--cross-only", action="store_true",
                    help="run only the cross-attention and one-token workloads (prints their "
                         "section alone; used under a profiler)")
+    p.add_argument("--no-torch", action="store_true",
+                   help="skip timing torch's own scaled_dot_product_attention (context)")
+    p.add_argument("--torch-only", action="store_true",
+                   help="time only torch's scaled_dot_product_attention on the workload")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="instead of the benchmark, run 5 plain device-to-device copies of "
                         "BYTES bytes (the reference kernel for scaling HBM byte counters)")
@@ -156,6 +160,9 @@ def main():
         return
     if args.rope_only:
         print(json.dumps({"rope_packed": rope_section(cfg, dtypes, args, stream, log)}), flush=True)
+        return
+    if args.torch_only:
+        print(json.dumps({"torch_sdpa": torch_sdpa_section(cfg, args, log)}), flush=True)
         return
 
     results = {}
@@ -290,10 +297,76 @@ def main():
     if not args.no_rope and not args.only_step:
         line["rope_packed"] = rope_section(cfg, dtypes, args, stream, log)
 
+    if not args.no_torch and not args.only_step:
+        line["torch_sdpa"] = torch_sdpa_section(cfg, args, log)
+
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the float64 oracle on the host")
         line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def torch_sdpa_section(cfg, args, log) -> dict:
+    """Context, not part of the path: torch's own fused attention
+    (torch.nn.functional.scaled_dot_product_attention with autograd) timed on
+    the same workload and GPU, one forward + backward per step, with the
+    backend pinned so that no unfused fallback runs: the flash kernel for
+    bf16, the memory-efficient kernel for float32 (flash takes no float32).
+    A backend this torch build lacks is reported, not substituted."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    from attention_forward_backward_amd import synth
+
+    B, H, S, D = cfg.shape
+    out = {"what": "torch.nn.functional.scaled_dot_product_attention forward + autograd "
+                   "backward, same shape, inputs and stream; context only",
+           "torch": torch.__version__}
+    stream = torch.cuda.current_stream()
+    for dt, backend in (("f32", SDPBackend.EFFICIENT_ATTENTION),
+                        ("bf16", SDPBackend.FLASH_ATTENTION)):
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        inp = synth.config_inputs(cfg, args.seed, "f32")
+        q, k, v = (torch.from_numpy(inp[n]).cuda().to(tdt).requires_grad_(True)
+                   for n in ("q", "k", "v"))
+        do = torch.from_numpy(inp["do"]).cuda().to(tdt)
+        rec = {"backend": backend.name}
+        try:
+            with sdpa_kernel([backend]):
+                def fwd():
+                    return F.scaled_dot_product_attention(q, k, v, is_causal=cfg.causal,
+                                                          scale=cfg.scale)
+
+                def step():
+                    o = fwd()
+                    torch.autograd.grad(o, (q, k, v), do)
+
+                def timed(fn, steps, warmup):
+                    for _ in range(warmup):
+                        fn()
+                    torch.cuda.synchronize()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(steps):
+                        fn()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    return e0.elapsed_time(e1) / steps
+
+                log(f"[bench] torch sdpa {dt} ({backend.name})")
+                n = min(args.steps, 200)
+                with torch.no_grad():
+                    ms_f = timed(fwd, n, 20)
+                ms_s = timed(step, n, 20)
+            rec.update({"fwd_us": round(ms_f * 1e3, 2), "fwd_bwd_us": round(ms_s * 1e3, 2),
+                        "fwd_bwd_tflops": round(cfg.flops["fwd_bwd"] / (ms_s * 1e-3) / 1e12, 3)})
+        except Exception as e:  # a backend this build lacks: say so
+            rec["unavailable"] = f"{type(e).__name__}: {str(e)[:200]}"
+        out[dt] = rec
+        del q, k, v, do
+        torch.cuda.empty_cache()
+    return out
 
 
 def visible_pairs(w, kv_len) -> int:
