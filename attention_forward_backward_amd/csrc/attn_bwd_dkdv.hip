@@ -307,11 +307,14 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
         const int arow = qbl * 32 + pi32(n);
         f32x16 s = dot_tile<E, D>(Qt, arow, h, kf, zero16());
         f32x16 dp = dot_tile<E, D>(dOt, arow, h, vf, zero16());
-        if ((CAUSAL && qq0 < k0 + 31 - coff) || qq0 + 32 > Sq || (CROSS && k0 + 32 > cL)) {
+        if ((CAUSAL && qq0 < k0 + 31 - coff) || qq0 + 32 > Sq || k0 + 32 > (CROSS ? cL : Sk)) {
           // query(r) = qq0 + 8h + (16*(r/8) + r%8) sees key kj iff
-          // kj - off <= query < Sq (and, with CROSS, kj < L)
+          // kj - off <= query < Sq and kj < L (L = Sk without CROSS); a key
+          // past them gets P = 0 and dS = 0 exactly (its K, V registers
+          // hold finite values: zeros, or a copy of the last valid row), so
+          // blocks of valid keys need no select
           int lo = CAUSAL ? kj - coff - qq0 - 8 * h : -64;
-          if (CROSS && kj >= cL) lo = 64;
+          if (kj >= (CROSS ? cL : Sk)) lo = 64;
           const int hi = Sq - 1 - qq0 - 8 * h;
           // all-ones where o < lo or o > hi, built without per-element
           // compare masks (which would hold 16 scalar register pairs); the
@@ -351,8 +354,6 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
           // qq0 + 8h + {0..7} and qq0 + 16 + 8h + {0..7} (exact zeros where
           // masked, for queries past Sq and for keys past Sk).
           T* row = dSout + ((size_t)bh * SPk + kj) * SPq + qq0 + 8 * h;
-          // keys past Sk (only in the last key tile) store zeros
-          if (k0 + 32 > Sk && kj >= Sk) dp = zero16();
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             if constexpr (is_bf16<E>()) {

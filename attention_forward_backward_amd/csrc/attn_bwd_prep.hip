@@ -79,7 +79,7 @@ template <class E, int D, bool STR>
 static hipError_t launch(const BwdArgs& a) {
   constexpr int EPC = 16 / (int)sizeof(typename E::T);
   constexpr int RPW = 64 / (D / EPC);
-  constexpr int UNR = 4;
+  constexpr int UNR = is_bf16<E>() ? ATTN_PREP_UNR_BF16 : ATTN_PREP_UNR_F32;
   const int L = a.BH * a.Sq;
   const int waves = (L + RPW * UNR - 1) / (RPW * UNR);
   const int blocks = (waves + 3) / 4;

@@ -93,9 +93,26 @@
 #ifndef ATTN_DKDV_MINW_F32
 #define ATTN_DKDV_MINW_F32 2
 #endif
-// Query-chunk split of the dK+dV pass (dkdv_query_chunks).
-#ifndef ATTN_DKDV_SPLIT_BELOW
-#define ATTN_DKDV_SPLIT_BELOW 256
+// Row steps each wave of the prep pass loads before its arithmetic.  At
+// B8 H12 S512 D64 the prep kernel took 5.6 / 5.8 / 6.0 / 7.0 us (f32) and
+// 4.1 / 3.9 / 4.4 / 5.3 us (bf16) with 2 / 1 / 4 / 8 steps: more, smaller
+// waves start loading sooner.
+#ifndef ATTN_PREP_UNR_F32
+#define ATTN_PREP_UNR_F32 2
+#endif
+#ifndef ATTN_PREP_UNR_BF16
+#define ATTN_PREP_UNR_BF16 1
+#endif
+// Query-chunk split of the dK+dV pass (dkdv_query_chunks): shapes with
+// fewer (key tile, head) items than these are split.  At B1 H16 S1024 D128
+// causal (256 items, the longest walking 16 query tiles) two chunks took the
+// f32 backward from 220 to 168 us; bf16 measured 58.4 us unsplit, 60.3 with
+// two chunks and 77.6 with four, so it keeps the lower bound.
+#ifndef ATTN_DKDV_SPLIT_BELOW_F32
+#define ATTN_DKDV_SPLIT_BELOW_F32 512
+#endif
+#ifndef ATTN_DKDV_SPLIT_BELOW_BF16
+#define ATTN_DKDV_SPLIT_BELOW_BF16 256
 #endif
 #ifndef ATTN_DKDV_SPLIT_TARGET
 #define ATTN_DKDV_SPLIT_TARGET 512
@@ -310,7 +327,7 @@ inline int dkdv_query_chunks(bool bf16, long long BH, int Sq, int Sk) {
   const long long nkt = (Sk + dkdv_key_tile(bf16) - 1) / dkdv_key_tile(bf16);
   const int nqt = (Sq + dkdv_query_tile(bf16) - 1) / dkdv_query_tile(bf16);
   const long long items = BH * nkt;
-  if (items >= ATTN_DKDV_SPLIT_BELOW) return 1;
+  if (items >= (bf16 ? ATTN_DKDV_SPLIT_BELOW_BF16 : ATTN_DKDV_SPLIT_BELOW_F32)) return 1;
   long long n = (ATTN_DKDV_SPLIT_TARGET + items - 1) / items;
   n = std::min<long long>(n, nqt / ATTN_DKDV_QCHUNK_MIN);
   n = std::min<long long>(n, 64);

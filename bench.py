@@ -74,13 +74,17 @@ def parse():
     p.add_argument("--no-rope", action="store_true",
                    help="skip the packed-QKV + RoPE layout pass measurement")
     p.add_argument("--no-graph", action="store_true",
-                   help="time the cross and RoPE sections from eager calls only, no HIP graphs "
+                   help="time the configs, cross and RoPE sections from eager calls only, no HIP graphs "
                         "(for counter runs under a profiler)")
     p.add_argument("--rope-only", action="store_true",
                    help="run only the packed-QKV + RoPE measurement (used under a profiler)")
     p.add_argument("--cross-only", action="store_true",
                    help="run only the cross-attention and one-token workloads (prints their "
                         "section alone; used under a profiler)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip timing the five self-attention workloads (configs key)")
+    p.add_argument("--configs-only", action="store_true",
+                   help="time only the five self-attention workloads")
     p.add_argument("--no-torch", action="store_true",
                    help="skip timing torch's own scaled_dot_product_attention (context)")
     p.add_argument("--torch-only", action="store_true",
@@ -164,6 +168,9 @@ def main():
     if args.torch_only:
         print(json.dumps({"torch_sdpa": torch_sdpa_section(cfg, args, log)}), flush=True)
         return
+    if args.configs_only:
+        print(json.dumps({"configs": configs_section(args, log)}), flush=True)
+        return
 
     results = {}
     for dt in dtypes:
@@ -207,17 +214,7 @@ def main():
             bwd()
 
         def timed(fn, steps, warmup):
-            for _ in range(warmup):
-                fn()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(steps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / steps  # ms per call
+            return timed_events(fn, steps, warmup, stream)  # ms per call
 
         log(f"[bench] {dt}: {args.warmup} warmup + {args.steps} timed steps (fwd+bwd)")
         ms_step = timed(step, args.steps, args.warmup)
@@ -229,7 +226,11 @@ def main():
                     "attn_bwd_dkdv": timed(bwd_dkdv, args.steps, 3),
                     "attn_bwd_dq": timed(bwd_dq, args.steps, 3)}
             res["phases"] = {
-                ph: {"ms": ms[ph], "tflops": flops[ph] / (ms[ph] * 1e-3) / 1e12}
+                ph: {"ms": ms[ph], "tflops": flops[ph] / (ms[ph] * 1e-3) / 1e12,
+                     "frac_of_mfma_peak": round(
+                         flops[ph] / (ms[ph] * 1e-3) / 1e12 /
+                         PEAK_TFLOPS[mfma_dtype(dt, "attn_fwd" if ph == "fwd" else "attn_bwd_dkdv")],
+                         4)}
                 for ph in ("fwd", "bwd")}
             res["kernels"] = {}
             esz = 2 if dt == "bf16" else 4
@@ -297,6 +298,8 @@ def main():
     if not args.no_rope and not args.only_step:
         line["rope_packed"] = rope_section(cfg, dtypes, args, stream, log)
 
+    if not args.no_configs and not args.only_step:
+        line["configs"] = configs_section(args, log)
     if not args.no_torch and not args.only_step:
         line["torch_sdpa"] = torch_sdpa_section(cfg, args, log)
 
@@ -341,24 +344,11 @@ def torch_sdpa_section(cfg, args, log) -> dict:
                     o = fwd()
                     torch.autograd.grad(o, (q, k, v), do)
 
-                def timed(fn, steps, warmup):
-                    for _ in range(warmup):
-                        fn()
-                    torch.cuda.synchronize()
-                    e0 = torch.cuda.Event(enable_timing=True)
-                    e1 = torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    for _ in range(steps):
-                        fn()
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    return e0.elapsed_time(e1) / steps
-
                 log(f"[bench] torch sdpa {dt} ({backend.name})")
                 n = min(args.steps, 200)
                 with torch.no_grad():
-                    ms_f = timed(fwd, n, 20)
-                ms_s = timed(step, n, 20)
+                    ms_f = timed_events(fwd, n, 20, stream)
+                ms_s = timed_events(step, n, 20, stream)
             rec.update({"fwd_us": round(ms_f * 1e3, 2), "fwd_bwd_us": round(ms_s * 1e3, 2),
                         "fwd_bwd_tflops": round(cfg.flops["fwd_bwd"] / (ms_s * 1e-3) / 1e12, 3)})
         except Exception as e:  # a backend this build lacks: say so
@@ -383,6 +373,115 @@ def visible_pairs(w, kv_len) -> int:
     return total * w.heads
 
 
+def timed_events(fn, steps, warmup, stream):
+    """ms per call of fn: warmup calls, then steps calls between two events
+    on `stream`, synchronised on both sides."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def timed_graph(fn, per_graph=20, replays=30):
+    """ms per call of fn from replays of a HIP graph of per_graph calls (no
+    host launch cost between calls); fn launches on the current stream."""
+    import torch
+    for _ in range(per_graph):
+        fn()
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for _ in range(per_graph):
+            fn()
+    for _ in range(3):
+        gr.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del gr
+    return e0.elapsed_time(e1) / (replays * per_graph)
+
+
+def configs_section(args, log) -> dict:
+    """fwd, bwd and fwd+bwd of every self-attention workload (tiny, small
+    decoder, decoder step, long context, ragged encoder) in each of its
+    contracts, GPU time from HIP-graph replays (eager calls with --no-graph):
+    credited TFLOP/s, its fraction of the contract's dense MFMA peak, and the
+    compulsory HBM bytes (every input read once, every output written once)
+    per second."""
+    import torch
+    import attention_forward_backward_amd as afb
+    from attention_forward_backward_amd import synth
+
+    out = {}
+    for name, cfg in synth.CONFIGS.items():
+        B, H, S, D = cfg.shape
+        T, L = B * H * S * D, B * H * S
+        rec = {"shape": f"B{B} H{H} S{S} D{D} {'causal' if cfg.causal else 'non-causal'}",
+               "visible_pairs": cfg.pairs}
+        for dt in cfg.dtypes:
+            inp = synth.config_inputs(cfg, args.seed, dt)
+
+            def dev(n):
+                if dt == "bf16":
+                    return torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+                return torch.from_numpy(inp[n]).cuda()
+
+            q, k, v, do = (dev(n) for n in ("q", "k", "v", "do"))
+            o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+            lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+            code = afb.ATTN_BF16 if dt == "bf16" else afb.ATTN_F32
+            ws = torch.empty(afb.attn_bwd_workspace_size(code, B, H, S, D, cfg.causal),
+                             dtype=torch.uint8, device="cuda")
+
+            def fwd():
+                afb.attn_fwd(q, k, v, o, lse, cfg.causal, cfg.scale, None)
+
+            def bwd():
+                afb.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, cfg.causal, cfg.scale, None)
+
+            def step():
+                fwd()
+                bwd()
+
+            log(f"[bench] configs {name} {rec['shape']} dtype={dt}")
+            step()
+            if args.no_graph:
+                tm = lambda fn: timed_events(fn, args.steps, 3, torch.cuda.current_stream())
+            else:
+                tm = timed_graph
+            ms = {"fwd": tm(fwd), "bwd": tm(bwd), "fwd_bwd": tm(step)}
+            esz = 2 if dt == "bf16" else 4
+            nbytes = {"fwd": 4 * T * esz + 4 * L, "bwd": 8 * T * esz + 4 * L}
+            nbytes["fwd_bwd"] = nbytes["fwd"] + nbytes["bwd"]
+            peak = PEAK_TFLOPS["bf16" if dt == "bf16" else "f32"]
+            r = {}
+            for ph in ("fwd", "bwd", "fwd_bwd"):
+                tf = cfg.flops[ph] / (ms[ph] * 1e-3) / 1e12
+                r[ph] = {"us": round(ms[ph] * 1e3, 2), "tflops": round(tf, 3),
+                         "frac_of_mfma_peak": round(tf / peak, 4),
+                         "compulsory_bytes": nbytes[ph],
+                         "gbs": round(nbytes[ph] / (ms[ph] * 1e-3) / 1e9, 1)}
+            rec[dt] = r
+            del q, k, v, do, o, dq, dk, dv, lse, ws
+            torch.cuda.empty_cache()
+        out[name] = rec
+    return out
+
+
 def cross_section(dtypes, args, stream, log) -> dict:
     """fwd and fwd+bwd time of the cross-attention and one-token workloads
     (attn_fwd_cross / attn_bwd_cross), per arithmetic contract: from replays
@@ -393,40 +492,7 @@ def cross_section(dtypes, args, stream, log) -> dict:
     from attention_forward_backward_amd import synth
 
     def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-
-    def timed_graph(fn, per_graph=20, replays=30):
-        """Per-call time of fn from replays of a HIP graph of per_graph calls
-        (no host launch cost between calls)."""
-        for _ in range(per_graph):
-            fn()
-        torch.cuda.synchronize()
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for _ in range(per_graph):
-                fn()
-        for _ in range(3):
-            gr.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(replays):
-            gr.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        del gr
-        return e0.elapsed_time(e1) / (replays * per_graph)
+        return timed_events(fn, steps, warmup, stream)
 
     out = {}
     for wname, w in synth.CROSS_WORKLOADS.items():

@@ -103,8 +103,9 @@ attn_status_t attn_fwd(attn_dtype_t dtype,
  *   2. dS transposed, [B*H][Sp][Sp] with Sp = ceil(S/128)*128, in the
  *      element type, which lets dQ be computed as one GEMM dS K instead of
  *      recomputing the scores (the dS path);
- *   3. only for shapes with few (key tile, head) pairs -- fewer than 256,
- *      e.g. many queries over few keys -- float32 partial sums of dK and dV
+ *   3. only for shapes with few (key tile, head) pairs -- fewer than 512
+ *      with float32 tensors, 256 with bf16 (64-key tiles), e.g. many queries
+ *      over few keys, or few long heads -- float32 partial sums of dK and dV
  *      over chunks of the queries, [2][C][B*H][S][D] with C chunks chosen
  *      from the shape alone (each chunk is then its own work item and the
  *      chunks are added up in a fixed order, so results stay deterministic).
