@@ -91,6 +91,12 @@ def test_workspace_size():
     assert wfull(0, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4 + 8 * 12 * 512 * 512 * 4
     assert wfull(1, 8, 12, 512, 64, True) == 2 * 8 * 12 * 512 * 4 + 8 * 12 * 512 * 512 * 2
     assert wfull(0, 32, 8, 197, 64, False) == r256(2 * 32 * 8 * 197 * 4) + r256(32 * 8 * 256 * 256 * 4)
+    # few long heads (B1 H16 S1024 D128 causal: 16 x 16 = 256 (key tile, head)
+    # pairs): with f32 tensors the dK, dV partials of a 2-chunk query split
+    # follow dS^T; bf16 keeps the unsplit backward
+    assert wfull(0, 1, 16, 1024, 128, True) == (2 * 16 * 1024 * 4 + 16 * 1024 * 1024 * 4
+                                                + 2 * 2 * 16 * 1024 * 128 * 4)
+    assert wfull(1, 1, 16, 1024, 128, True) == 2 * 16 * 1024 * 4 + 16 * 1024 * 1024 * 2
     # the practical contract (bf16 forward operands, strict f32 backward) sizes as f32
     assert wfull(2, 8, 12, 512, 64, True) == wfull(0, 8, 12, 512, 64, True)
     assert wmin(2, 32, 8, 197, 64, False) == wmin(0, 32, 8, 197, 64, False)
