@@ -42,6 +42,20 @@ def to_host(t) -> np.ndarray:
     return t.detach().float().cpu().numpy()
 
 
+def workspace_bytes(ws_mode: str, code: int, shape, causal: bool) -> int:
+    """Backward workspace for a mode: "full" the recommended size (dS^T, so dQ
+    is a GEMM, plus the dK, dV partials of the query split where the shape
+    takes it); "min" the minimum (dQ recomputes the scores, no split);
+    "ds_only" the minimum plus dS^T; "split_only" the recommended size less
+    dS^T (the query split with dQ recomputed)."""
+    B, H, S, D = shape
+    rec = afb.attn_bwd_workspace_size(code, B, H, S, D, causal)
+    mn = afb.attn_bwd_workspace_size_min(code, B, H, S, D, causal)
+    sp = (S + 127) // 128 * 128
+    ds = (B * H * sp * sp * (2 if code == afb.ATTN_BF16 else 4) + 255) // 256 * 256
+    return {"full": rec, "min": mn, "ds_only": mn + ds, "split_only": rec - ds}[ws_mode]
+
+
 def gpu_fwd_bwd(inp: dict, shape, dtype: str, causal: bool, scale: float, guard: int = 0,
                 fill=float("nan"), ws_mode: str = "full"):
     """Run attn_fwd then attn_bwd (fed the GPU's own O and LSE).
@@ -65,9 +79,7 @@ def gpu_fwd_bwd(inp: dict, shape, dtype: str, causal: bool, scale: float, guard:
         bufs[name] = out((B, H, S, D), tdt)
     bufs["lse"] = out((B, H, S), torch.float32)
     code = afb.ATTN_BF16 if dtype == "bf16" else afb.ATTN_F32
-    # "full": room for dS (dQ as a GEMM); "min": dQ recomputes the scores
-    wsf = afb.attn_bwd_workspace_size if ws_mode == "full" else afb.attn_bwd_workspace_size_min
-    ws_bytes = wsf(code, B, H, S, D, causal)
+    ws_bytes = workspace_bytes(ws_mode, code, shape, causal)
     ws = torch.full((ws_bytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
     t = {k_: v_[1] for k_, v_ in bufs.items()}
     afb.attn_fwd(dev["q"], dev["k"], dev["v"], t["o"], t["lse"], causal, scale)

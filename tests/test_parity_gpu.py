@@ -5,8 +5,9 @@ backward is fed the GPU forward's own O and LSE (the pipeline is gated)."""
 import numpy as np
 import pytest
 
+import attention_forward_backward_amd as afb
 from attention_forward_backward_amd import synth
-from parity_util import TOL, compare, gpu_fwd_bwd, max_rel_err, note, run_case
+from parity_util import TOL, compare, gpu_fwd_bwd, max_rel_err, note, run_case, workspace_bytes
 
 pytestmark = pytest.mark.gpu
 
@@ -156,3 +157,21 @@ def test_paths_agree():
         for n in ("o", "lse", "dk", "dv"):
             assert np.array_equal(hf[n], hm[n]), n
         assert max_rel_err(hf["dq"], hm["dq"]) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 16, 1024, 128), "f32"), ((1, 4, 1024, 64), "bf16")])
+@pytest.mark.parametrize("ws", ["full", "ds_only", "split_only"])
+def test_few_long_heads_workspace_paths(shape, dtype, ws):
+    """Few long causal heads take the query-chunk split of dK+dV (with f32
+    tensors the long-context workload itself; with bf16 below 256 (key tile,
+    head) items): every workspace layout that selects or skips the split and
+    the dS path gives the oracle's result within the contract's gate."""
+    B, H, S, D = shape
+    code = afb.ATTN_BF16 if dtype == "bf16" else afb.ATTN_F32
+    rec = afb.attn_bwd_workspace_size(code, B, H, S, D, True)
+    assert rec > workspace_bytes("ds_only", code, shape, True)  # the split's partials are there
+    errs, host, *_ = run_case(shape, 0, dtype, True, 1.0 / np.sqrt(D), guard=64, ws_mode=ws)
+    for name, e in errs.items():
+        assert e <= TOL[dtype], f"{name}: {e:.3e} > {TOL[dtype]} (workspace {ws})"
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        assert host[name + "_guard_ok"], f"{name}: guard band written"
