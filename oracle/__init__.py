@@ -8,3 +8,5 @@ from .attention import (attention_backward, attention_forward,  # noqa: F401
 from .fdcheck import fd_full, fd_grad  # noqa: F401
 from .rope import (gather_rows, rope, rope_angles_1d, rope_angles_axial,  # noqa: F401
                    rope_transpose, scatter_rows)
+from .conv import (conv2d_backward_data, conv2d_backward_filter,  # noqa: F401
+                   conv2d_forward, conv2d_loss, out_size)
