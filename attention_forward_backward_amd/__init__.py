@@ -16,12 +16,14 @@ __all__ = ["AttnError", "lib", "attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bw
            "attn_bwd_dq", "attn_bwd_workspace_size", "attn_bwd_workspace_size_min",
            "attn_fwd_cross", "attn_bwd_cross", "attn_bwd_cross_workspace_size",
            "attn_bwd_cross_workspace_size_min",
-           "attn_status_string", "attn_version",
+           "attn_status_string", "attn_version", "conv2d_fwd", "conv2d_bwd_data",
+           "conv2d_bwd_filter", "conv2d_bwd_filter_workspace_size", "conv2d_out_size",
            "ATTN_F32", "ATTN_BF16", "ATTN_F32_BF16FWD", "STATUS", "LIB_PATH", "HEADER_PATH"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "attn.h")
+CONV_HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "conv.h")
 
 ATTN_F32, ATTN_BF16, ATTN_F32_BF16FWD = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED",
@@ -57,6 +59,10 @@ _SIGS = {
     "attn_rope_copy": (_I, [_I, _P, ctypes.POINTER(ctypes.c_longlong), _P,
                             ctypes.POINTER(ctypes.c_longlong), _P, _P, _I, _I, _I, _I, _I, _I,
                             _I, _P]),
+    "conv2d_fwd": (_I, [_I, _P, _P, _P] + [_I] * 11 + [_P]),
+    "conv2d_bwd_data": (_I, [_I, _P, _P, _P] + [_I] * 11 + [_P]),
+    "conv2d_bwd_filter_workspace_size": (_Z, [_I] * 12),
+    "conv2d_bwd_filter": (_I, [_I, _P, _P, _P, _P, _Z] + [_I] * 11 + [_P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_version": (ctypes.c_char_p, []),
 }
@@ -80,10 +86,14 @@ def lib() -> ctypes.CDLL:
 
 
 def declared_symbols() -> list[str]:
-    """Function names declared in include/attn.h."""
-    with open(HEADER_PATH) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attn_\w+)\s*\(", text, re.M)))
+    """Function names declared in include/attn.h and include/conv.h."""
+    names = set()
+    for path in (HEADER_PATH, CONV_HEADER_PATH):
+        with open(path) as f:
+            text = f.read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?((?:attn|conv2d)_\w+)\s*\(",
+                                text, re.M))
+    return sorted(names)
 
 
 def attn_status_string(code: int) -> str:
@@ -402,3 +412,65 @@ def attn_rope_copy(src, src_offset: int, src_strides, dst, dst_offset: int, dst_
                                 rows, int(pos_offset), B, H, S, D, int(bool(transpose)),
                                 _stream(stream))
     _raise("attn_rope_copy", code)
+
+
+# ---------------------------------------------------------------- convolution (include/conv.h)
+def conv2d_out_size(height: int, width: int, kh: int, kw: int, stride, pad) -> tuple:
+    """(P, Q) of the convolution output (rounded down)."""
+    return ((height + 2 * pad[0] - kh) // stride[0] + 1, (width + 2 * pad[1] - kw) // stride[1] + 1)
+
+
+def _conv_dims(x_shape, w_shape, stride, pad) -> list:
+    N, H, W, C = x_shape
+    K, R, S, C2 = w_shape
+    if C != C2:
+        raise ValueError(f"x has {C} channels, w {C2}")
+    return [N, H, W, C, K, R, S, int(stride[0]), int(stride[1]), int(pad[0]), int(pad[1])]
+
+
+def conv2d_fwd(x, w, y, stride=(1, 1), pad=(0, 0), stream=None) -> None:
+    """y [N,P,Q,K] = conv(x [N,H,W,C], w [K,R,S,C]) (include/conv.h)."""
+    dims = _conv_dims(x.shape, w.shape, stride, pad)
+    P, Q = conv2d_out_size(dims[1], dims[2], dims[5], dims[6], stride, pad)
+    _check({"x": x}, x.shape, x.dtype)
+    _check({"w": w}, w.shape, x.dtype)
+    _check({"y": y}, (dims[0], P, Q, dims[4]), x.dtype)
+    _raise("conv2d_fwd", lib().conv2d_fwd(_dtype_code(x), x.data_ptr(), w.data_ptr(),
+                                          y.data_ptr(), *dims, _stream(stream)))
+
+
+def conv2d_bwd_data(dy, w, dx, stride=(1, 1), pad=(0, 0), stream=None) -> None:
+    """dx [N,H,W,C] from dy [N,P,Q,K] and w [K,R,S,C] (include/conv.h)."""
+    dims = _conv_dims(dx.shape, w.shape, stride, pad)
+    P, Q = conv2d_out_size(dims[1], dims[2], dims[5], dims[6], stride, pad)
+    _check({"dx": dx}, dx.shape, dx.dtype)
+    _check({"w": w}, w.shape, dx.dtype)
+    _check({"dy": dy}, (dims[0], P, Q, dims[4]), dx.dtype)
+    _raise("conv2d_bwd_data", lib().conv2d_bwd_data(_dtype_code(dx), dy.data_ptr(), w.data_ptr(),
+                                                    dx.data_ptr(), *dims, _stream(stream)))
+
+
+def conv2d_bwd_filter_workspace_size(dtype: int, x_shape, w_shape, stride=(1, 1),
+                                     pad=(0, 0)) -> int:
+    return int(lib().conv2d_bwd_filter_workspace_size(dtype, *_conv_dims(x_shape, w_shape,
+                                                                           stride, pad)))
+
+
+def conv2d_bwd_filter(x, dy, dw, workspace, stride=(1, 1), pad=(0, 0), stream=None) -> None:
+    """dw [K,R,S,C] from x [N,H,W,C] and dy [N,P,Q,K]; workspace: a device
+    tensor of at least conv2d_bwd_filter_workspace_size bytes, or None when
+    that size is 0 (include/conv.h)."""
+    dims = _conv_dims(x.shape, dw.shape, stride, pad)
+    P, Q = conv2d_out_size(dims[1], dims[2], dims[5], dims[6], stride, pad)
+    _check({"x": x}, x.shape, x.dtype)
+    _check({"dw": dw}, dw.shape, x.dtype)
+    _check({"dy": dy}, (dims[0], P, Q, dims[4]), x.dtype)
+    if workspace is None:
+        wp, wb = 0, 0
+    else:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        wp, wb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _raise("conv2d_bwd_filter", lib().conv2d_bwd_filter(_dtype_code(x), x.data_ptr(),
+                                                        dy.data_ptr(), dw.data_ptr(), wp, wb,
+                                                        *dims, _stream(stream)))

@@ -389,6 +389,6 @@ const char* attn_status_string(attn_status_t s) {
   return "unknown status";
 }
 
-const char* attn_version(void) { return "0.5.0"; }
+const char* attn_version(void) { return "0.6.0"; }
 
 }  // extern "C"

@@ -1,0 +1,333 @@
+// conv_igemm.hip -- 2-D convolution and its two derivatives as implicit
+// GEMMs on the MFMA units (gfx950), and their C ABI (include/conv.h).
+//
+// "Meganeura: Portable GPU Training and Inference through Vulkan and Metal"
+// (arXiv 2608.01563): convolution is a graph node with local input and weight
+// derivatives (Section 3.1), lowered to implicit-GEMM kernels (Section 3.3);
+// its weight-gradient, small weight-gradient and input-gradient kernels were
+// most of a ResNet-50 training step (Section 7.3).  The operation is the
+// deep-learning cross-correlation with zero padding and a stride, NHWC:
+//   y[n,p,q,k]  = sum_{r,s,c} x[n, p*sh+r-ph, q*sw+s-pw, c] w[k,r,s,c]
+//   dx[n,h,w,c] = sum_{p,q,r,s,k : p*sh+r-ph = h, q*sw+s-pw = w} dy[n,p,q,k] w[k,r,s,c]
+//   dw[k,r,s,c] = sum_{n,p,q} dy[n,p,q,k] x[n, p*sh+r-ph, q*sw+s-pw, c]
+// Each is one GEMM out[M][NC] = sum_kk A[m][kk] B[kk][j] whose operands are
+// gathered from the tensors on the fly (no im2col buffer):
+//   forward      M = N*P*Q (n,p,q)  NC = K          KD = R*S*C (r,s,c)
+//                A = x at the tap's input pixel, B[kk][k] = w[k][kk]
+//   data grad    M = N*H*W (n,h,w)  NC = C          KD = R*S*K (r,s,k)
+//                A = dy at the output pixel that tap (r,s) maps onto (h,w),
+//                zero where none does (stride), B[kk][c] = w[k,r,s,c]
+//   filter grad  M = K              NC = R*S*C      KD = N*P*Q (n,p,q)
+//                A[k][kk] = dy[kk][k], B[kk][(r,s,c)] = x at the tap's pixel
+// so the output is row-major [M][NC] in every case: y [N,P,Q,K], dx
+// [N,H,W,C], dw [K,R,S,C].  The filter gradient's reduction (N*P*Q) is long
+// and its output small, so it is split over gridDim.z slices whose float32
+// partials a second kernel adds in slice order (deterministic).
+//
+// Work split: a workgroup of 4 waves computes a 64 x 64 output tile, wave
+// (wm, wn) one 32 x 32 MFMA block.  The reduction runs in chunks of KC
+// values: every thread gathers its share of the A and B chunk into
+// registers (the next chunk's loads are in flight while the current chunk
+// is multiplied out of LDS), then stores them to LDS as rows of the output
+// index with the reduction index contiguous, which is the operand layout of
+// both MFMA shapes (strict f32: one value per lane and k-step; bf16: eight).
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "attn.h"
+#include "attn_device.hpp"
+#include "conv.h"
+
+namespace attn {
+
+enum ConvMode { CONV_FWD = 0, CONV_DATA = 1, CONV_FILTER = 2 };
+
+struct ConvShape {
+  int N, H, W, C, K, R, S, P, Q, sh, sw, ph, pw;
+  int M, NC, KD;  // the GEMM's rows, columns and reduction length
+};
+
+constexpr int CT = 64;  // output tile rows and columns
+constexpr int KC = 32;  // reduction values per chunk
+constexpr int PER = CT * KC / 256;  // values of one operand per thread per chunk
+
+// A[m][kk] of the GEMM (zero outside the tensors and past KD).
+template <class T, int MODE>
+__device__ inline float a_val(const T* __restrict__ a, const ConvShape& s, int m, int kk) {
+  if (m >= s.M || kk >= s.KD) return 0.f;
+  if constexpr (MODE == CONV_FWD) {
+    const int q = m % s.Q, t = m / s.Q, p = t % s.P, n = t / s.P;
+    const int c = kk % s.C, u = kk / s.C, ss = u % s.S, r = u / s.S;
+    const int ih = p * s.sh + r - s.ph, iw = q * s.sw + ss - s.pw;
+    if (ih < 0 || ih >= s.H || iw < 0 || iw >= s.W) return 0.f;
+    return (float)a[(((size_t)n * s.H + ih) * s.W + iw) * s.C + c];
+  } else if constexpr (MODE == CONV_DATA) {
+    const int w = m % s.W, t = m / s.W, h = t % s.H, n = t / s.H;
+    const int k = kk % s.K, u = kk / s.K, ss = u % s.S, r = u / s.S;
+    const int ph = h + s.ph - r, pw = w + s.pw - ss;  // p*sh and q*sw
+    if (ph < 0 || pw < 0 || ph % s.sh != 0 || pw % s.sw != 0) return 0.f;
+    const int p = ph / s.sh, q = pw / s.sw;
+    if (p >= s.P || q >= s.Q) return 0.f;
+    return (float)a[(((size_t)n * s.P + p) * s.Q + q) * s.K + k];
+  } else {
+    return (float)a[(size_t)kk * s.K + m];  // dy[(n,p,q)][k]
+  }
+}
+
+// B[kk][j] of the GEMM (zero outside the tensors and past KD).
+template <class T, int MODE>
+__device__ inline float b_val(const T* __restrict__ b, const ConvShape& s, int kk, int j) {
+  if (j >= s.NC || kk >= s.KD) return 0.f;
+  if constexpr (MODE == CONV_FWD) {
+    return (float)b[(size_t)j * s.KD + kk];  // w[k][(r,s,c)]
+  } else if constexpr (MODE == CONV_DATA) {
+    const int k = kk % s.K, u = kk / s.K;  // u = r*S + s
+    return (float)b[((size_t)k * s.R * s.S + u) * s.C + j];  // w[k,r,s,c]
+  } else {
+    const int q = kk % s.Q, t = kk / s.Q, p = t % s.P, n = t / s.P;
+    const int c = j % s.C, u = j / s.C, ss = u % s.S, r = u / s.S;
+    const int ih = p * s.sh + r - s.ph, iw = q * s.sw + ss - s.pw;
+    if (ih < 0 || ih >= s.H || iw < 0 || iw >= s.W) return 0.f;
+    return (float)b[(((size_t)n * s.H + ih) * s.W + iw) * s.C + c];
+  }
+}
+
+template <class E, int MODE>
+__global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __restrict__ A,
+                                                         const typename E::T* __restrict__ B,
+                                                         typename E::T* __restrict__ out,
+                                                         float* __restrict__ part, int kspan,
+                                                         const ConvShape s) {
+  // out (or, with part != null, part[blockIdx.z]) = A B over the reduction
+  // range [blockIdx.z * kspan, min(KD, +kspan)) for the 64 x 64 tile
+  // (blockIdx.y, blockIdx.x).
+  using T = typename E::T;
+  constexpr int LDK = KC + (is_bf16<E>() ? 8 : 1);  // padded LDS row (bf16: 16-byte reads)
+  __shared__ __attribute__((aligned(16))) T As[CT * LDK];
+  __shared__ __attribute__((aligned(16))) T Bs[CT * LDK];
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, h = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wv >> 1, wn = wv & 1;
+  const int m0 = blockIdx.y * CT, j0 = blockIdx.x * CT;
+  const int k0 = blockIdx.z * kspan, k1 = min(s.KD, k0 + kspan);
+  // Gather pattern: the filter gradient walks the output index fastest (its
+  // A and B rows are contiguous along it); the others the reduction index.
+  auto slot = [&](int i, int& row, int& kk) __attribute__((always_inline)) {
+    const int e = i * 256 + tid;
+    if constexpr (MODE == CONV_FILTER) {
+      row = e % CT;
+      kk = e / CT;
+    } else {
+      row = e / KC;
+      kk = e % KC;
+    }
+  };
+  float ra[PER], rb[PER];
+  auto gather = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int row, kk;
+      slot(i, row, kk);
+      const int g = kc + kk;
+      const bool in = g < k1;
+      ra[i] = in ? a_val<T, MODE>(A, s, m0 + row, g) : 0.f;
+      rb[i] = in ? b_val<T, MODE>(B, s, g, j0 + row) : 0.f;
+    }
+  };
+  f32x16 acc = zero16();
+  gather(k0);
+  for (int kc = k0; kc < k1; kc += KC) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int row, kk;
+      slot(i, row, kk);
+      As[row * LDK + kk] = (T)ra[i];
+      Bs[row * LDK + kk] = (T)rb[i];
+    }
+    __syncthreads();
+    if (kc + KC < k1) gather(kc + KC);  // in flight during the products below
+    const T* ar = As + (wm * 32 + n) * LDK;
+    const T* br = Bs + (wn * 32 + n) * LDK;
+    if constexpr (is_bf16<E>()) {
+#pragma unroll
+      for (int t = 0; t < KC / 16; ++t) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ar + 16 * t + 8 * h);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(br + 16 * t + 8 * h);
+        acc = E::mma(a, b, acc);
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < KC / 2; ++t) acc = E::mma(ar[2 * t + h], br[2 * t + h], acc);
+    }
+    __syncthreads();
+  }
+  // element r: row m0 + 32 wm + out_row(r, h), column j0 + 32 wn + n
+  const int j = j0 + wn * 32 + n;
+  if (j >= s.NC) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + wm * 32 + out_row(r, h);
+    if (m < s.M) {
+      if (part != nullptr)
+        part[((size_t)blockIdx.z * s.M + m) * s.NC + j] = acc[r];
+      else
+        out[(size_t)m * s.NC + j] = (T)acc[r];
+    }
+  }
+}
+
+// out[i] = sum over the z slices of part[z][i], in slice order.
+template <class T>
+__global__ __launch_bounds__(256) void conv_split_reduce_kernel(const float* __restrict__ part,
+                                                                T* __restrict__ out, int total,
+                                                                int nz) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  float v = 0.f;
+  for (int z = 0; z < nz; ++z) v += part[(size_t)z * total + i];
+  out[i] = (T)v;
+}
+
+}  // namespace attn
+
+namespace {
+
+using attn::ConvShape;
+
+// Reduction slices of the filter gradient: enough 64 x 64 tiles x slices to
+// fill the chip (about 1024 workgroups), each slice at least 512 long.
+int filter_slices(const ConvShape& s) {
+  const long long tiles = (long long)((s.M + 63) / 64) * ((s.NC + 63) / 64);
+  long long z = (1024 + tiles - 1) / tiles;
+  z = std::min<long long>(z, (s.KD + 511) / 512);
+  return (int)std::max<long long>(1, std::min<long long>(z, 256));
+}
+
+// Checks the shape and fills s; false on any invalid value.
+bool make_shape(int N, int H, int W, int C, int K, int R, int S, int sh, int sw, int ph, int pw,
+                ConvShape& s) {
+  if (N <= 0 || H <= 0 || W <= 0 || C <= 0 || K <= 0 || R <= 0 || S <= 0) return false;
+  if (sh <= 0 || sw <= 0 || ph < 0 || pw < 0) return false;
+  const long long P = ((long long)H + 2LL * ph - R) / sh + 1;
+  const long long Q = ((long long)W + 2LL * pw - S) / sw + 1;
+  if ((long long)H + 2LL * ph < R || (long long)W + 2LL * pw < S || P <= 0 || Q <= 0) return false;
+  const long long lim = 1LL << 31;
+  // every tensor and every GEMM extent indexed in 32 bits
+  if ((long long)N * H * W * C >= lim || (long long)K * R * S * C >= lim ||
+      (long long)N * P * Q * K >= lim || (long long)N * P * Q >= lim)
+    return false;
+  s = ConvShape{N, H, W, C, K, R, S, (int)P, (int)Q, sh, sw, ph, pw, 0, 0, 0};
+  return true;
+}
+
+template <class E, int MODE>
+hipError_t launch(const void* a, const void* b, void* out, float* part, int nz, ConvShape s,
+                  hipStream_t st) {
+  using T = typename E::T;
+  if (MODE == attn::CONV_FWD) {
+    s.M = s.N * s.P * s.Q; s.NC = s.K; s.KD = s.R * s.S * s.C;
+  } else if (MODE == attn::CONV_DATA) {
+    s.M = s.N * s.H * s.W; s.NC = s.C; s.KD = s.R * s.S * s.K;
+  } else {
+    s.M = s.K; s.NC = s.R * s.S * s.C; s.KD = s.N * s.P * s.Q;
+  }
+  const int kspan = ((s.KD + nz - 1) / nz + attn::KC - 1) / attn::KC * attn::KC;
+  dim3 grid((s.NC + 63) / 64, (s.M + 63) / 64, nz);
+  hipLaunchKernelGGL((attn::conv_igemm_kernel<E, MODE>), grid, dim3(256), 0, st, (const T*)a,
+                     (const T*)b, (T*)out, part, kspan, s);
+  if (part != nullptr) {
+    const int total = s.M * s.NC;
+    hipLaunchKernelGGL((attn::conv_split_reduce_kernel<T>), dim3((total + 255) / 256), dim3(256),
+                       0, st, (const float*)part, (T*)out, total, nz);
+  }
+  return hipGetLastError();
+}
+
+attn_status_t status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t conv2d_fwd(attn_dtype_t dtype, const void* x, const void* w, void* y, int batch,
+                         int height, int width, int channels, int filters, int kh, int kw,
+                         int stride_h, int stride_w, int pad_h, int pad_w, void* stream) {
+  ConvShape s;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!x || !w || !y) return ATTN_ERR_INVALID_ARG;
+  const size_t es = dtype == ATTN_BF16 ? 2 : 4;
+  if (!aligned(x, es) || !aligned(w, es) || !aligned(y, es)) return ATTN_ERR_INVALID_ARG;
+  if (!make_shape(batch, height, width, channels, filters, kh, kw, stride_h, stride_w, pad_h,
+                  pad_w, s))
+    return ATTN_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return status(dtype == ATTN_BF16
+                    ? launch<attn::EBF16, attn::CONV_FWD>(x, w, y, nullptr, 1, s, st)
+                    : launch<attn::EF32, attn::CONV_FWD>(x, w, y, nullptr, 1, s, st));
+}
+
+attn_status_t conv2d_bwd_data(attn_dtype_t dtype, const void* dy, const void* w, void* dx,
+                              int batch, int height, int width, int channels, int filters,
+                              int kh, int kw, int stride_h, int stride_w, int pad_h, int pad_w,
+                              void* stream) {
+  ConvShape s;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!dy || !w || !dx) return ATTN_ERR_INVALID_ARG;
+  const size_t es = dtype == ATTN_BF16 ? 2 : 4;
+  if (!aligned(dy, es) || !aligned(w, es) || !aligned(dx, es)) return ATTN_ERR_INVALID_ARG;
+  if (!make_shape(batch, height, width, channels, filters, kh, kw, stride_h, stride_w, pad_h,
+                  pad_w, s))
+    return ATTN_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return status(dtype == ATTN_BF16
+                    ? launch<attn::EBF16, attn::CONV_DATA>(dy, w, dx, nullptr, 1, s, st)
+                    : launch<attn::EF32, attn::CONV_DATA>(dy, w, dx, nullptr, 1, s, st));
+}
+
+size_t conv2d_bwd_filter_workspace_size(attn_dtype_t dtype, int batch, int height, int width,
+                                        int channels, int filters, int kh, int kw, int stride_h,
+                                        int stride_w, int pad_h, int pad_w) {
+  ConvShape s;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return 0;
+  if (!make_shape(batch, height, width, channels, filters, kh, kw, stride_h, stride_w, pad_h,
+                  pad_w, s))
+    return 0;
+  s.M = s.K; s.NC = s.R * s.S * s.C; s.KD = s.N * s.P * s.Q;
+  const int nz = filter_slices(s);
+  return nz > 1 ? ((size_t)nz * s.M * s.NC * sizeof(float) + 255) / 256 * 256 : 0;
+}
+
+attn_status_t conv2d_bwd_filter(attn_dtype_t dtype, const void* x, const void* dy, void* dw,
+                                void* workspace, size_t workspace_bytes, int batch, int height,
+                                int width, int channels, int filters, int kh, int kw,
+                                int stride_h, int stride_w, int pad_h, int pad_w, void* stream) {
+  ConvShape s;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (!x || !dy || !dw) return ATTN_ERR_INVALID_ARG;
+  const size_t es = dtype == ATTN_BF16 ? 2 : 4;
+  if (!aligned(x, es) || !aligned(dy, es) || !aligned(dw, es)) return ATTN_ERR_INVALID_ARG;
+  if (!make_shape(batch, height, width, channels, filters, kh, kw, stride_h, stride_w, pad_h,
+                  pad_w, s))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = conv2d_bwd_filter_workspace_size(dtype, batch, height, width, channels,
+                                                       filters, kh, kw, stride_h, stride_w,
+                                                       pad_h, pad_w);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 16)))
+    return ATTN_ERR_WORKSPACE;
+  ConvShape g = s;
+  g.M = g.K; g.NC = g.R * g.S * g.C; g.KD = g.N * g.P * g.Q;
+  const int nz = need > 0 ? filter_slices(g) : 1;
+  float* part = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return status(dtype == ATTN_BF16
+                    ? launch<attn::EBF16, attn::CONV_FILTER>(dy, x, dw, part, nz, s, st)
+                    : launch<attn::EF32, attn::CONV_FILTER>(dy, x, dw, part, nz, s, st));
+}
+
+}  // extern "C"

@@ -236,3 +236,28 @@ def cross_inputs(shape_q, shape_k, seed: int, dtype: str = "f32") -> dict:
         out.update({n + "_bits": qi[n + "_bits"] for n in ("q", "do")})
         out.update({n + "_bits": ki[n + "_bits"] for n in ("k", "v")})
     return out
+
+
+# Convolution inputs: x [N,H,W,C], w [K,R,S,C] and dy [N,P,Q,K] from streams
+# of their own.
+CONV_TENSOR_IDS = {"x": 20, "w": 21, "dy": 22}
+
+
+def conv_inputs(x_shape, w_shape, dy_shape, seed: int, dtype: str = "f32") -> dict:
+    """x, w, dy ~ N(0, 1) as float32 arrays holding the exact values the GPU
+    sees (bf16-rounded for ``dtype == "bf16"``, with the raw bits under
+    "<name>_bits"); w is drawn with sigma 1/sqrt(R*S*C), so that y is of
+    unit size."""
+    K, R, S, C = w_shape
+    out = {}
+    for name, shape in (("x", x_shape), ("w", w_shape), ("dy", dy_shape)):
+        sigma = 1.0 / math.sqrt(R * S * C) if name == "w" else 1.0
+        x = normal_f32(seed, CONV_TENSOR_IDS[name], shape, sigma)
+        if dtype == "bf16":
+            bits = f32_to_bf16_bits(x)
+            out[name + "_bits"] = bits
+            x = bf16_bits_to_f32(bits)
+        elif dtype != "f32":
+            raise ValueError(f"unknown dtype {dtype!r}")
+        out[name] = x
+    return out

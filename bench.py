@@ -85,6 +85,10 @@ def parse():
                    help="skip timing the five self-attention workloads (configs key)")
     p.add_argument("--configs-only", action="store_true",
                    help="time only the five self-attention workloads")
+    p.add_argument("--no-conv", action="store_true",
+                   help="skip timing the convolution entry points (conv key)")
+    p.add_argument("--conv-only", action="store_true",
+                   help="time only the convolution entry points")
     p.add_argument("--no-torch", action="store_true",
                    help="skip timing torch's own scaled_dot_product_attention (context)")
     p.add_argument("--torch-only", action="store_true",
@@ -170,6 +174,9 @@ def main():
         return
     if args.configs_only:
         print(json.dumps({"configs": configs_section(args, log)}), flush=True)
+        return
+    if args.conv_only:
+        print(json.dumps({"conv": conv_section(args, log)}), flush=True)
         return
 
     results = {}
@@ -300,6 +307,8 @@ def main():
 
     if not args.no_configs and not args.only_step:
         line["configs"] = configs_section(args, log)
+    if not args.no_conv and not args.only_step:
+        line["conv"] = conv_section(args, log)
     if not args.no_torch and not args.only_step:
         line["torch_sdpa"] = torch_sdpa_section(cfg, args, log)
 
@@ -477,6 +486,63 @@ def configs_section(args, log) -> dict:
                          "gbs": round(nbytes[ph] / (ms[ph] * 1e-3) / 1e9, 1)}
             rec[dt] = r
             del q, k, v, do, o, dq, dk, dv, lse, ws
+            torch.cuda.empty_cache()
+        out[name] = rec
+    return out
+
+
+# ResNet-50 convolutions at batch 32 and 224 x 224 input (the pages' ResNet-50
+# workload; its batch and image size are not given): name -> (N, H, W, C, K,
+# R, S, stride, pad).
+CONV_LAYERS = {
+    "stem_7x7_s2": (32, 224, 224, 3, 64, 7, 7, (2, 2), (3, 3)),
+    "conv2_3x3": (32, 56, 56, 64, 64, 3, 3, (1, 1), (1, 1)),
+    "conv4_1x1": (32, 14, 14, 1024, 256, 1, 1, (1, 1), (0, 0)),
+}
+
+
+def conv_section(args, log) -> dict:
+    """Forward, data derivative and filter derivative of three ResNet-50
+    convolutions (include/conv.h), strict f32 and bf16: time per call from
+    HIP events over back-to-back calls, TFLOP/s (2 N P Q K R S C per call)
+    and its fraction of the contract's dense MFMA peak."""
+    import torch
+    import attention_forward_backward_amd as afb
+    from attention_forward_backward_amd import synth
+
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, (N, H, W, C, K, R, S, st, pd) in CONV_LAYERS.items():
+        P, Q = afb.conv2d_out_size(H, W, R, S, st, pd)
+        flop = 2 * N * P * Q * K * R * S * C
+        rec = {"shape": f"N{N} {H}x{W} C{C} K{K} {R}x{S} stride {st[0]} pad {pd[0]}",
+               "flop_per_call": flop}
+        for dt in ("f32", "bf16"):
+            inp = synth.conv_inputs((N, H, W, C), (K, R, S, C), (N, P, Q, K), args.seed, dt)
+
+            def dev(n):
+                if dt == "bf16":
+                    return torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+                return torch.from_numpy(inp[n]).cuda()
+
+            x, w, dy = dev("x"), dev("w"), dev("dy")
+            y, dx, dw = torch.empty_like(dy), torch.empty_like(x), torch.empty_like(w)
+            code = afb.ATTN_BF16 if dt == "bf16" else afb.ATTN_F32
+            wsb = afb.conv2d_bwd_filter_workspace_size(code, x.shape, w.shape, st, pd)
+            ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+            calls = {"fwd": lambda: afb.conv2d_fwd(x, w, y, st, pd),
+                     "bwd_data": lambda: afb.conv2d_bwd_data(dy, w, dx, st, pd),
+                     "bwd_filter": lambda: afb.conv2d_bwd_filter(x, dy, dw, ws, st, pd)}
+            log(f"[bench] conv {name} {rec['shape']} dtype={dt}")
+            peak = PEAK_TFLOPS["bf16" if dt == "bf16" else "f32"]
+            r = {}
+            for op, fn in calls.items():
+                ms = timed_events(fn, 20, 3, stream)
+                tf = flop / (ms * 1e-3) / 1e12
+                r[op] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 2),
+                         "frac_of_mfma_peak": round(tf / peak, 4)}
+            rec[dt] = r
+            del x, w, dy, y, dx, dw, ws
             torch.cuda.empty_cache()
         out[name] = rec
     return out

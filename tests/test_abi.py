@@ -20,10 +20,12 @@ def test_library_loads_and_exports_header_symbols():
                              "attn_bwd_workspace_size_min", "attn_fwd_cross", "attn_bwd_cross",
                              "attn_bwd_cross_workspace_size", "attn_bwd_cross_workspace_size_min",
                              "attn_rope_copy", "attn_fwd_strided", "attn_bwd_strided",
-                             "attn_status_string", "attn_version"}
+                             "attn_status_string", "attn_version", "conv2d_fwd",
+                             "conv2d_bwd_data", "conv2d_bwd_filter",
+                             "conv2d_bwd_filter_workspace_size"}
     for name in declared:
         assert hasattr(L, name), name
-    assert afb.attn_version() == "0.5.0"
+    assert afb.attn_version() == "0.6.0"
     for code in range(5):
         assert afb.attn_status_string(code) not in ("", "unknown status")
     assert afb.attn_status_string(99) == "unknown status"
@@ -202,3 +204,32 @@ def test_strided_validation():
     mq = bhsd + [S * D, 0, D] * 2
     assert _bwds(mq + bhsd * 2 + bshd + [S * D, 0, D] * 2) == 1
     assert _bwds(mq + bhsd * 5, wsb=16) == 3                       # workspace still checked
+
+
+def _conv(fn, dtype=0, a=FAKE, b=FAKE, out=FAKE, dims=(2, 8, 8, 4, 6, 3, 3, 1, 1, 1, 1)):
+    return getattr(afb.lib(), fn)(dtype, a, b, out, *dims, None)
+
+
+def test_conv_validation():
+    L = afb.lib()
+    for fn in ("conv2d_fwd", "conv2d_bwd_data"):
+        assert _conv(fn, dtype=5) == 2                               # unknown dtype
+        assert _conv(fn, dtype=2) == 2                               # practical: not a conv contract
+        assert _conv(fn, a=None) == 1 and _conv(fn, out=None) == 1   # null pointers
+        assert _conv(fn, a=FAKE + 2) == 1                            # f32 needs 4-byte alignment
+        bad = [(0, 8, 8, 4, 6, 3, 3, 1, 1, 1, 1),    # empty batch
+               (2, 8, 8, 4, 6, 3, 3, 0, 1, 1, 1),    # zero stride
+               (2, 8, 8, 4, 6, 3, 3, 1, 1, -1, 1),   # negative padding
+               (2, 2, 8, 4, 6, 5, 3, 1, 1, 1, 1),    # filter taller than the padded image
+               (1 << 16, 256, 256, 4, 6, 3, 3, 1, 1, 1, 1)]  # x beyond 2^31 elements
+        for d in bad:
+            assert _conv(fn, dims=d) == 1, (fn, d)
+    ws = L.conv2d_bwd_filter_workspace_size
+    # small reductions take one slice and need no workspace; long ones split
+    assert ws(0, 1, 4, 4, 2, 3, 3, 3, 1, 1, 1, 1) == 0
+    big = (32, 56, 56, 64, 64, 3, 3, 1, 1, 1, 1)
+    n32, n16 = ws(0, *big), ws(1, *big)
+    assert n32 > 0 and n32 % 256 == 0 and n32 % (64 * 576 * 4) == 0 and n16 == n32
+    assert ws(5, *big) == 0 and ws(0, 0, 56, 56, 64, 64, 3, 3, 1, 1, 1, 1) == 0
+    args = lambda wsp, wsb: L.conv2d_bwd_filter(0, FAKE, FAKE, FAKE, wsp, wsb, *big, None)
+    assert args(None, n32) == 3 and args(FAKE, n32 - 256) == 3 and args(FAKE + 8, n32) == 3
