@@ -46,9 +46,35 @@ namespace attn {
 
 enum ConvMode { CONV_FWD = 0, CONV_DATA = 1, CONV_FILTER = 2 };
 
+// Division of indices below 2^31 by an invariant divisor d >= 1 as a
+// multiply-high, add and shift (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l.  The
+// sum stays below 2^32 because n < 2^31.
+struct FastDiv {
+  unsigned d, m;
+  int l;
+  __host__ static FastDiv make(unsigned d) {
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const unsigned m = (unsigned)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    return FastDiv{d, m, l};
+  }
+  __device__ inline int div(int n) const {
+    return (int)((__umulhi((unsigned)n, m) + (unsigned)n) >> l);
+  }
+  // n = q d + r with 0 <= r < d
+  __device__ inline int divmod(int n, int& r) const {
+    const int q = div(n);
+    r = n - q * (int)d;
+    return q;
+  }
+};
+
 struct ConvShape {
   int N, H, W, C, K, R, S, P, Q, sh, sw, ph, pw;
   int M, NC, KD;  // the GEMM's rows, columns and reduction length
+  FastDiv dC, dK, dS, dP, dQ, dH, dW, dsh, dsw;
 };
 
 constexpr int CT = 64;  // output tile rows and columns
@@ -60,18 +86,21 @@ template <class T, int MODE>
 __device__ inline float a_val(const T* __restrict__ a, const ConvShape& s, int m, int kk) {
   if (m >= s.M || kk >= s.KD) return 0.f;
   if constexpr (MODE == CONV_FWD) {
-    const int q = m % s.Q, t = m / s.Q, p = t % s.P, n = t / s.P;
-    const int c = kk % s.C, u = kk / s.C, ss = u % s.S, r = u / s.S;
+    int q, p, c, ss;
+    const int n = s.dP.divmod(s.dQ.divmod(m, q), p);
+    const int r = s.dS.divmod(s.dC.divmod(kk, c), ss);
     const int ih = p * s.sh + r - s.ph, iw = q * s.sw + ss - s.pw;
     if (ih < 0 || ih >= s.H || iw < 0 || iw >= s.W) return 0.f;
     return (float)a[(((size_t)n * s.H + ih) * s.W + iw) * s.C + c];
   } else if constexpr (MODE == CONV_DATA) {
-    const int w = m % s.W, t = m / s.W, h = t % s.H, n = t / s.H;
-    const int k = kk % s.K, u = kk / s.K, ss = u % s.S, r = u / s.S;
+    int w, h, k, ss;
+    const int n = s.dH.divmod(s.dW.divmod(m, w), h);
+    const int r = s.dS.divmod(s.dK.divmod(kk, k), ss);
     const int ph = h + s.ph - r, pw = w + s.pw - ss;  // p*sh and q*sw
-    if (ph < 0 || pw < 0 || ph % s.sh != 0 || pw % s.sw != 0) return 0.f;
-    const int p = ph / s.sh, q = pw / s.sw;
-    if (p >= s.P || q >= s.Q) return 0.f;
+    if (ph < 0 || pw < 0) return 0.f;
+    int rh, rw;
+    const int p = s.dsh.divmod(ph, rh), q = s.dsw.divmod(pw, rw);
+    if (rh != 0 || rw != 0 || p >= s.P || q >= s.Q) return 0.f;
     return (float)a[(((size_t)n * s.P + p) * s.Q + q) * s.K + k];
   } else {
     return (float)a[(size_t)kk * s.K + m];  // dy[(n,p,q)][k]
@@ -85,11 +114,13 @@ __device__ inline float b_val(const T* __restrict__ b, const ConvShape& s, int k
   if constexpr (MODE == CONV_FWD) {
     return (float)b[(size_t)j * s.KD + kk];  // w[k][(r,s,c)]
   } else if constexpr (MODE == CONV_DATA) {
-    const int k = kk % s.K, u = kk / s.K;  // u = r*S + s
+    int k;
+    const int u = s.dK.divmod(kk, k);  // u = r*S + s
     return (float)b[((size_t)k * s.R * s.S + u) * s.C + j];  // w[k,r,s,c]
   } else {
-    const int q = kk % s.Q, t = kk / s.Q, p = t % s.P, n = t / s.P;
-    const int c = j % s.C, u = j / s.C, ss = u % s.S, r = u / s.S;
+    int q, p, c, ss;
+    const int n = s.dP.divmod(s.dQ.divmod(kk, q), p);
+    const int r = s.dS.divmod(s.dC.divmod(j, c), ss);
     const int ih = p * s.sh + r - s.ph, iw = q * s.sw + ss - s.pw;
     if (ih < 0 || ih >= s.H || iw < 0 || iw >= s.W) return 0.f;
     return (float)b[(((size_t)n * s.H + ih) * s.W + iw) * s.C + c];
@@ -220,7 +251,13 @@ bool make_shape(int N, int H, int W, int C, int K, int R, int S, int sh, int sw,
   if ((long long)N * H * W * C >= lim || (long long)K * R * S * C >= lim ||
       (long long)N * P * Q * K >= lim || (long long)N * P * Q >= lim)
     return false;
-  s = ConvShape{N, H, W, C, K, R, S, (int)P, (int)Q, sh, sw, ph, pw, 0, 0, 0};
+  s = ConvShape{N, H, W, C, K, R, S, (int)P, (int)Q, sh, sw, ph, pw, 0, 0, 0, {}, {}, {}, {}, {}, {},
+                {}, {}, {}};
+  using attn::FastDiv;
+  s.dC = FastDiv::make(C); s.dK = FastDiv::make(K); s.dS = FastDiv::make(S);
+  s.dP = FastDiv::make((unsigned)P); s.dQ = FastDiv::make((unsigned)Q);
+  s.dH = FastDiv::make(H); s.dW = FastDiv::make(W);
+  s.dsh = FastDiv::make(sh); s.dsw = FastDiv::make(sw);
   return true;
 }
 
