@@ -211,16 +211,26 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
   }
 }
 
-// out[i] = sum over the z slices of part[z][i], in slice order.
+// out[i] = sum over the z slices of part[z][i] in a fixed order: eight
+// running sums over the slices z = u (mod 8), added pairwise at the end, so
+// that eight independent loads are in flight per thread (deterministic).
 template <class T>
 __global__ __launch_bounds__(256) void conv_split_reduce_kernel(const float* __restrict__ part,
                                                                 T* __restrict__ out, int total,
                                                                 int nz) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= total) return;
-  float v = 0.f;
-  for (int z = 0; z < nz; ++z) v += part[(size_t)z * total + i];
-  out[i] = (T)v;
+  const float* p = part + i;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int z = 0;
+  for (; z + 8 <= nz; z += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] += p[(size_t)(z + u) * total];
+  }
+#pragma unroll
+  for (int u = 0; u < 7; ++u)
+    if (z + u < nz) a[u] += p[(size_t)(z + u) * total];
+  out[i] = (T)(((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])));
 }
 
 }  // namespace attn
