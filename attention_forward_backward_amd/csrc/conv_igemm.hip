@@ -127,7 +127,64 @@ __device__ inline float b_val(const T* __restrict__ b, const ConvShape& s, int k
   }
 }
 
-template <class E, int MODE>
+// How an operand is gathered: one element per load, or 16-byte vectors of
+// V = 16 / sizeof(T) consecutive elements along the reduction index (the
+// channels of x and dy, the rows of w) or along the output index (the
+// channels of w in the data derivative, dy and x in the filter derivative).  The host takes a vector gather only where
+// every group of V is contiguous and 16-byte aligned (channel counts and
+// reduction lengths multiples of V, aligned base pointers).
+enum Gather { G_SCALAR = 0, G_ALONG_K = 1, G_ALONG_ROW = 2 };
+
+// The V values of operand WHICH (0: A, 1: B) at output index row (the first
+// of V rows with G_ALONG_ROW) and reduction index kk (the first of V with
+// G_ALONG_K), zero outside the tensors: one index decomposition, one load.
+template <class T, int MODE, int WHICH>
+__device__ inline u32x4 vec_val(const T* __restrict__ src, const ConvShape& s, int row, int kk) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  if (kk >= s.KD) return zero;
+  if constexpr (WHICH == 0 && MODE == CONV_FWD) {  // x channels c .. c+V-1 of the tap's pixel
+    if (row >= s.M) return zero;
+    int q, p, c, ss;
+    const int n = s.dP.divmod(s.dQ.divmod(row, q), p);
+    const int r = s.dS.divmod(s.dC.divmod(kk, c), ss);
+    const int ih = p * s.sh + r - s.ph, iw = q * s.sw + ss - s.pw;
+    if (ih < 0 || ih >= s.H || iw < 0 || iw >= s.W) return zero;
+    return *reinterpret_cast<const u32x4*>(src + (((size_t)n * s.H + ih) * s.W + iw) * s.C + c);
+  } else if constexpr (WHICH == 1 && MODE == CONV_FWD) {  // w[k][kk .. kk+V-1]
+    if (row >= s.NC) return zero;
+    return *reinterpret_cast<const u32x4*>(src + (size_t)row * s.KD + kk);
+  } else if constexpr (WHICH == 0 && MODE == CONV_DATA) {  // dy channels k .. k+V-1
+    if (row >= s.M) return zero;
+    int w, h, k, ss;
+    const int n = s.dH.divmod(s.dW.divmod(row, w), h);
+    const int r = s.dS.divmod(s.dK.divmod(kk, k), ss);
+    const int ph = h + s.ph - r, pw = w + s.pw - ss;
+    if (ph < 0 || pw < 0) return zero;
+    int rh, rw;
+    const int p = s.dsh.divmod(ph, rh), q = s.dsw.divmod(pw, rw);
+    if (rh != 0 || rw != 0 || p >= s.P || q >= s.Q) return zero;
+    return *reinterpret_cast<const u32x4*>(src + (((size_t)n * s.P + p) * s.Q + q) * s.K + k);
+  } else if constexpr (WHICH == 1 && MODE == CONV_DATA) {  // w[k, r, s, c .. c+V-1]
+    if (row >= s.NC) return zero;
+    int k;
+    const int u = s.dK.divmod(kk, k);  // u = r*S + s
+    return *reinterpret_cast<const u32x4*>(src + ((size_t)k * s.R * s.S + u) * s.C + row);
+  } else if constexpr (WHICH == 0 && MODE == CONV_FILTER) {  // dy[kk][k .. k+V-1]
+    if (row >= s.M) return zero;
+    return *reinterpret_cast<const u32x4*>(src + (size_t)kk * s.K + row);
+  } else {  // B of the filter derivative: x channels c .. c+V-1 of tap (r, s)
+    static_assert(WHICH == 1 && MODE == CONV_FILTER, "no vector gather for this operand");
+    if (row >= s.NC) return zero;
+    int q, p, c, ss;
+    const int n = s.dP.divmod(s.dQ.divmod(kk, q), p);
+    const int r = s.dS.divmod(s.dC.divmod(row, c), ss);
+    const int ih = p * s.sh + r - s.ph, iw = q * s.sw + ss - s.pw;
+    if (ih < 0 || ih >= s.H || iw < 0 || iw >= s.W) return zero;
+    return *reinterpret_cast<const u32x4*>(src + (((size_t)n * s.H + ih) * s.W + iw) * s.C + c);
+  }
+}
+
+template <class E, int MODE, int GA, int GB>
 __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __restrict__ A,
                                                          const typename E::T* __restrict__ B,
                                                          typename E::T* __restrict__ out,
@@ -135,8 +192,10 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
                                                          const ConvShape s) {
   // out (or, with part != null, part[blockIdx.z]) = A B over the reduction
   // range [blockIdx.z * kspan, min(KD, +kspan)) for the 64 x 64 tile
-  // (blockIdx.y, blockIdx.x).
+  // (blockIdx.y, blockIdx.x); GA, GB: how A and B are gathered (Gather).
   using T = typename E::T;
+  constexpr int V = 16 / (int)sizeof(T);            // elements per vector gather
+  constexpr int NV = CT * KC / V / 256;             // vector groups per thread per chunk
   constexpr int LDK = KC + (is_bf16<E>() ? 8 : 1);  // padded LDS row (bf16: 16-byte reads)
   __shared__ __attribute__((aligned(16))) T As[CT * LDK];
   __shared__ __attribute__((aligned(16))) T Bs[CT * LDK];
@@ -145,8 +204,9 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
   const int wm = wv >> 1, wn = wv & 1;
   const int m0 = blockIdx.y * CT, j0 = blockIdx.x * CT;
   const int k0 = blockIdx.z * kspan, k1 = min(s.KD, k0 + kspan);
-  // Gather pattern: the filter gradient walks the output index fastest (its
-  // A and B rows are contiguous along it); the others the reduction index.
+  // Element-gather pattern: the filter gradient walks the output index
+  // fastest (its A and B rows are contiguous along it); the others the
+  // reduction index.
   auto slot = [&](int i, int& row, int& kk) __attribute__((always_inline)) {
     const int e = i * 256 + tid;
     if constexpr (MODE == CONV_FILTER) {
@@ -157,28 +217,89 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
       kk = e % KC;
     }
   };
-  float ra[PER], rb[PER];
+  // Vector-group pattern (first row and reduction index of group g).
+  auto vslot = [&](int g, int mode, int& row, int& kk) __attribute__((always_inline)) {
+    const int e = g * 256 + tid;
+    if (mode == G_ALONG_K) {
+      row = e / (KC / V);
+      kk = (e % (KC / V)) * V;
+    } else {
+      kk = e / (CT / V);
+      row = (e % (CT / V)) * V;
+    }
+  };
+  float sa[GA == G_SCALAR ? PER : 1], sb[GB == G_SCALAR ? PER : 1];
+  u32x4 va[GA == G_SCALAR ? 1 : NV], vb[GB == G_SCALAR ? 1 : NV];
+  // (k1 and every group boundary are multiples of V on the vector paths, so
+  // a group is either wholly inside the chunk range or wholly outside)
   auto gather = [&](int kc) __attribute__((always_inline)) {
+    if constexpr (GA == G_SCALAR) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int row, kk;
-      slot(i, row, kk);
-      const int g = kc + kk;
-      const bool in = g < k1;
-      ra[i] = in ? a_val<T, MODE>(A, s, m0 + row, g) : 0.f;
-      rb[i] = in ? b_val<T, MODE>(B, s, g, j0 + row) : 0.f;
+      for (int i = 0; i < PER; ++i) {
+        int row, kk;
+        slot(i, row, kk);
+        sa[i] = kc + kk < k1 ? a_val<T, MODE>(A, s, m0 + row, kc + kk) : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < NV; ++g) {
+        int row, kk;
+        vslot(g, GA, row, kk);
+        va[g] = kc + kk < k1 ? vec_val<T, MODE, 0>(A, s, m0 + row, kc + kk) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if constexpr (GB == G_SCALAR) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        int row, kk;
+        slot(i, row, kk);
+        sb[i] = kc + kk < k1 ? b_val<T, MODE>(B, s, kc + kk, j0 + row) : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < NV; ++g) {
+        int row, kk;
+        vslot(g, GB, row, kk);
+        vb[g] = kc + kk < k1 ? vec_val<T, MODE, 1>(B, s, j0 + row, kc + kk) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  // The gathered chunk into LDS rows (output index) with the reduction index
+  // contiguous.
+  auto put = [&](T* dst, const float* sv, const u32x4* vv, auto modec) __attribute__((always_inline)) {
+    constexpr int mode = decltype(modec)::value;
+    if constexpr (mode == G_SCALAR) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        int row, kk;
+        slot(i, row, kk);
+        dst[row * LDK + kk] = (T)sv[i];
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < NV; ++g) {
+        int row, kk;
+        vslot(g, mode, row, kk);
+        if constexpr (mode == G_ALONG_K && is_bf16<E>()) {
+          *reinterpret_cast<u32x4*>(dst + row * LDK + kk) = vv[g];  // 16-byte aligned row part
+        } else {
+          const T* e = reinterpret_cast<const T*>(&vv[g]);
+#pragma unroll
+          for (int u = 0; u < V; ++u) {
+            if constexpr (mode == G_ALONG_K)
+              dst[row * LDK + kk + u] = e[u];
+            else
+              dst[(row + u) * LDK + kk] = e[u];
+          }
+        }
+      }
     }
   };
   f32x16 acc = zero16();
   gather(k0);
   for (int kc = k0; kc < k1; kc += KC) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int row, kk;
-      slot(i, row, kk);
-      As[row * LDK + kk] = (T)ra[i];
-      Bs[row * LDK + kk] = (T)rb[i];
-    }
+    put(As, sa, va, std::integral_constant<int, GA>{});
+    put(Bs, sb, vb, std::integral_constant<int, GB>{});
     __syncthreads();
     if (kc + KC < k1) gather(kc + KC);  // in flight during the products below
     const T* ar = As + (wm * 32 + n) * LDK;
@@ -271,10 +392,21 @@ bool make_shape(int N, int H, int W, int C, int K, int R, int S, int sh, int sw,
   return true;
 }
 
+template <class E, int MODE, int GA, int GB>
+void launch_g(const void* a, const void* b, void* out, float* part, int kspan, dim3 grid,
+              const ConvShape& s, hipStream_t st) {
+  using T = typename E::T;
+  hipLaunchKernelGGL((attn::conv_igemm_kernel<E, MODE, GA, GB>), grid, dim3(256), 0, st,
+                     (const T*)a, (const T*)b, (T*)out, part, kspan, s);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 template <class E, int MODE>
 hipError_t launch(const void* a, const void* b, void* out, float* part, int nz, ConvShape s,
                   hipStream_t st) {
   using T = typename E::T;
+  constexpr int V = 16 / (int)sizeof(T);
   if (MODE == attn::CONV_FWD) {
     s.M = s.N * s.P * s.Q; s.NC = s.K; s.KD = s.R * s.S * s.C;
   } else if (MODE == attn::CONV_DATA) {
@@ -284,8 +416,27 @@ hipError_t launch(const void* a, const void* b, void* out, float* part, int nz, 
   }
   const int kspan = ((s.KD + nz - 1) / nz + attn::KC - 1) / attn::KC * attn::KC;
   dim3 grid((s.NC + 63) / 64, (s.M + 63) / 64, nz);
-  hipLaunchKernelGGL((attn::conv_igemm_kernel<E, MODE>), grid, dim3(256), 0, st, (const T*)a,
-                     (const T*)b, (T*)out, part, kspan, s);
+  // Vector gathers where every group of V is contiguous and aligned.
+  using namespace attn;
+  if (MODE == CONV_FWD) {
+    const bool va = s.C % V == 0 && aligned16(a), vb = s.KD % V == 0 && aligned16(b);
+    if (va && vb) launch_g<E, CONV_FWD, G_ALONG_K, G_ALONG_K>(a, b, out, part, kspan, grid, s, st);
+    else if (va) launch_g<E, CONV_FWD, G_ALONG_K, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
+    else if (vb) launch_g<E, CONV_FWD, G_SCALAR, G_ALONG_K>(a, b, out, part, kspan, grid, s, st);
+    else launch_g<E, CONV_FWD, G_SCALAR, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
+  } else if (MODE == CONV_DATA) {
+    const bool va = s.K % V == 0 && aligned16(a), vb = s.C % V == 0 && aligned16(b);
+    if (va && vb) launch_g<E, CONV_DATA, G_ALONG_K, G_ALONG_ROW>(a, b, out, part, kspan, grid, s, st);
+    else if (va) launch_g<E, CONV_DATA, G_ALONG_K, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
+    else if (vb) launch_g<E, CONV_DATA, G_SCALAR, G_ALONG_ROW>(a, b, out, part, kspan, grid, s, st);
+    else launch_g<E, CONV_DATA, G_SCALAR, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
+  } else {
+    const bool va = s.K % V == 0 && aligned16(a), vb = s.C % V == 0 && aligned16(b);
+    if (va && vb) launch_g<E, CONV_FILTER, G_ALONG_ROW, G_ALONG_ROW>(a, b, out, part, kspan, grid, s, st);
+    else if (va) launch_g<E, CONV_FILTER, G_ALONG_ROW, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
+    else if (vb) launch_g<E, CONV_FILTER, G_SCALAR, G_ALONG_ROW>(a, b, out, part, kspan, grid, s, st);
+    else launch_g<E, CONV_FILTER, G_SCALAR, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
+  }
   if (part != nullptr) {
     const int total = s.M * s.NC;
     hipLaunchKernelGGL((attn::conv_split_reduce_kernel<T>), dim3((total + 255) / 256), dim3(256),
