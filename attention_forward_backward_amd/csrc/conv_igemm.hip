@@ -78,8 +78,18 @@ struct ConvShape {
 };
 
 constexpr int CT = 64;  // output tile rows and columns
-constexpr int KC = 32;  // reduction values per chunk
-constexpr int PER = CT * KC / 256;  // values of one operand per thread per chunk
+// Reduction values per chunk (between two workgroup barriers), per element
+// type: a bf16 MFMA consumes 16 per instruction, an f32 one 2.
+#ifndef ATTN_CONV_KC_F32
+#define ATTN_CONV_KC_F32 32
+#endif
+#ifndef ATTN_CONV_KC_BF16
+#define ATTN_CONV_KC_BF16 32
+#endif
+template <class E>
+__host__ __device__ constexpr int conv_kc() {
+  return is_bf16<E>() ? ATTN_CONV_KC_BF16 : ATTN_CONV_KC_F32;
+}
 
 // A[m][kk] of the GEMM (zero outside the tensors and past KD).
 template <class T, int MODE>
@@ -195,6 +205,8 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
   // (blockIdx.y, blockIdx.x); GA, GB: how A and B are gathered (Gather).
   using T = typename E::T;
   constexpr int V = 16 / (int)sizeof(T);            // elements per vector gather
+  constexpr int KC = conv_kc<E>();
+  constexpr int PER = CT * KC / 256;                // values of one operand per thread per chunk
   constexpr int NV = CT * KC / V / 256;             // vector groups per thread per chunk
   constexpr int LDK = KC + (is_bf16<E>() ? 8 : 1);  // padded LDS row (bf16: 16-byte reads)
   __shared__ __attribute__((aligned(16))) T As[CT * LDK];
@@ -414,7 +426,8 @@ hipError_t launch(const void* a, const void* b, void* out, float* part, int nz, 
   } else {
     s.M = s.K; s.NC = s.R * s.S * s.C; s.KD = s.N * s.P * s.Q;
   }
-  const int kspan = ((s.KD + nz - 1) / nz + attn::KC - 1) / attn::KC * attn::KC;
+  constexpr int KC = attn::conv_kc<E>();
+  const int kspan = ((s.KD + nz - 1) / nz + KC - 1) / KC * KC;
   dim3 grid((s.NC + 63) / 64, (s.M + 63) / 64, nz);
   // Vector gathers where every group of V is contiguous and aligned.
   using namespace attn;
