@@ -228,6 +228,7 @@ def main():
         res = {"ms_per_step": ms_step,
                "value": flops["fwd_bwd"] / (ms_step * 1e-3) / 1e12}
         if not args.only_step:
+            res["step_samples"] = step_samples(step, stream)
             ms = {"fwd": timed(fwd, args.steps, 3), "bwd": timed(bwd, args.steps, 3)}
             kern = {"attn_fwd": ms["fwd"], "attn_bwd_prep": timed(bwd_prep, args.steps, 3),
                     "attn_bwd_dkdv": timed(bwd_dkdv, args.steps, 3),
@@ -293,7 +294,7 @@ def main():
                    "backward_workspace": args.workspace},
         "kernel_sources": src_hash,
     }
-    for key in ("roofline", "phases", "kernels", "step_frac_of_mfma_peak"):
+    for key in ("roofline", "phases", "kernels", "step_frac_of_mfma_peak", "step_samples"):
         if key in results[head]:
             line[key] = results[head][key]
     for dt in dtypes[1:]:
@@ -397,6 +398,35 @@ def timed_events(fn, steps, warmup, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def step_samples(step, stream, n: int = 50, flush_bytes: int = 512 << 20) -> dict:
+    """Distribution of single-step times (HIP events around each step, one
+    synchronisation per sample): "warm" back to back, as in repeated
+    training steps (the working set stays in the 256 MB Infinity Cache), and
+    "flushed" with a 512 MB buffer written between samples, so the step
+    starts from HBM.  Median, quartiles, minimum and maximum in us."""
+    import torch
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    out = {}
+    for mode in ("warm", "flushed"):
+        t = []
+        for _ in range(n):
+            if mode == "flushed":
+                scratch.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e3)
+        q = np.percentile(t, [0, 25, 50, 75, 100])
+        out[mode] = {"median_us": round(float(q[2]), 2), "p25_us": round(float(q[1]), 2),
+                     "p75_us": round(float(q[3]), 2), "min_us": round(float(q[0]), 2),
+                     "max_us": round(float(q[4]), 2), "samples": n}
+    del scratch
+    return out
 
 
 def timed_graph(fn, per_graph=20, replays=30):
