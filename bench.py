@@ -458,9 +458,10 @@ def configs_section(args, log) -> dict:
     """fwd, bwd and fwd+bwd of every self-attention workload (tiny, small
     decoder, decoder step, long context, ragged encoder) in each of its
     contracts, GPU time from HIP-graph replays (eager calls with --no-graph):
-    credited TFLOP/s, its fraction of the contract's dense MFMA peak, and the
-    compulsory HBM bytes (every input read once, every output written once)
-    per second."""
+    credited TFLOP/s, its fraction of the contract's dense MFMA peak and of
+    the attainable roofline min(peak, FLOP per compulsory byte x 8 TB/s), and
+    the compulsory HBM bytes (every input read once, every output written
+    once) per second."""
     import torch
     import attention_forward_backward_amd as afb
     from attention_forward_backward_amd import synth
@@ -510,8 +511,12 @@ def configs_section(args, log) -> dict:
             r = {}
             for ph in ("fwd", "bwd", "fwd_bwd"):
                 tf = cfg.flops[ph] / (ms[ph] * 1e-3) / 1e12
+                # attainable: min(MFMA peak, arithmetic intensity x HBM peak)
+                attain = min(peak, cfg.flops[ph] / nbytes[ph] * PEAK_HBM_GBS / 1e3)
                 r[ph] = {"us": round(ms[ph] * 1e3, 2), "tflops": round(tf, 3),
                          "frac_of_mfma_peak": round(tf / peak, 4),
+                         "attainable_tflops": round(attain, 1),
+                         "frac_of_attainable": round(tf / attain, 4),
                          "compulsory_bytes": nbytes[ph],
                          "gbs": round(nbytes[ph] / (ms[ph] * 1e-3) / 1e9, 1)}
             rec[dt] = r
