@@ -86,6 +86,14 @@ constexpr int CT = 64;  // output tile rows and columns
 #ifndef ATTN_CONV_KC_BF16
 #define ATTN_CONV_KC_BF16 32
 #endif
+// Chunks gathered ahead of the one being multiplied (1 or 2).  On the
+// ResNet-50 layers of the benchmark two were slower everywhere but the bf16
+// 1x1 forward (3x3 f32 forward 98 -> 103 us, stem bf16 forward 174 -> 218;
+// 1x1 bf16 forward 21.7 -> 18.9), so one is the default.
+#ifndef ATTN_CONV_PREFETCH
+#define ATTN_CONV_PREFETCH 1
+#endif
+static_assert(ATTN_CONV_PREFETCH == 1 || ATTN_CONV_PREFETCH == 2, "prefetch depth 1 or 2");
 template <class E>
 __host__ __device__ constexpr int conv_kc() {
   return is_bf16<E>() ? ATTN_CONV_KC_BF16 : ATTN_CONV_KC_F32;
@@ -240,11 +248,18 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
       row = (e % (CT / V)) * V;
     }
   };
-  float sa[GA == G_SCALAR ? PER : 1], sb[GB == G_SCALAR ? PER : 1];
-  u32x4 va[GA == G_SCALAR ? 1 : NV], vb[GB == G_SCALAR ? 1 : NV];
+  // Register sets of gathered chunks (ATTN_CONV_PREFETCH chunks in flight).
+  constexpr int NS = ATTN_CONV_PREFETCH;
+  float sa_[NS][GA == G_SCALAR ? PER : 1], sb_[NS][GB == G_SCALAR ? PER : 1];
+  u32x4 va_[NS][GA == G_SCALAR ? 1 : NV], vb_[NS][GB == G_SCALAR ? 1 : NV];
   // (k1 and every group boundary are multiples of V on the vector paths, so
   // a group is either wholly inside the chunk range or wholly outside)
-  auto gather = [&](int kc) __attribute__((always_inline)) {
+  auto gather = [&](int kc, auto setc) __attribute__((always_inline)) {
+    constexpr int st = decltype(setc)::value;
+    float* sa = sa_[st];
+    float* sb = sb_[st];
+    u32x4* va = va_[st];
+    u32x4* vb = vb_[st];
     if constexpr (GA == G_SCALAR) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
@@ -308,12 +323,14 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
     }
   };
   f32x16 acc = zero16();
-  gather(k0);
-  for (int kc = k0; kc < k1; kc += KC) {
-    put(As, sa, va, std::integral_constant<int, GA>{});
-    put(Bs, sb, vb, std::integral_constant<int, GB>{});
+  // One chunk: its registers into LDS, the gather of the chunk NS ahead into
+  // the same registers, the products out of LDS.
+  auto chunk = [&](int kc, auto setc) __attribute__((always_inline)) {
+    constexpr int st = decltype(setc)::value;
+    put(As, sa_[st], va_[st], std::integral_constant<int, GA>{});
+    put(Bs, sb_[st], vb_[st], std::integral_constant<int, GB>{});
     __syncthreads();
-    if (kc + KC < k1) gather(kc + KC);  // in flight during the products below
+    if (kc + NS * KC < k1) gather(kc + NS * KC, setc);  // in flight during later chunks
     const T* ar = As + (wm * 32 + n) * LDK;
     const T* br = Bs + (wn * 32 + n) * LDK;
     if constexpr (is_bf16<E>()) {
@@ -328,6 +345,17 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
       for (int t = 0; t < KC / 2; ++t) acc = E::mma(ar[2 * t + h], br[2 * t + h], acc);
     }
     __syncthreads();
+  };
+  gather(k0, std::integral_constant<int, 0>{});
+  if constexpr (NS == 2) {
+    if (k0 + KC < k1) gather(k0 + KC, std::integral_constant<int, 1>{});
+    for (int kc = k0; kc < k1; kc += 2 * KC) {
+      chunk(kc, std::integral_constant<int, 0>{});
+      if (kc + KC >= k1) break;
+      chunk(kc + KC, std::integral_constant<int, NS - 1>{});
+    }
+  } else {
+    for (int kc = k0; kc < k1; kc += KC) chunk(kc, std::integral_constant<int, 0>{});
   }
   // element r: row m0 + 32 wm + out_row(r, h), column j0 + 32 wn + n
   const int j = j0 + wn * 32 + n;

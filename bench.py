@@ -361,7 +361,7 @@ def torch_sdpa_section(cfg, args, log) -> dict:
                 ms_s = timed_events(step, n, 20, stream)
             rec.update({"fwd_us": round(ms_f * 1e3, 2), "fwd_bwd_us": round(ms_s * 1e3, 2),
                         "fwd_bwd_tflops": round(cfg.flops["fwd_bwd"] / (ms_s * 1e-3) / 1e12, 3)})
-        except Exception as e:  # a backend this build lacks: say so
+        except Exception as e:  # a backend this torch lacks: say so
             rec["unavailable"] = f"{type(e).__name__}: {str(e)[:200]}"
         out[dt] = rec
         del q, k, v, do
