@@ -326,8 +326,10 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
 
 template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
 static hipError_t launch_gemm(const BwdArgs& a) {
-  constexpr int NW = 4, NSPLIT = 2, KPW = 1;
-  constexpr int NST = is_bf16<E>() ? 3 : 2;
+  constexpr int NW = is_bf16<E>() ? ATTN_DQG_NW_BF16 : ATTN_DQG_NW_F32;
+  constexpr int NSPLIT = is_bf16<E>() ? ATTN_DQG_NSPLIT_BF16 : ATTN_DQG_NSPLIT_F32;
+  constexpr int KPW = 1;
+  constexpr int NST = is_bf16<E>() ? ATTN_DQG_NST_BF16 : ATTN_DQG_NST_F32;
   using T = typename E::T;
   constexpr int BR = 32 * (NW / NSPLIT);
   const int nqt = (a.Sq + BR - 1) / BR;

@@ -88,6 +88,28 @@
 #ifndef ATTN_DKDV_NST_BF16
 #define ATTN_DKDV_NST_BF16 3
 #endif
+// The dQ GEMM (dS K with the stored dS^T): waves per workgroup, waves
+// sharing each 32-query block, LDS stages.  At B8 H12 S512 D64 causal the
+// f32 defaults took 23.4 us against 27.9 with 3 stages, 26.3 with 8 waves
+// and 29.5 without the split; bf16 measured the same with 2 stages as 3.
+#ifndef ATTN_DQG_NW_F32
+#define ATTN_DQG_NW_F32 4
+#endif
+#ifndef ATTN_DQG_NSPLIT_F32
+#define ATTN_DQG_NSPLIT_F32 2
+#endif
+#ifndef ATTN_DQG_NST_F32
+#define ATTN_DQG_NST_F32 2
+#endif
+#ifndef ATTN_DQG_NW_BF16
+#define ATTN_DQG_NW_BF16 4
+#endif
+#ifndef ATTN_DQG_NSPLIT_BF16
+#define ATTN_DQG_NSPLIT_BF16 2
+#endif
+#ifndef ATTN_DQG_NST_BF16
+#define ATTN_DQG_NST_BF16 3
+#endif
 // Workgroups per CU the f32 dK+dV kernel (D <= 64) must fit: 2 holds its
 // registers to 256, so two of its single-wave-per-SIMD workgroups share a CU.
 #ifndef ATTN_DKDV_MINW_F32
