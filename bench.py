@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import glob
 import json
+import math
 import os
 import sys
 import time
@@ -85,6 +86,10 @@ def parse():
                    help="skip timing the five self-attention workloads (configs key)")
     p.add_argument("--configs-only", action="store_true",
                    help="time only the five self-attention workloads")
+    p.add_argument("--no-scaling", action="store_true",
+                   help="skip the longer-sequence shapes (scaling key)")
+    p.add_argument("--scaling-only", action="store_true",
+                   help="time only the longer-sequence shapes")
     p.add_argument("--no-conv", action="store_true",
                    help="skip timing the convolution entry points (conv key)")
     p.add_argument("--conv-only", action="store_true",
@@ -177,6 +182,9 @@ def main():
         return
     if args.conv_only:
         print(json.dumps({"conv": conv_section(args, log)}), flush=True)
+        return
+    if args.scaling_only:
+        print(json.dumps({"scaling": scaling_section(args, log)}), flush=True)
         return
 
     results = {}
@@ -308,6 +316,8 @@ def main():
 
     if not args.no_configs and not args.only_step:
         line["configs"] = configs_section(args, log)
+    if not args.no_scaling and not args.only_step:
+        line["scaling"] = scaling_section(args, log)
     if not args.no_conv and not args.only_step:
         line["conv"] = conv_section(args, log)
     if not args.no_torch and not args.only_step:
@@ -520,6 +530,65 @@ def configs_section(args, log) -> dict:
                          "compulsory_bytes": nbytes[ph],
                          "gbs": round(nbytes[ph] / (ms[ph] * 1e-3) / 1e9, 1)}
             rec[dt] = r
+            del q, k, v, do, o, dq, dk, dv, lse, ws
+            torch.cuda.empty_cache()
+        out[name] = rec
+    return out
+
+
+# Longer sequences at the decoder-step token count (B*S = 4096) and one long
+# D128 head set: how the contracts' MFMA fractions grow with the work per
+# (query tile, head) item.  Timing only (the kernels and their parity are
+# those of the five workloads).
+SCALING_SHAPES = [(2, 12, 2048, 64), (1, 12, 4096, 64), (1, 16, 4096, 128)]
+
+
+def scaling_section(args, log) -> dict:
+    """fwd+bwd of causal self-attention at longer sequences, both contracts,
+    GPU time from HIP-graph replays (recommended workspace): credited
+    TFLOP/s (14 D per visible pair) and its fraction of the MFMA peak."""
+    import torch
+    import attention_forward_backward_amd as afb
+    from attention_forward_backward_amd import synth
+
+    out = {}
+    for (B, H, S, D) in SCALING_SHAPES:
+        name = f"B{B} H{H} S{S} D{D} causal"
+        pairs = B * H * S * (S + 1) // 2
+        rec = {"visible_pairs": pairs}
+        for dt in ("f32", "bf16"):
+            inp = synth.make_inputs((B, H, S, D), args.seed, dt)
+
+            def dev(n):
+                if dt == "bf16":
+                    return torch.from_numpy(inp[n + "_bits"].view(np.int16)).view(torch.bfloat16).cuda()
+                return torch.from_numpy(inp[n]).cuda()
+
+            q, k, v, do = (dev(n) for n in ("q", "k", "v", "do"))
+            o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+            lse = torch.empty((B, H, S), dtype=torch.float32, device="cuda")
+            code = afb.ATTN_BF16 if dt == "bf16" else afb.ATTN_F32
+            ws = torch.empty(afb.attn_bwd_workspace_size(code, B, H, S, D, True),
+                             dtype=torch.uint8, device="cuda")
+            sc = 1.0 / math.sqrt(D)
+
+            def fwd():
+                afb.attn_fwd(q, k, v, o, lse, True, sc, None)
+
+            def step():
+                fwd()
+                afb.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, True, sc, None)
+
+            log(f"[bench] scaling {name} dtype={dt}")
+            step()
+            ms_f, ms_s = timed_graph(fwd, 10, 10), timed_graph(step, 10, 10)
+            peak = PEAK_TFLOPS["bf16" if dt == "bf16" else "f32"]
+            tf_f = 4 * D * pairs / (ms_f * 1e-3) / 1e12
+            tf_s = 14 * D * pairs / (ms_s * 1e-3) / 1e12
+            rec[dt] = {"fwd_us": round(ms_f * 1e3, 1), "fwd_tflops": round(tf_f, 1),
+                       "fwd_frac_of_mfma_peak": round(tf_f / peak, 4),
+                       "fwd_bwd_us": round(ms_s * 1e3, 1), "fwd_bwd_tflops": round(tf_s, 1),
+                       "fwd_bwd_frac_of_mfma_peak": round(tf_s / peak, 4)}
             del q, k, v, do, o, dq, dk, dv, lse, ws
             torch.cuda.empty_cache()
         out[name] = rec
