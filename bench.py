@@ -86,9 +86,9 @@ def parse():
                    help="skip timing the five self-attention workloads (configs key)")
     p.add_argument("--configs-only", action="store_true",
                    help="time only the five self-attention workloads")
-    p.add_argument("--no-scaling", action="store_true",
-                   help="skip the longer-sequence shapes (scaling key)")
-    p.add_argument("--scaling-only", action="store_true",
+    p.add_argument("--no-long-seq", action="store_true",
+                   help="skip the longer-sequence shapes (long_seq key)")
+    p.add_argument("--long-seq-only", action="store_true",
                    help="time only the longer-sequence shapes")
     p.add_argument("--no-conv", action="store_true",
                    help="skip timing the convolution entry points (conv key)")
@@ -183,8 +183,8 @@ def main():
     if args.conv_only:
         print(json.dumps({"conv": conv_section(args, log)}), flush=True)
         return
-    if args.scaling_only:
-        print(json.dumps({"scaling": scaling_section(args, log)}), flush=True)
+    if args.long_seq_only:
+        print(json.dumps({"long_seq": scaling_section(args, log)}), flush=True)
         return
 
     results = {}
@@ -316,8 +316,8 @@ def main():
 
     if not args.no_configs and not args.only_step:
         line["configs"] = configs_section(args, log)
-    if not args.no_scaling and not args.only_step:
-        line["scaling"] = scaling_section(args, log)
+    if not args.no_long_seq and not args.only_step:
+        line["long_seq"] = scaling_section(args, log)
     if not args.no_conv and not args.only_step:
         line["conv"] = conv_section(args, log)
     if not args.no_torch and not args.only_step:
