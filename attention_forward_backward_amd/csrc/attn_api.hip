@@ -62,7 +62,8 @@ size_t ws_full_bytes(attn_dtype_t dtype, int batch, int heads, int sq, int sk) {
 // when the shape needs no split; the backward arithmetic is f32 unless the
 // tensors are bf16).
 size_t ws_part_bytes(attn_dtype_t dtype, int batch, int heads, int sq, int sk, int head_dim) {
-  const int nqs = attn::dkdv_query_chunks(dtype == ATTN_BF16, (long long)batch * heads, sq, sk);
+  const int nqs =
+      attn::dkdv_query_chunks(dtype == ATTN_BF16, (long long)batch * heads, sq, sk, head_dim);
   return nqs > 1 ? round256(2 * (size_t)nqs * batch * heads * sk * head_dim * sizeof(float)) : 0;
 }
 
@@ -96,7 +97,8 @@ attn::BwdArgs make_bwd(attn_dtype_t dtype, const void* q, const void* k, const v
   a.ds = full ? static_cast<char*>(ws) + wmin : nullptr;
   a.part = split ? reinterpret_cast<float*>(static_cast<char*>(ws) + (full ? wfull : wmin))
                  : nullptr;
-  a.nqs = split ? attn::dkdv_query_chunks(dtype == ATTN_BF16, (long long)batch * heads, sq, sk)
+  a.nqs = split ? attn::dkdv_query_chunks(dtype == ATTN_BF16, (long long)batch * heads, sq, sk,
+                                           head_dim)
                 : 1;
   a.SPq = ds_stride(sq); a.SPk = ds_stride(sk);
   a.BH = batch * heads; a.H = heads; a.Sq = sq; a.Sk = sk; a.D = head_dim;

@@ -441,17 +441,15 @@ __global__ __launch_bounds__(64) void bwd_dkdv_reduce_kernel(const float* __rest
 
 template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool QSPLIT, bool STR>
 static hipError_t launch(const BwdArgs& a) {
-  constexpr int NW = is_bf16<E>() ? ATTN_DKDV_NW_BF16 : ATTN_DKDV_NW_F32;
-  constexpr int NSPLIT = is_bf16<E>() ? ATTN_DKDV_NSPLIT_BF16 : ATTN_DKDV_NSPLIT_F32;
-  constexpr int KPW = is_bf16<E>() ? ATTN_DKDV_KPW_BF16 : ATTN_DKDV_KPW_F32;
-  constexpr int NST = is_bf16<E>() ? ATTN_DKDV_NST_BF16 : ATTN_DKDV_NST_F32;
+  constexpr LShape SH = dkdv_shape(is_bf16<E>(), D);
+  constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
   using T = typename E::T;
   constexpr auto kern =
       bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS, QSPLIT, STR>;
   const Layout lay = a.layout != nullptr ? *a.layout : Layout{};
   constexpr int BKV = 32 * (NW / NSPLIT);
   constexpr int BQ = 32 * NSPLIT * KPW;
-  static_assert(BKV == dkdv_key_tile(is_bf16<E>()) && BQ == dkdv_query_tile(is_bf16<E>()),
+  static_assert(BKV == dkdv_key_tile(is_bf16<E>(), D) && BQ == dkdv_query_tile(is_bf16<E>(), D),
                 "tile sizes of the query-chunk choice");
   const int nkt = (a.Sk + BKV - 1) / BKV;
   const int nqt = (a.Sq + BQ - 1) / BQ;

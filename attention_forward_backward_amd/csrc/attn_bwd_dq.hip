@@ -1,4 +1,4 @@
-// attn_bwd_dq.hip -- first backward kernel for gfx950: D and dQ.
+// attn_bwd_dq.hip -- the dQ stage of the attention backward for gfx950.
 //
 // The pages ("Meganeura: Portable GPU Training and Inference through Vulkan
 // and Metal", arXiv 2608.01563) lower the attention derivative to a dQ
@@ -326,10 +326,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
 
 template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
 static hipError_t launch_gemm(const BwdArgs& a) {
-  constexpr int NW = is_bf16<E>() ? ATTN_DQG_NW_BF16 : ATTN_DQG_NW_F32;
-  constexpr int NSPLIT = is_bf16<E>() ? ATTN_DQG_NSPLIT_BF16 : ATTN_DQG_NSPLIT_F32;
-  constexpr int KPW = 1;
-  constexpr int NST = is_bf16<E>() ? ATTN_DQG_NST_BF16 : ATTN_DQG_NST_F32;
+  constexpr LShape SH = dqg_shape(is_bf16<E>(), D);
+  constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
   using T = typename E::T;
   constexpr int BR = 32 * (NW / NSPLIT);
   const int nqt = (a.Sq + BR - 1) / BR;
@@ -343,10 +341,8 @@ static hipError_t launch_gemm(const BwdArgs& a) {
 
 template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
 static hipError_t launch(const BwdArgs& a) {
-  constexpr int NW = is_bf16<E>() ? ATTN_DQ_NW_BF16 : ATTN_DQ_NW_F32;
-  constexpr int NSPLIT = is_bf16<E>() ? ATTN_DQ_NSPLIT_BF16 : ATTN_DQ_NSPLIT_F32;
-  constexpr int KPW = is_bf16<E>() ? ATTN_DQ_KPW_BF16 : ATTN_DQ_KPW_F32;
-  constexpr int NST = is_bf16<E>() ? ATTN_DQ_NST_BF16 : ATTN_DQ_NST_F32;
+  constexpr LShape SH = dq_shape(is_bf16<E>(), D);
+  constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
   using T = typename E::T;
   constexpr int BR = 32 * (NW / NSPLIT);
   const int nqt = (a.Sq + BR - 1) / BR;

@@ -628,6 +628,18 @@ struct RegOperand<EF32B> : RegOperand<EBF16> {};
 // element e of the 8-byte row read of lane 4e + i/4, position i%4; so lanes
 // that read rows kbase + r/4, columns colbase + 4(r%4) .. +3 hand lane i
 // rows kbase .. kbase+3 of column colbase + i).
+// One transposed LDS read (ds_read_b64_tr_b16).  The pointer goes through a
+// __restrict__ parameter of an inlined function so that the read carries
+// alias-scope metadata: without any, the compiler's wait insertion assumes
+// it may read LDS that a direct global->LDS load still in flight writes,
+// and puts a vmcnt(0) before it, which also waits for every tile the ring
+// is prefetching.  The tile it reads has been waited for explicitly.
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __attribute__((always_inline)) inline s16x4 ds_read_tr(
+    const lds_s16x4* __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(p));
+}
+
 template <class E, int COLS>
 __device__ inline void read_kslot_operand(RegOperand<E>& X, const char* tile, int row0, int col0,
                                           int lane) {
@@ -644,8 +656,7 @@ __device__ inline void read_kslot_operand(RegOperand<E>& X, const char* tile, in
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int row = row0 + 16 * u + 8 * h + 4 * j + (r >> 2);
-        part[j] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(tile + TL::off(row, col)));
+        part[j] = ds_read_tr((const lds_s16x4*)(tile + TL::off(row, col)));
       }
       const s16x8 all = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
       X.v[u] = __builtin_bit_cast(bf16x8, all);

@@ -378,10 +378,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
 
 template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
 static hipError_t launch(const FwdArgs& a) {
-  constexpr int NW = is_bf16<E>() ? ATTN_FWD_NW_BF16 : ATTN_FWD_NW_F32;
-  constexpr int NSPLIT = is_bf16<E>() ? ATTN_FWD_NSPLIT_BF16 : ATTN_FWD_NSPLIT_F32;
-  constexpr int KPW = is_bf16<E>() ? ATTN_FWD_KPW_BF16 : ATTN_FWD_KPW_F32;
-  constexpr int NST = is_bf16<E>() ? ATTN_FWD_NST_BF16 : ATTN_FWD_NST_F32;
+  constexpr LShape SH = fwd_shape(is_bf16<E>(), D);
+  constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
   using T = typename E::T;
   constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR>;
   constexpr int BR = 32 * (NW / NSPLIT);

@@ -328,14 +328,54 @@ inline Sched make_sched(int G, int BH, const std::vector<int>& works) {
   return s;
 }
 
-// Tiles of the dK+dV kernel: keys per item, queries per staged tile.
-constexpr int dkdv_key_tile(bool bf16) {
-  return bf16 ? 32 * (ATTN_DKDV_NW_BF16 / ATTN_DKDV_NSPLIT_BF16)
-              : 32 * (ATTN_DKDV_NW_F32 / ATTN_DKDV_NSPLIT_F32);
+// Launch shape of one kernel for an element type and head_dim: NW waves per
+// workgroup, NSPLIT waves sharing each 32-row block, KPW 32-row blocks per
+// wave per staged tile, NST ring stages (the macros above).  head_dim-32
+// tiles hold half the bytes of head_dim-64 ones: with more than 4 waves or
+// 2-way splits a wave's share of a tile, or a merge's partials, would not
+// fill whole 1 KiB loads or one stage, so head_dim 32 keeps 4 waves, 2-way
+// splits and one block per wave.
+struct LShape {
+  int nw, nsplit, kpw, nst;
+};
+constexpr LShape small_d_shape(int nst) { return LShape{4, 2, 1, nst}; }
+constexpr LShape fwd_shape(bool bf16, int D) {
+  return bf16 ? (D < 64 ? small_d_shape(ATTN_FWD_NST_BF16)
+                        : LShape{ATTN_FWD_NW_BF16, ATTN_FWD_NSPLIT_BF16, ATTN_FWD_KPW_BF16,
+                                 ATTN_FWD_NST_BF16})
+              : (D < 64 ? small_d_shape(ATTN_FWD_NST_F32)
+                        : LShape{ATTN_FWD_NW_F32, ATTN_FWD_NSPLIT_F32, ATTN_FWD_KPW_F32,
+                                 ATTN_FWD_NST_F32});
 }
-constexpr int dkdv_query_tile(bool bf16) {
-  return bf16 ? 32 * ATTN_DKDV_NSPLIT_BF16 * ATTN_DKDV_KPW_BF16
-              : 32 * ATTN_DKDV_NSPLIT_F32 * ATTN_DKDV_KPW_F32;
+constexpr LShape dkdv_shape(bool bf16, int D) {
+  return bf16 ? (D < 64 ? small_d_shape(ATTN_DKDV_NST_BF16)
+                        : LShape{ATTN_DKDV_NW_BF16, ATTN_DKDV_NSPLIT_BF16, ATTN_DKDV_KPW_BF16,
+                                 ATTN_DKDV_NST_BF16})
+              : (D < 64 ? small_d_shape(ATTN_DKDV_NST_F32)
+                        : LShape{ATTN_DKDV_NW_F32, ATTN_DKDV_NSPLIT_F32, ATTN_DKDV_KPW_F32,
+                                 ATTN_DKDV_NST_F32});
+}
+constexpr LShape dq_shape(bool bf16, int D) {  // dQ with recomputed scores
+  return bf16 ? (D < 64 ? small_d_shape(ATTN_DQ_NST_BF16)
+                        : LShape{ATTN_DQ_NW_BF16, ATTN_DQ_NSPLIT_BF16, ATTN_DQ_KPW_BF16,
+                                 ATTN_DQ_NST_BF16})
+              : (D < 64 ? small_d_shape(ATTN_DQ_NST_F32)
+                        : LShape{ATTN_DQ_NW_F32, ATTN_DQ_NSPLIT_F32, ATTN_DQ_KPW_F32,
+                                 ATTN_DQ_NST_F32});
+}
+constexpr LShape dqg_shape(bool bf16, int D) {  // dQ GEMM over the stored dS^T
+  return bf16 ? (D < 64 ? small_d_shape(ATTN_DQG_NST_BF16)
+                        : LShape{ATTN_DQG_NW_BF16, ATTN_DQG_NSPLIT_BF16, 1, ATTN_DQG_NST_BF16})
+              : (D < 64 ? small_d_shape(ATTN_DQG_NST_F32)
+                        : LShape{ATTN_DQG_NW_F32, ATTN_DQG_NSPLIT_F32, 1, ATTN_DQG_NST_F32});
+}
+
+// Tiles of the dK+dV kernel: keys per item, queries per staged tile.
+constexpr int dkdv_key_tile(bool bf16, int D) {
+  return 32 * (dkdv_shape(bf16, D).nw / dkdv_shape(bf16, D).nsplit);
+}
+constexpr int dkdv_query_tile(bool bf16, int D) {
+  return 32 * dkdv_shape(bf16, D).nsplit * dkdv_shape(bf16, D).kpw;
 }
 
 // Query chunks of the dK+dV pass for a shape (a function of the shape
@@ -345,9 +385,9 @@ constexpr int dkdv_query_tile(bool bf16) {
 // cut into chunks of at least ATTN_DKDV_QCHUNK_MIN tiles, towards
 // ATTN_DKDV_SPLIT_TARGET items, and the chunks' partial sums are added up
 // afterwards.
-inline int dkdv_query_chunks(bool bf16, long long BH, int Sq, int Sk) {
-  const long long nkt = (Sk + dkdv_key_tile(bf16) - 1) / dkdv_key_tile(bf16);
-  const int nqt = (Sq + dkdv_query_tile(bf16) - 1) / dkdv_query_tile(bf16);
+inline int dkdv_query_chunks(bool bf16, long long BH, int Sq, int Sk, int D) {
+  const long long nkt = (Sk + dkdv_key_tile(bf16, D) - 1) / dkdv_key_tile(bf16, D);
+  const int nqt = (Sq + dkdv_query_tile(bf16, D) - 1) / dkdv_query_tile(bf16, D);
   const long long items = BH * nkt;
   if (items >= (bf16 ? ATTN_DKDV_SPLIT_BELOW_BF16 : ATTN_DKDV_SPLIT_BELOW_F32)) return 1;
   long long n = (ATTN_DKDV_SPLIT_TARGET + items - 1) / items;

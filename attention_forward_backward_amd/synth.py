@@ -261,3 +261,19 @@ def conv_inputs(x_shape, w_shape, dy_shape, seed: int, dtype: str = "f32") -> di
             raise ValueError(f"unknown dtype {dtype!r}")
         out[name] = x
     return out
+
+
+# Longer causal self-attention shapes the benchmark times beside the five
+# workloads: the decoder-step token count at S = 2048 and 4096, and a long
+# head_dim-128 set, (B, H, S, D).
+LONG_SEQ_SHAPES = [(2, 12, 2048, 64), (1, 12, 4096, 64), (1, 16, 4096, 128)]
+
+# ResNet-50 convolutions at batch 32 and 224 x 224 input (the pages' ResNet-50
+# workload; its batch and image size are not given): name -> (N, H, W, C, K,
+# R, S, stride, pad).  The stem's input is the image, which takes no
+# gradient, so it has no data derivative.
+CONV_LAYERS = {
+    "stem_7x7_s2": (32, 224, 224, 3, 64, 7, 7, (2, 2), (3, 3)),
+    "conv2_3x3": (32, 56, 56, 64, 64, 3, 3, (1, 1), (1, 1)),
+    "conv4_1x1": (32, 14, 14, 1024, 256, 1, 1, (1, 1), (0, 0)),
+}

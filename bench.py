@@ -94,10 +94,6 @@ def parse():
                    help="skip timing the convolution entry points (conv key)")
     p.add_argument("--conv-only", action="store_true",
                    help="time only the convolution entry points")
-    p.add_argument("--no-torch", action="store_true",
-                   help="skip timing torch's own scaled_dot_product_attention (context)")
-    p.add_argument("--torch-only", action="store_true",
-                   help="time only torch's scaled_dot_product_attention on the workload")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="instead of the benchmark, run 5 plain device-to-device copies of "
                         "BYTES bytes (the reference kernel for scaling HBM byte counters)")
@@ -174,9 +170,6 @@ def main():
     if args.rope_only:
         print(json.dumps({"rope_packed": rope_section(cfg, dtypes, args, stream, log)}), flush=True)
         return
-    if args.torch_only:
-        print(json.dumps({"torch_sdpa": torch_sdpa_section(cfg, args, log)}), flush=True)
-        return
     if args.configs_only:
         print(json.dumps({"configs": configs_section(args, log)}), flush=True)
         return
@@ -235,6 +228,10 @@ def main():
         ms_step = timed(step, args.steps, args.warmup)
         res = {"ms_per_step": ms_step,
                "value": flops["fwd_bwd"] / (ms_step * 1e-3) / 1e12}
+        # The spread of single steps: the same K steps again right after the
+        # headline bracket, with an event after each (kept out of the
+        # headline bracket so its K steps run back to back).
+        _, res["timed_steps"] = timed_events_samples(step, args.steps, 0, stream)
         if not args.only_step:
             res["step_samples"] = step_samples(step, stream)
             ms = {"fwd": timed(fwd, args.steps, 3), "bwd": timed(bwd, args.steps, 3)}
@@ -302,7 +299,8 @@ def main():
                    "backward_workspace": args.workspace},
         "kernel_sources": src_hash,
     }
-    for key in ("roofline", "phases", "kernels", "step_frac_of_mfma_peak", "step_samples"):
+    for key in ("timed_steps", "roofline", "phases", "kernels", "step_frac_of_mfma_peak",
+                "step_samples"):
         if key in results[head]:
             line[key] = results[head][key]
     for dt in dtypes[1:]:
@@ -320,63 +318,11 @@ def main():
         line["long_seq"] = scaling_section(args, log)
     if not args.no_conv and not args.only_step:
         line["conv"] = conv_section(args, log)
-    if not args.no_torch and not args.only_step:
-        line["torch_sdpa"] = torch_sdpa_section(cfg, args, log)
 
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the float64 oracle on the host")
         line["cpu_baseline"] = cpu_baseline(cfg, args.seed, args.cpu_seconds)
     print(json.dumps(line), flush=True)
-
-
-def torch_sdpa_section(cfg, args, log) -> dict:
-    """Context, not part of the path: torch's own fused attention
-    (torch.nn.functional.scaled_dot_product_attention with autograd) timed on
-    the same workload and GPU, one forward + backward per step, with the
-    backend pinned so that no unfused fallback runs: the flash kernel for
-    bf16, the memory-efficient kernel for float32 (flash takes no float32).
-    A backend this torch build lacks is reported, not substituted."""
-    import torch
-    import torch.nn.functional as F
-    from torch.nn.attention import SDPBackend, sdpa_kernel
-    from attention_forward_backward_amd import synth
-
-    B, H, S, D = cfg.shape
-    out = {"what": "torch.nn.functional.scaled_dot_product_attention forward + autograd "
-                   "backward, same shape, inputs and stream; context only",
-           "torch": torch.__version__}
-    stream = torch.cuda.current_stream()
-    for dt, backend in (("f32", SDPBackend.EFFICIENT_ATTENTION),
-                        ("bf16", SDPBackend.FLASH_ATTENTION)):
-        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
-        inp = synth.config_inputs(cfg, args.seed, "f32")
-        q, k, v = (torch.from_numpy(inp[n]).cuda().to(tdt).requires_grad_(True)
-                   for n in ("q", "k", "v"))
-        do = torch.from_numpy(inp["do"]).cuda().to(tdt)
-        rec = {"backend": backend.name}
-        try:
-            with sdpa_kernel([backend]):
-                def fwd():
-                    return F.scaled_dot_product_attention(q, k, v, is_causal=cfg.causal,
-                                                          scale=cfg.scale)
-
-                def step():
-                    o = fwd()
-                    torch.autograd.grad(o, (q, k, v), do)
-
-                log(f"[bench] torch sdpa {dt} ({backend.name})")
-                n = min(args.steps, 200)
-                with torch.no_grad():
-                    ms_f = timed_events(fwd, n, 20, stream)
-                ms_s = timed_events(step, n, 20, stream)
-            rec.update({"fwd_us": round(ms_f * 1e3, 2), "fwd_bwd_us": round(ms_s * 1e3, 2),
-                        "fwd_bwd_tflops": round(cfg.flops["fwd_bwd"] / (ms_s * 1e-3) / 1e12, 3)})
-        except Exception as e:  # a backend this torch lacks: say so
-            rec["unavailable"] = f"{type(e).__name__}: {str(e)[:200]}"
-        out[dt] = rec
-        del q, k, v, do
-        torch.cuda.empty_cache()
-    return out
 
 
 def visible_pairs(w, kv_len) -> int:
@@ -391,6 +337,29 @@ def visible_pairs(w, kv_len) -> int:
             per = w.seq_q * L
         total += per
     return total * w.heads
+
+
+def timed_events_samples(fn, steps, warmup, stream):
+    """timed_events, plus the time of each call inside the same bracket (an
+    event recorded after every call): (ms per call, {median, quartiles,
+    minimum, maximum} of the single calls in us)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]) * 1e3
+    stats = {"median_us": round(float(np.median(per)), 2),
+             "p25_us": round(float(np.percentile(per, 25)), 2),
+             "p75_us": round(float(np.percentile(per, 75)), 2),
+             "min_us": round(float(per.min()), 2), "max_us": round(float(per.max()), 2),
+             "samples": int(steps)}
+    return ev[0].elapsed_time(ev[-1]) / steps, stats
 
 
 def timed_events(fn, steps, warmup, stream):
@@ -536,11 +505,6 @@ def configs_section(args, log) -> dict:
     return out
 
 
-# Longer sequences at the decoder-step token count (B*S = 4096) and one long
-# D128 head set: how the contracts' MFMA fractions grow with the work per
-# (query tile, head) item.  Timing only (the kernels and their parity are
-# those of the five workloads).
-SCALING_SHAPES = [(2, 12, 2048, 64), (1, 12, 4096, 64), (1, 16, 4096, 128)]
 
 
 def scaling_section(args, log) -> dict:
@@ -552,7 +516,7 @@ def scaling_section(args, log) -> dict:
     from attention_forward_backward_amd import synth
 
     out = {}
-    for (B, H, S, D) in SCALING_SHAPES:
+    for (B, H, S, D) in synth.LONG_SEQ_SHAPES:
         name = f"B{B} H{H} S{S} D{D} causal"
         pairs = B * H * S * (S + 1) // 2
         rec = {"visible_pairs": pairs}
@@ -595,15 +559,6 @@ def scaling_section(args, log) -> dict:
     return out
 
 
-# ResNet-50 convolutions at batch 32 and 224 x 224 input (the pages' ResNet-50
-# workload; its batch and image size are not given): name -> (N, H, W, C, K,
-# R, S, stride, pad).  The stem's input is the image, which takes no
-# gradient, so its data derivative is not timed.
-CONV_LAYERS = {
-    "stem_7x7_s2": (32, 224, 224, 3, 64, 7, 7, (2, 2), (3, 3)),
-    "conv2_3x3": (32, 56, 56, 64, 64, 3, 3, (1, 1), (1, 1)),
-    "conv4_1x1": (32, 14, 14, 1024, 256, 1, 1, (1, 1), (0, 0)),
-}
 
 
 def conv_section(args, log) -> dict:
@@ -617,7 +572,7 @@ def conv_section(args, log) -> dict:
 
     stream = torch.cuda.current_stream()
     out = {}
-    for name, (N, H, W, C, K, R, S, st, pd) in CONV_LAYERS.items():
+    for name, (N, H, W, C, K, R, S, st, pd) in synth.CONV_LAYERS.items():
         P, Q = afb.conv2d_out_size(H, W, R, S, st, pd)
         flop = 2 * N * P * Q * K * R * S * C
         rec = {"shape": f"N{N} {H}x{W} C{C} K{K} {R}x{S} stride {st[0]} pad {pd[0]}",
@@ -855,32 +810,54 @@ def rope_section(cfg, dtypes, args, stream, log) -> dict:
     return out
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo; 'unknown' if absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, seed: int, target_s: float) -> dict:
     """The float64 oracle, as it stands, timed on this host's cores over whole
-    passes of the workload until about `target_s` seconds have passed."""
+    passes of the workload: once with its BLAS held to one thread and once
+    with every thread the BLAS library starts, each leg until about
+    target_s / 2 seconds have passed.  `value` is the all-core leg."""
     import oracle
     from attention_forward_backward_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = None
+    from threadpoolctl import threadpool_info, threadpool_limits
+
     inp = synth.config_inputs(cfg, seed, "f32")
     q, k, v, do = (inp[n].astype(np.float64) for n in ("q", "k", "v", "do"))
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.attention_forward(q, k, v, cfg.causal, cfg.scale)
-        oracle.attention_backward(q, k, v, do, cfg.causal, cfg.scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or el / reps * (reps + 1) > 2.5 * target_s:
-            break
-    per = el / reps
-    return {"value": cfg.flops["fwd_bwd"] / per / 1e12, "unit": "TFLOP/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full pass(es) of the {cfg.name} workload (fwd+bwd, float64, "
-                      f"numpy), {per:.2f} s per pass, {os.cpu_count()} logical CPUs visible"}
+
+    def leg(limit_s: float) -> tuple:
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.attention_forward(q, k, v, cfg.causal, cfg.scale)
+            oracle.attention_backward(q, k, v, do, cfg.causal, cfg.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= limit_s or el / reps * (reps + 1) > 2.5 * limit_s:
+                break
+        return reps, el / reps
+
+    with threadpool_limits(limits=1):
+        reps1, per1 = leg(target_s / 2)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    repsn, pern = leg(target_s / 2)
+    flop = cfg.flops["fwd_bwd"]
+    return {"value": flop / pern / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(), "logical_cpus": os.cpu_count(),
+            "single_thread": {"value": flop / per1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                              "s_per_pass": round(per1, 3), "passes": reps1},
+            "sample": f"{repsn} full pass(es) of the {cfg.name} workload (fwd+bwd, float64, "
+                      f"numpy oracle) with {threads} BLAS threads, {pern:.2f} s per pass; "
+                      f"single-thread leg {reps1} pass(es), {per1:.2f} s per pass"}
 
 
 if __name__ == "__main__":

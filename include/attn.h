@@ -40,8 +40,10 @@
  *  - Validation happens before anything is enqueued: on any error nothing
  *    is launched and the error code is returned.
  *      ATTN_ERR_INVALID_ARG  null pointer, batch/heads/seq <= 0, causal not
- *                            0 or 1, scale not a finite positive number (the
- *                            kernels take row maxima of unscaled scores), a
+ *                            0 or 1, scale not a finite positive number (a
+ *                            softmax temperature; the kernels take row
+ *                            maxima of the unscaled scores, which are the
+ *                            maxima of the scaled ones only for scale > 0), a
  *                            pointer not 16-byte aligned, or sizes whose
  *                            element count overflows a 32-bit signed index
  *      ATTN_ERR_UNSUPPORTED  head_dim not in {32, 64, 128}, or unknown dtype
@@ -81,8 +83,9 @@ typedef enum {
  *        lse       [B,H,S]   float32 natural-log row normaliser, scale
  *                                    included; the backward reads it.  NULL
  *                                    skips it: an inference-only forward
- *                                    (pages' Section 4.3, "one complete
- *                                    no-gradient forward pass").
+ *                                    that keeps no statistics for a
+ *                                    backward (the inference timing of the
+ *                                    pages' Section 4.3).
  * ATTN_F32_BF16FWD is the pages' practical contract (Section 4.2: forward
  * matrix and attention inputs rounded locally to reduced precision, f32
  * accumulation and stores, backward kept f32): tensors as ATTN_F32, MFMA
@@ -97,7 +100,10 @@ attn_status_t attn_fwd(attn_dtype_t dtype,
 
 /*
  * Workspace of the backward, in bytes (pure host functions; 0 for arguments
- * attn_bwd would reject).  The workspace holds, in this order:
+ * attn_bwd would reject).  The pages' runtime plans its buffers statically
+ * and allocates nothing while a step runs (Section 3.5, static execution and
+ * memory planning); here the caller owns every scratch byte, sized by these
+ * functions from the shape alone.  The workspace holds, in this order:
  *   1. for every query row, D_i = sum_d dO_id O_id and LSE_i * log2(e) (two
  *      [B,H,S] float32 vectors, rounded up to 256 bytes): the minimum;
  *   2. dS transposed, [B*H][Sp][Sp] with Sp = ceil(S/128)*128, in the
