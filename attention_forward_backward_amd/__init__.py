@@ -12,7 +12,8 @@ import ctypes
 import os
 import re
 
-__all__ = ["AttnError", "lib", "attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dkdv",
+__all__ = ["AttnError", "lib", "attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_prep",
+           "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_workspace_size", "attn_bwd_workspace_size_min",
            "attn_fwd_cross", "attn_bwd_cross", "attn_bwd_cross_workspace_size",
            "attn_bwd_cross_workspace_size_min",
@@ -50,6 +51,8 @@ _SIGS = {
     "attn_bwd_prep": (_I, [_I, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _P]),
     "attn_bwd": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                       _I, _I, _I, _I, _I, _F, _P]),
+    "attn_bwd_noalloc": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                              _I, _I, _I, _I, _I, _F, _P]),
     "attn_bwd_dq": (_I, [_I, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _P]),
     "attn_bwd_dkdv": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _P]),
     "attn_fwd_strided": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P,
@@ -316,6 +319,22 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: 
                           _nbytes(workspace), B, H, S, D,
                           int(causal), float(scale), _stream(stream))
     _raise("attn_bwd", code)
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: float,
+                     stream=None) -> None:
+    """dQ, dK, dV <- attention backward with the library's own device scratch
+    as the workspace (no workspace argument; calls on one GPU must not
+    overlap)."""
+    B, H, S, D = q.shape
+    _check({"q": q, "k": k, "v": v, "o": o, "dout": dout, "dq": dq, "dk": dk, "dv": dv},
+           (B, H, S, D), q.dtype)
+    _check_f32({"lse": lse}, (B, H, S))
+    code = lib().attn_bwd_noalloc(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  o.data_ptr(), dout.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+                                  dk.data_ptr(), dv.data_ptr(), B, H, S, D,
+                                  int(causal), float(scale), _stream(stream))
+    _raise("attn_bwd_noalloc", code)
 
 
 def attn_bwd_prep(o, dout, lse, workspace, stream=None) -> None:

@@ -1,18 +1,44 @@
 // attn_api.hip -- the C ABI declared in include/attn.h.
 //
 // Validates every argument on the host before anything is enqueued, then
-// hands a launch descriptor to the kernel launchers.  No device memory is
-// allocated and no pointer is retained between calls (the launchers cache
-// only occupancy figures and schedule patterns, on the host).
+// hands a launch descriptor to the kernel launchers.  No call allocates
+// device memory and no pointer is retained between calls (the launchers
+// cache only occupancy figures and schedule patterns, on the host); the one
+// device buffer of the library is the static scratch array of the
+// allocation-free backward.
 #include <math.h>
 
+#include <mutex>
 #include <utility>
 #include <stdint.h>
 
 #include "../../include/attn.h"
 #include "attn_launch.hpp"
 
+// The allocation-free backward (attn_bwd_noalloc) takes its workspace from
+// this device array: one copy per GPU, resident while the process runs.  In
+// host code `scratch` names a host-side stand-in, never the device memory;
+// scratch_base() gives the device address.
+constexpr size_t kScratchBytes = ATTN_BWD_NOALLOC_MAX_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
+
+// Device address of this GPU's scratch array, looked up once per device
+// (with that device current) and kept; null if the lookup fails.
+void* scratch_base() {
+  static std::mutex mu;
+  static void* base[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (base[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    base[dev] = p;
+  }
+  return base[dev];
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -281,6 +307,23 @@ attn_status_t attn_bwd(attn_dtype_t dtype, const void* q, const void* k, const v
                   heads, seq, seq, head_dim, nullptr, causal, scale, stream);
 }
 
+attn_status_t attn_bwd_noalloc(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                               const void* o, const void* dout, const float* lse, void* dq,
+                               void* dk, void* dv, int batch, int heads, int seq, int head_dim,
+                               int causal, float scale, void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, seq, seq, head_dim, causal, scale, true);
+  if (st != ATTN_OK) return st;
+  if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv})) != ATTN_OK) return st;
+  if (ws_min_bytes(batch, heads, seq) > kScratchBytes) return ATTN_ERR_WORKSPACE;
+  void* ws = scratch_base();
+  if (ws == nullptr) return ATTN_ERR_HIP;
+  // The largest workspace layout the array holds (make_bwd picks the dS
+  // path and the query split by size, as for a caller's workspace).
+  const size_t bytes = std::min(kScratchBytes, ws_rec_bytes(dtype, batch, heads, seq, seq, head_dim));
+  return bwd_impl(dtype, q, k, v, o, dout, lse, dq, dk, dv, ws, bytes, batch, heads, seq, seq,
+                  head_dim, nullptr, causal, scale, stream);
+}
+
 attn_status_t attn_bwd_cross(attn_dtype_t dtype, const void* q, const void* k, const void* v,
                              const void* o, const void* dout, const float* lse, void* dq,
                              void* dk, void* dv, void* workspace, size_t workspace_bytes,
@@ -391,6 +434,6 @@ const char* attn_status_string(attn_status_t s) {
   return "unknown status";
 }
 
-const char* attn_version(void) { return "0.6.0"; }
+const char* attn_version(void) { return "0.7.0"; }
 
 }  // extern "C"

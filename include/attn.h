@@ -149,6 +149,34 @@ attn_status_t attn_bwd(attn_dtype_t dtype,
                        int causal, float scale, void* stream);
 
 /*
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): attn_bwd without the workspace arguments.  Its workspace is a
+ * device array inside the library, ATTN_BWD_NOALLOC_MAX_BYTES (128 MiB) per
+ * GPU, reserved when the library's device code is loaded on that GPU and
+ * held until the process ends; the call itself allocates and frees nothing.
+ * It uses the largest layout of attn_bwd_workspace_size() that fits the
+ * array (the dS path whenever the minimum plus dS^T fits: up to 127 heads
+ * of S = 512 in float32, 254 in bf16), so its results are bitwise those of
+ * attn_bwd given a workspace of that size.
+ * Errors as attn_bwd, and ATTN_ERR_WORKSPACE when even the minimum workspace
+ * (2 * batch * heads * seq float32, rounded up to 256 bytes) exceeds the
+ * array, i.e. when batch * heads * seq > 16,777,216.
+ * Every call on one GPU uses that GPU's one array: calls that can overlap in
+ * time on the same GPU (several streams, several host threads) race and give
+ * undefined results, so serialise them (one stream).  Nothing in the array
+ * has to start at zero: every workspace value a call uses is written earlier
+ * in the same call.
+ */
+#define ATTN_BWD_NOALLOC_MAX_BYTES ((size_t)128 << 20)
+attn_status_t attn_bwd_noalloc(attn_dtype_t dtype,
+                               const void* q, const void* k, const void* v,
+                               const void* o, const void* dout, const float* lse,
+                               void* dq, void* dk, void* dv,
+                               int batch, int heads, int seq, int head_dim,
+                               int causal, float scale, void* stream);
+
+/*
  * Backward stage 1 alone: D_i = sum_d dO_id O_id and LSE_i * log2(e) into
  * the workspace (memory-bound, one pass over O and dO).
  */

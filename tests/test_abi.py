@@ -15,7 +15,8 @@ MIS = 0x10008           # 8-byte aligned only
 def test_library_loads_and_exports_header_symbols():
     L = afb.lib()
     declared = afb.declared_symbols()
-    assert set(declared) == {"attn_fwd", "attn_bwd", "attn_bwd_prep", "attn_bwd_dq",
+    assert set(declared) == {"attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_prep",
+                             "attn_bwd_dq",
                              "attn_bwd_dkdv", "attn_bwd_workspace_size",
                              "attn_bwd_workspace_size_min", "attn_fwd_cross", "attn_bwd_cross",
                              "attn_bwd_cross_workspace_size", "attn_bwd_cross_workspace_size_min",
@@ -25,7 +26,7 @@ def test_library_loads_and_exports_header_symbols():
                              "conv2d_bwd_filter_workspace_size"}
     for name in declared:
         assert hasattr(L, name), name
-    assert afb.attn_version() == "0.6.0"
+    assert afb.attn_version() == "0.7.0"
     for code in range(5):
         assert afb.attn_status_string(code) not in ("", "unknown status")
     assert afb.attn_status_string(99) == "unknown status"
@@ -42,6 +43,26 @@ def _bwd(dtype=0, ptr=FAKE, ws=FAKE, wsb=1 << 20, B=1, H=1, S=8, D=64, causal=1,
     if misalign is not None:
         p[misalign] = MIS
     return afb.lib().attn_bwd(dtype, *p, ws, wsb, B, H, S, D, causal, scale, None)
+
+
+def _bwd_noalloc(dtype=0, ptr=FAKE, B=1, H=1, S=8, D=64, causal=1, scale=0.125, misalign=None):
+    p = [ptr] * 9
+    if misalign is not None:
+        p[misalign] = MIS
+    return afb.lib().attn_bwd_noalloc(dtype, *p, B, H, S, D, causal, scale, None)
+
+
+def test_bwd_noalloc_validation():
+    """The allocation-free backward validates like attn_bwd and rejects a
+    shape whose minimum workspace exceeds its 128 MiB scratch array
+    (B*H*S > 2^24 query rows) before touching the GPU."""
+    for i in range(9):
+        assert _bwd_noalloc(misalign=i) == 1, i
+    assert _bwd_noalloc(ptr=None) == 1
+    assert _bwd_noalloc(D=96) == 2 and _bwd_noalloc(dtype=5) == 2
+    assert _bwd_noalloc(causal=3) == 1 and _bwd_noalloc(scale=math.nan) == 1
+    assert _bwd_noalloc(B=1, H=256, S=(1 << 16) + 1) == 3
+    assert _bwd_noalloc(B=4, H=64, S=(1 << 16) + 8, D=32) == 3
 
 
 def test_fwd_validation():
