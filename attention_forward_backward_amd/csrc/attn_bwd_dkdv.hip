@@ -26,9 +26,10 @@
 // registers from LDS) and then its query tiles (Q, dO, and the queries' LSE
 // and D), so the next item's rows and first queries load while the current
 // item finishes.  Per 32-query block a wave forms S = Q K^T and dP = dO V^T
-// (queries x keys; each lane holds one key), then P^T and dS^T are the
-// register A operands of dV (keys x d) += P^T dO and dK += dS^T Q, with dO
-// and Q read back from LDS.
+// (queries x keys; each lane holds one key), then P and dS are the register
+// B operands of dV^T (d x keys) += dO^T P and dK^T += Q^T dS, with dO and Q
+// read back from LDS: each lane accumulates the d values of its own key, so
+// dK and dV leave in 16-byte (f32) or 8-byte (bf16) row stores.
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
 
@@ -209,40 +210,46 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
     }
     int nstores = 0;
     if (sp == 0 && active) {
-      // element r of acc[db]: row k0 + out_row(r, h), column db*32 + n
+      // The accumulators hold dK^T and dV^T: element r of acc[db] is key
+      // k0 + n, column db*32 + out_row(r, h), so elements 4j .. 4j+3 are four
+      // consecutive columns of one key row and go out in one store.
+      const int key = k0 + n;
       if constexpr (!QSPLIT) {
         T* dk = dK + head_off<STR, D>(lay.dk, bh, H, Sk);
         T* dv = dV + head_off<STR, D>(lay.dv, bh, H, Sk);
         const int lddk = row_ld<STR, D>(lay.dk), lddv = row_ld<STR, D>(lay.dv);
+        if (key < Sk) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = k0 + out_row(r, h);
-          if (row < Sk) {
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              dk[(size_t)row * lddk + db * 32 + n] = (T)(dkacc[db][r] * scale);
-              dv[(size_t)row * lddv + db * 32 + n] = (T)dvacc[db][r];
+            for (int j = 0; j < 4; ++j) {
+              const int d = db * 32 + 8 * j + 4 * h;
+              store4<T>(dk + (size_t)key * lddk + d, dkacc[db][4 * j] * scale,
+                        dkacc[db][4 * j + 1] * scale, dkacc[db][4 * j + 2] * scale,
+                        dkacc[db][4 * j + 3] * scale);
+              store4<T>(dv + (size_t)key * lddv + d, dvacc[db][4 * j], dvacc[db][4 * j + 1],
+                        dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
             }
-          }
         }
       } else {
         float* pk = part + ((size_t)qc * BH + bh) * Sk * D;
         float* pv = part + ((size_t)(nqs + qc) * BH + bh) * Sk * D;
+        if (key < Sk) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = k0 + out_row(r, h);
-          if (row < Sk) {
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-              pk[(size_t)row * D + db * 32 + n] = dkacc[db][r] * scale;
-              pv[(size_t)row * D + db * 32 + n] = dvacc[db][r];
+            for (int j = 0; j < 4; ++j) {
+              const int d = db * 32 + 8 * j + 4 * h;
+              store4<float>(pk + (size_t)key * D + d, dkacc[db][4 * j] * scale,
+                            dkacc[db][4 * j + 1] * scale, dkacc[db][4 * j + 2] * scale,
+                            dkacc[db][4 * j + 3] * scale);
+              store4<float>(pv + (size_t)key * D + d, dvacc[db][4 * j], dvacc[db][4 * j + 1],
+                            dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
             }
-          }
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (k0 + out_row(r, 1) < Sk) nstores += 2 * NDB;
+      // (counted only when every lane's key exists, so that every lane stores)
+      if (k0 + 31 < Sk) nstores = 2 * 4 * NDB;
     }
     return nstores;
   };
@@ -377,8 +384,10 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
         dS.set(dp);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          dvacc[db] = second_tile<E, D, true>(P, dOt, qbl * 32, db * 32, lane, dvacc[db]);
-          dkacc[db] = second_tile<E, D, true>(dS, Qt, qbl * 32, db * 32, lane, dkacc[db]);
+          // dV^T (d x keys) += dO^T P and dK^T += Q^T dS: the register
+          // operand is the B side, so a lane accumulates its own key's row
+          dvacc[db] = second_tile<E, D, false>(P, dOt, qbl * 32, db * 32, lane, dvacc[db]);
+          dkacc[db] = second_tile<E, D, false>(dS, Qt, qbl * 32, db * 32, lane, dkacc[db]);
         }
       }
     }

@@ -22,8 +22,10 @@
 // issued NST-1 tiles ahead (one barrier per tile).  Per 32-key block a wave
 // forms S^T = K Q^T and dP^T = V dO^T (keys x queries; each lane holds one
 // query, so LSE_i and D_i are one register each), then
-// dS^T = P^T o (dP^T - D) in registers, which is the A operand of
-// dQ (queries x d) += dS K with K read back from the same LDS tile.
+// dS^T = P^T o (dP^T - D) in registers, which is the B operand of
+// dQ^T (d x queries) += K^T dS^T with K read back from the same LDS tile:
+// each lane accumulates the d values of its own query, so dQ leaves in
+// 16-byte (f32) or 8-byte (bf16) row stores.
 #include "attn_device.hpp"
 #include "attn_launch.hpp"
 
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
       dS.set(st);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        acc[db] = second_tile<E, D, true>(dS, Kt, kb * 32, db * 32, lane, acc[db]);
+        acc[db] = second_tile<E, D, false>(dS, Kt, kb * 32, db * 32, lane, acc[db]);
     }
   };
   if constexpr (NST * LD::BYTES <= 65536) {
@@ -185,17 +187,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     }
   }
   if (!wave_active) return;
-  // acc[db] element r: dQ[q0 + out_row(r, h)][db*32 + n]
+  // acc[db] holds dQ^T: element r is query q0 + n, column db*32 + out_row(r, h),
+  // so elements 4j .. 4j+3 are four consecutive columns (one store)
   T* dq = STR ? dQ + head_off<STR, D>(lay.dq, bh, H, Sq) : dQ + base;
   const int lddq = row_ld<STR, D>(lay.dq);
+  if (qvalid) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = q0 + out_row(r, h);
-    if (row < Sq) {
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dq[(size_t)row * lddq + db * 32 + n] = (T)(acc[db][r] * scale);
-    }
+      for (int j = 0; j < 4; ++j)
+        store4<T>(dq + (size_t)qi * lddq + db * 32 + 8 * j + 4 * h, acc[db][4 * j] * scale,
+                  acc[db][4 * j + 1] * scale, acc[db][4 * j + 2] * scale,
+                  acc[db][4 * j + 3] * scale);
   }
 }
 
@@ -278,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
       read_kslot_operand<E, BR>(R, St, kb * 32, qb * 32, lane);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
-        acc[db] = second_tile<E, D, true>(R, Kt, kb * 32, db * 32, lane, acc[db]);
+        acc[db] = second_tile<E, D, false>(R, Kt, kb * 32, db * 32, lane, acc[db]);
     }
   };
   if constexpr (NST * STAGE <= 65536) {
@@ -311,16 +314,18 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
     }
   }
   if (!wave_active) return;
+  // acc[db] holds dQ^T: element r is query q0 + n, column db*32 + out_row(r, h)
   T* dq = dQ + head_off<STR, D>(lay.dq, bh, H, Sq);
   const int lddq = row_ld<STR, D>(lay.dq);
+  const int qi = q0 + n;
+  if (qi < Sq) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = q0 + out_row(r, h);
-    if (row < Sq) {
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
-        dq[(size_t)row * lddq + db * 32 + n] = (T)(acc[db][r] * scale);
-    }
+      for (int j = 0; j < 4; ++j)
+        store4<T>(dq + (size_t)qi * lddq + db * 32 + 8 * j + 4 * h, acc[db][4 * j] * scale,
+                  acc[db][4 * j + 1] * scale, acc[db][4 * j + 2] * scale,
+                  acc[db][4 * j + 3] * scale);
   }
 }
 

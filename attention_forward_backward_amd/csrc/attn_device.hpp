@@ -226,7 +226,7 @@ __device__ inline void for_stages(int n, F&& f) {
 // Workgroups are dispatched round-robin over the 8 XCDs, so keeping the
 // residue keeps every item of a head on one XCD and its L2.  Item numbers
 // grow with r, so a workgroup stops at its first number >= the count.
-__device__ inline int snake_item(int r, int g, int G) {
+__host__ __device__ inline int snake_item(int r, int g, int G) {
   if (!(r & 1)) return r * G + g;
   const int gr = (G % 8 == 0) ? g % 8 + 8 * (G / 8 - 1 - g / 8) : G - 1 - g;
   return r * G + gr;
@@ -304,11 +304,11 @@ struct Sched {
 // The 16-bit entries are read as the 32-bit words that hold them: with a
 // wave-uniform index those are scalar loads, while a 16-bit read would be a
 // vector load (and a vector-memory wait that also drains the tile loads).
-__device__ inline int sched_entry(const uint16_t* a, int i) {
+__host__ __device__ inline int sched_entry(const uint16_t* a, int i) {
   const uint32_t v = reinterpret_cast<const uint32_t*>(a)[i >> 1];
   return (int)((i & 1) ? v >> 16 : v & 0xffffu);
 }
-__device__ inline int sched_item(const Sched& s, int r, int g, int G, int BH) {
+__host__ __device__ inline int sched_item(const Sched& s, int r, int g, int G, int BH) {
   const int e0 = sched_entry(s.first, (g >> 3) & (kSchedSlots - 1));
   if (s.M == 0) return snake_item(r, g, G);
   if (r >= s.R) return 0x7fffffff;
@@ -359,6 +359,27 @@ __device__ inline void wait_tiles(int newer, int blocks = 0) {
     else wait_vmem<0>();
   }
 }
+// The issue count just after the loads of the tile in each slot of an
+// NST-stage ring (see the kernels' wait rule), as separate scalars: a small
+// array indexed by a run-time slot would be placed in LDS by the compiler.
+template <int NST>
+struct RingMarks {
+  int m0 = 0, m1 = 0, m2 = 0, m3 = 0;
+  __host__ __device__ inline void set(int slot, int v) {
+    if (slot == 0) m0 = v;
+    if (NST > 1 && slot == 1) m1 = v;
+    if (NST > 2 && slot == 2) m2 = v;
+    if (NST > 3 && slot == 3) m3 = v;
+  }
+  __host__ __device__ inline int get(int slot) const {
+    int v = m0;
+    if (NST > 1 && slot == 1) v = m1;
+    if (NST > 2 && slot == 2) v = m2;
+    if (NST > 3 && slot == 3) v = m3;
+    return v;
+  }
+};
+
 // Workgroup barrier that orders LDS accesses without waiting for pending
 // global loads (those are waited for explicitly with wait_vmem).
 __device__ inline void lds_barrier() {

@@ -98,9 +98,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   // (vmcnt counts loads and stores, and they retire in issue order);
   // counting fewer stores than issued only makes a wait stricter.
   int vm = 0, qmark = 0;
-  int mk[NST];
-#pragma unroll
-  for (int i = 0; i < NST; ++i) mk[i] = 0;
+  RingMarks<NST> mk;
 
   // Loader cursor: tile lkt of item lit is the next one to issue.
   int lr = 0, lit = sched_item(sched, 0, g, G, BH), lkt = 0, lnkt = item_nkt(lit);
@@ -116,9 +114,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     else
       LD::issue(smem + slot * STAGE, K + kbase, V + vbase, lkt * BK, lrows, w, lane, lo);
     vm += LD::NLOADS;
-#pragma unroll
-    for (int i = 0; i < NST; ++i)
-      if (slot == i) mk[i] = vm;
+    mk.set(slot, vm);
     if (++lkt == lnkt) {
       lit = sched_item(sched, ++lr, g, G, BH);
       lkt = 0;
@@ -232,10 +228,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   // is unrolled by NST with the slot constant.
   auto step = [&](const int pos, auto sc) __attribute__((always_inline)) {
     const int si = sc;  // pos % NST
-    int mark = mk[0];
-#pragma unroll
-    for (int i = 1; i < NST; ++i)
-      if (si == i) mark = mk[i];
+    int mark = mk.get(si);
     if (kt == 0) mark = max(mark, qmark);  // the item's Q rows too
     wait_vmem_dyn(vm - mark);
     lds_barrier();  // tile pos (and on an item's first tile its Q) is in LDS;

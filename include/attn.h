@@ -70,10 +70,14 @@ typedef enum {
 typedef enum {
   ATTN_F32 = 0,         /* strict float32 contract */
   ATTN_BF16 = 1,        /* bf16 storage and MFMA operands, f32 accumulation */
-  ATTN_F32_BF16FWD = 2  /* float32 storage; the forward rounds its MFMA
+  ATTN_F32_BF16FWD = 2, /* float32 storage; the forward rounds its MFMA
                            operands (Q, K, V, P) to bf16 and accumulates and
                            stores in f32; every backward entry point treats
                            it as ATTN_F32 (strict) */
+  ATTN_DTYPE_INT_RANGE_ = 0x7fffffff  /* not a dtype: makes every int value a
+                           valid attn_dtype_t in C++, so that an unknown code
+                           from a caller is rejected (ATTN_ERR_UNSUPPORTED)
+                           rather than being undefined behaviour */
 } attn_dtype_t;
 
 /*

@@ -80,8 +80,8 @@ def test_long_sequence_minimum_workspace(dt):
 
 def _cross_case(wl, dt, seed=0):
     import torch
-    B, H, Sq, Sk, D = wl.B, wl.H, wl.Sq, wl.Sk, wl.D
-    kvl = synth.key_lengths(seed, B, wl.kv_lo, Sk) if wl.padded else None
+    B, H, Sq, Sk, D = wl.batch, wl.heads, wl.seq_q, wl.seq_k, wl.head_dim
+    kvl = synth.key_lengths(seed, B, wl.min_keys, Sk) if wl.padded else None
     note(f"[gpu case] cross workload {wl.name} B{B} H{H} Sq{Sq} Sk{Sk} D{D} causal={wl.causal} "
          f"padded={wl.padded} dtype={dt} -> attn_fwd_cross + attn_bwd_cross")
     inp = synth.cross_inputs((B, H, Sq, D), (B, H, Sk, D), seed, dt)
