@@ -12,7 +12,7 @@ import ctypes
 import os
 import re
 
-__all__ = ["AttnError", "lib", "attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_prep",
+__all__ = ["AttnError", "lib", "attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_prep",
            "attn_bwd_dkdv",
            "attn_bwd_dq", "attn_bwd_workspace_size", "attn_bwd_workspace_size_min",
            "attn_fwd_cross", "attn_bwd_cross", "attn_bwd_cross_workspace_size",
@@ -42,6 +42,8 @@ _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 _SIGS = {
     "attn_fwd": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P]),
     "attn_fwd_cross": (_I, [_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _F, _P]),
+    "attn_fwd_ws": (_I, [_I, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_fwd_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "attn_bwd_cross": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                             _I, _I, _I, _I, _I, _P, _I, _F, _P]),
     "attn_bwd_cross_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
@@ -202,6 +204,32 @@ def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None,
                           o.data_ptr(), 0 if lse is None else lse.data_ptr(), B, H, S, D,
                           int(causal), float(scale), _stream(stream))
     _raise("attn_fwd", code)
+
+
+def attn_fwd_workspace_size(code: int, B: int, H: int, S: int, D: int, causal: bool) -> int:
+    """Bytes of workspace for the key-split forward (0: the shape is not split)."""
+    return int(lib().attn_fwd_workspace_size(code, B, H, S, D, int(causal)))
+
+
+def attn_fwd_ws(q, k, v, o, lse, workspace, causal: bool, scale: float, stream=None,
+                bf16_operands: bool = False) -> None:
+    """attn_fwd with a workspace (a device tensor, or None): the key split is
+    used when the workspace holds attn_fwd_workspace_size() bytes."""
+    B, H, S, D = q.shape
+    _check({"q": q, "k": k, "v": v, "o": o}, (B, H, S, D), q.dtype)
+    if lse is not None:
+        _check_f32({"lse": lse}, (B, H, S))
+    code = _dtype_code(q)
+    if bf16_operands:
+        if code != ATTN_F32:
+            raise TypeError("bf16_operands applies to float32 tensors")
+        code = ATTN_F32_BF16FWD
+    code = lib().attn_fwd_ws(code, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             0 if lse is None else lse.data_ptr(),
+                             0 if workspace is None else workspace.data_ptr(),
+                             0 if workspace is None else _nbytes(workspace), B, H, S, D,
+                             int(causal), float(scale), _stream(stream))
+    _raise("attn_fwd_ws", code)
 
 
 def attn_fwd_cross(q, k, v, o, lse, kv_len, causal: bool, scale: float, stream=None,

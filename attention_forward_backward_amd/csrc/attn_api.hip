@@ -93,10 +93,14 @@ size_t ws_part_bytes(attn_dtype_t dtype, int batch, int heads, int sq, int sk, i
   return nqs > 1 ? round256(2 * (size_t)nqs * batch * heads * sk * head_dim * sizeof(float)) : 0;
 }
 
-// Recommended workspace: the dS path plus, for shapes with few key tiles per
-// head, room for the dK, dV partials.
+// Recommended workspace: the dS path while its dS^T buffer fits
+// ATTN_DS_WORKSPACE_CAP bytes, else the minimum (so the recommended size is
+// O(S) for long sequences), plus, for shapes with few key tiles per head,
+// room for the dK, dV partials.
 size_t ws_rec_bytes(attn_dtype_t dtype, int batch, int heads, int sq, int sk, int head_dim) {
-  return ws_full_bytes(dtype, batch, heads, sq, sk) +
+  const size_t full = ws_full_bytes(dtype, batch, heads, sq, sk);
+  const size_t mn = ws_min_bytes(batch, heads, sq);
+  return (full - mn <= (size_t)ATTN_DS_WORKSPACE_CAP ? full : mn) +
          ws_part_bytes(dtype, batch, heads, sq, sk, head_dim);
 }
 
@@ -173,10 +177,23 @@ attn::Str3 str3(const long long* st) {
   return attn::Str3{(int)st[0], (int)st[1], (int)st[2]};
 }
 
+// Workspace of the key-split forward: unnormalised O partials [nch][B*H][Sp][D]
+// and (m, l) pairs [nch][B*H][Sp][2], float32; 0 when the shape is not split.
+size_t fwd_ws_bytes(attn_dtype_t dtype, int batch, int heads, int seq, int head_dim, int causal) {
+  if (seq <= (dtype == ATTN_BF16 ? ATTN_FWD_SMALL_MAXQ_BF16 : ATTN_FWD_SMALL_MAXQ_F32)) return 0;
+  int nch = 1, kc = 0;
+  const bool bf16 = dtype == ATTN_BF16;
+  if (!attn::fwd_key_split(bf16, (long long)batch * heads, seq, head_dim, causal != 0, nch, kc))
+    return 0;
+  const int br = attn::fwd_query_tile(bf16, head_dim);
+  const size_t sp = (size_t)(seq + br - 1) / br * br;
+  return round256((size_t)nch * batch * heads * sp * (head_dim + 2) * sizeof(float));
+}
+
 attn_status_t fwd_impl(attn_dtype_t dtype, const void* q, const void* k, const void* v, void* o,
                        float* lse, int batch, int heads, int sq, int sk, int head_dim,
                        const int* kvlen, int causal, float scale, void* stream,
-                       const attn::Layout* layout = nullptr) {
+                       const attn::Layout* layout = nullptr, float* part = nullptr) {
   attn_status_t st = check_shape(dtype, batch, heads, sq, sk, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
   if ((st = check_ptrs({q, k, v, o})) != ATTN_OK) return st;
@@ -192,6 +209,7 @@ attn_status_t fwd_impl(attn_dtype_t dtype, const void* q, const void* k, const v
   a.causal = causal != 0; a.scale = scale;
   a.stream = static_cast<hipStream_t>(stream);
   a.layout = layout;
+  a.part = part;
   return from_hip(attn::launch_fwd(a));
 }
 
@@ -222,6 +240,28 @@ attn_status_t attn_fwd(attn_dtype_t dtype, const void* q, const void* k, const v
                        float scale, void* stream) {
   return fwd_impl(dtype, q, k, v, o, lse, batch, heads, seq, seq, head_dim, nullptr, causal, scale,
                   stream);
+}
+
+size_t attn_fwd_workspace_size(attn_dtype_t dtype, int batch, int heads, int seq, int head_dim,
+                               int causal) {
+  if (check_shape(dtype, batch, heads, seq, seq, head_dim, causal, 1.f, false) != ATTN_OK) return 0;
+  return fwd_ws_bytes(dtype, batch, heads, seq, head_dim, causal);
+}
+
+attn_status_t attn_fwd_ws(attn_dtype_t dtype, const void* q, const void* k, const void* v, void* o,
+                          float* lse, void* workspace, size_t workspace_bytes, int batch,
+                          int heads, int seq, int head_dim, int causal, float scale,
+                          void* stream) {
+  if (workspace != nullptr && !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = check_shape(dtype, batch, heads, seq, seq, head_dim, causal, scale, true) ==
+                              ATTN_OK
+                          ? fwd_ws_bytes(dtype, batch, heads, seq, head_dim, causal)
+                          : 0;
+  float* part = (need > 0 && workspace != nullptr && workspace_bytes >= need)
+                    ? static_cast<float*>(workspace)
+                    : nullptr;
+  return fwd_impl(dtype, q, k, v, o, lse, batch, heads, seq, seq, head_dim, nullptr, causal, scale,
+                  stream, nullptr, part);
 }
 
 attn_status_t attn_fwd_cross(attn_dtype_t dtype, const void* q, const void* k, const void* v,

@@ -182,27 +182,43 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
       for (int pass = 0; pass < NPASS; ++pass) {
         const bool withk = NPASS == 1 || pass == 0, withv = NPASS == 1 || pass == 1;
         lds_barrier();  // every wave is done reading the stage (or the previous pass)
+        // Partials go through LDS four at a time: value group q of lane l at
+        // float (q * 64 + l) * 4, so each 16-byte write or read of a wave
+        // covers 1 KiB without bank conflicts.
         if (sp != 0 && active) {
-          float* dst = cb + ((kbk * (NSPLIT - 1) + sp - 1) * PER) * 64 + lane;
+          f32x4* dst = reinterpret_cast<f32x4*>(cb + ((kbk * (NSPLIT - 1) + sp - 1) * PER) * 64) + lane;
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              if (withk) dst[(db * 16 + r) * 64] = dkacc[db][r];
-              if (withv) dst[(VOFF + db * 16 + r) * 64] = dvacc[db][r];
+            for (int j = 0; j < 4; ++j) {
+              if (withk)
+                dst[(db * 4 + j) * 64] = f32x4{dkacc[db][4 * j], dkacc[db][4 * j + 1],
+                                               dkacc[db][4 * j + 2], dkacc[db][4 * j + 3]};
+              if (withv)
+                dst[(VOFF / 4 + db * 4 + j) * 64] = f32x4{dvacc[db][4 * j], dvacc[db][4 * j + 1],
+                                                          dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]};
             }
         }
         lds_barrier();
         if (sp == 0 && active) {
 #pragma unroll
           for (int p = 0; p < NSPLIT - 1; ++p) {
-            const float* src = cb + ((kbk * (NSPLIT - 1) + p) * PER) * 64 + lane;
+            const f32x4* src =
+                reinterpret_cast<const f32x4*>(cb + ((kbk * (NSPLIT - 1) + p) * PER) * 64) + lane;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                if (withk) dkacc[db][r] += src[(db * 16 + r) * 64];
-                if (withv) dvacc[db][r] += src[(VOFF + db * 16 + r) * 64];
+              for (int j = 0; j < 4; ++j) {
+                if (withk) {
+                  const f32x4 x = src[(db * 4 + j) * 64];
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) dkacc[db][4 * j + e] += x[e];
+                }
+                if (withv) {
+                  const f32x4 x = src[(VOFF / 4 + db * 4 + j) * 64];
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) dvacc[db][4 * j + e] += x[e];
+                }
               }
           }
         }
@@ -475,7 +491,8 @@ static hipError_t launch(const BwdArgs& a) {
     const int kt = c / nqs, qc = c % nqs;
     const int fq = CAUSAL ? std::min(nqt, std::max(0, kt * BKV - off) / BQ) : 0;
     const int lo = std::max(fq, qc * qpc), hi = std::min(nqt, (qc + 1) * qpc);
-    works[c] = 1 + std::max(0, hi - lo);
+    works[c] = 4 * std::max(0, hi - lo) +
+               (is_bf16<E>() ? ATTN_DKDV_ITEM_COST_BF16 : ATTN_DKDV_ITEM_COST_F32);
   }
   const Sched sched = make_sched(grid, a.BH, works);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,

@@ -166,23 +166,31 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   if constexpr (NSPLIT > 1) {
     float* cb = reinterpret_cast<float*>(smem);
     lds_barrier();  // every wave is done with the tiles (no loads pending)
+    // four values per 16-byte LDS access: group q of lane l at float (q * 64 + l) * 4
     if (sp != 0 && wave_active) {
-      float* dst = cb + ((qb * (NSPLIT - 1) + sp - 1) * 16 * NDB) * 64 + lane;
+      f32x4* dst = reinterpret_cast<f32x4*>(cb + ((qb * (NSPLIT - 1) + sp - 1) * 16 * NDB) * 64) + lane;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dst[(db * 16 + r) * 64] = acc[db][r];
+        for (int j = 0; j < 4; ++j)
+          dst[(db * 4 + j) * 64] =
+              f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]};
     }
     lds_barrier();
     if (sp != 0) return;
     if (wave_active) {
 #pragma unroll
       for (int p = 0; p < NSPLIT - 1; ++p) {
-        const float* src = cb + ((qb * (NSPLIT - 1) + p) * 16 * NDB) * 64 + lane;
+        const f32x4* src =
+            reinterpret_cast<const f32x4*>(cb + ((qb * (NSPLIT - 1) + p) * 16 * NDB) * 64) + lane;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] += src[(db * 16 + r) * 64];
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 x = src[(db * 4 + j) * 64];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[db][4 * j + e] += x[e];
+          }
       }
     }
   }
@@ -293,23 +301,31 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   if constexpr (NSPLIT > 1) {
     float* cb = reinterpret_cast<float*>(smem);
     lds_barrier();
+    // four values per 16-byte LDS access: group q of lane l at float (q * 64 + l) * 4
     if (sp != 0 && wave_active) {
-      float* dst = cb + ((qb * (NSPLIT - 1) + sp - 1) * 16 * NDB) * 64 + lane;
+      f32x4* dst = reinterpret_cast<f32x4*>(cb + ((qb * (NSPLIT - 1) + sp - 1) * 16 * NDB) * 64) + lane;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dst[(db * 16 + r) * 64] = acc[db][r];
+        for (int j = 0; j < 4; ++j)
+          dst[(db * 4 + j) * 64] =
+              f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]};
     }
     lds_barrier();
     if (sp != 0) return;
     if (wave_active) {
 #pragma unroll
       for (int p = 0; p < NSPLIT - 1; ++p) {
-        const float* src = cb + ((qb * (NSPLIT - 1) + p) * 16 * NDB) * 64 + lane;
+        const f32x4* src =
+            reinterpret_cast<const f32x4*>(cb + ((qb * (NSPLIT - 1) + p) * 16 * NDB) * 64) + lane;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] += src[(db * 16 + r) * 64];
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 x = src[(db * 4 + j) * 64];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[db][4 * j + e] += x[e];
+          }
       }
     }
   }

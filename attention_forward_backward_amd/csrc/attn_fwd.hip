@@ -35,17 +35,23 @@
 namespace attn {
 
 template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS,
-          bool STR>
+          bool STR, bool KS>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O,
     float* __restrict__ LSE, int Sq, int Sk_, float c, int BH, int H,
-    const int* __restrict__ kvlen, int nitems, const Sched sched, const Layout lay) {
+    const int* __restrict__ kvlen, int nitems, const Sched sched, const Layout lay, int nch,
+    int kc, float* __restrict__ part, int Sp) {
   // LSE may be null (an inference-only forward stores no LSE).  Queries Sq,
   // keys Sk (one length in self-attention, CROSS = false); per batch*head the
   // first L keys exist and key j is visible from query i iff j < L and, when
   // causal, j <= i + off (head_keys).  STR: Q, K, V, O are laid out by `lay`
   // (else [B, H, S, D] row-major).
+  // KS (key split, self-attention only): the key tiles a query tile sees are
+  // cut into at most nch chunks of at most kc tiles (fwd_key_split); item
+  // it = (query tile, chunk) * BH + head, and an item of a query tile with
+  // more than one chunk stores its unnormalised O (f32) and its (m, l) in
+  // `part` -- [nch][BH][Sp][D] then [nch][BH][Sp][2] -- for fwd_merge_kernel.
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-query blocks per item
@@ -71,16 +77,38 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   const int ldq = row_ld<STR, D>(lay.q), ldo = row_ld<STR, D>(lay.o);
   const unsigned lo = STR ? 0u : LD::lane_offset(w, lane);
   const unsigned qlo = QL::lane_offset(ldq, w, lane);
-  auto item_qt = [&](int it) { return nqt - 1 - it / BH; };
-  // Key tiles of item it: those holding a key visible from one of its
-  // queries; an item none of whose queries sees a key still takes one tile
-  // (processed fully masked), so that its zero rows are stored.
-  auto item_nkt = [&](int it) {
+  auto item_qt = [&](int it) { return nqt - 1 - (KS ? it / BH / nch : it / BH); };
+  // Key tiles of item it's query tile: those holding a key visible from one
+  // of its queries; an item none of whose queries sees a key still takes one
+  // tile (processed fully masked), so that its zero rows are stored.
+  auto qt_nkt = [&](int it) {
     int L, off;
     head_keys<CROSS>(kvlen, it % BH, H, Sq, Sk, L, off);
     const int kend = CAUSAL ? min(L, item_qt(it) * BR + BR + off) : L;
     const int n = (kend + BK - 1) / BK;
     return CROSS ? max(n, 1) : n;
+  };
+  // With KS, the chunk of item it: its first key tile kb0, its tile count
+  // and whether its query tile has more than one chunk (partial results).
+  auto item_chunk = [&](int it, int& kb0, int& ntl, bool& partial) {
+    const int full = qt_nkt(it);
+    if constexpr (KS) {
+      const int nq = (full + kc - 1) / kc;
+      const int csz = (full + nq - 1) / nq;
+      kb0 = (it / BH % nch) * csz;
+      ntl = min(csz, full - kb0);
+      partial = nq > 1;
+    } else {
+      kb0 = 0;
+      ntl = full;
+      partial = false;
+    }
+  };
+  auto item_nkt = [&](int it) {
+    int kb0, ntl;
+    bool partial;
+    item_chunk(it, kb0, ntl, partial);
+    return ntl;
   };
   // Rows a key tile may read: past them the loads read the last valid row
   // (finite, and masked), so padded rows are never read.
@@ -100,8 +128,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   int vm = 0, qmark = 0;
   RingMarks<NST> mk;
 
-  // Loader cursor: tile lkt of item lit is the next one to issue.
-  int lr = 0, lit = sched_item(sched, 0, g, G, BH), lkt = 0, lnkt = item_nkt(lit);
+  // Loader cursor: tile lkt (of lnkt, from key tile lkb) of item lit is the
+  // next one to issue.
+  int lr = 0, lit = sched_item(sched, 0, g, G, BH), lkt = 0, lnkt, lkb;
+  bool lpart;
+  item_chunk(lit, lkb, lnkt, lpart);
   int lrows = key_rows(lit);
   size_t kbase = head_off<STR, D>(lay.k, lit % BH, H, Sk);
   size_t vbase = head_off<STR, D>(lay.v, lit % BH, H, Sk);
@@ -110,16 +141,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   auto issue_next = [&](const int slot) __attribute__((always_inline)) {
     if (lit >= nitems) return;
     if constexpr (STR)
-      LD::issue_ld(smem + slot * STAGE, K + kbase, ldk, V + vbase, ldv, lkt * BK, lrows, w, lane);
+      LD::issue_ld(smem + slot * STAGE, K + kbase, ldk, V + vbase, ldv, (lkb + lkt) * BK, lrows,
+                   w, lane);
     else
-      LD::issue(smem + slot * STAGE, K + kbase, V + vbase, lkt * BK, lrows, w, lane, lo);
+      LD::issue(smem + slot * STAGE, K + kbase, V + vbase, (lkb + lkt) * BK, lrows, w, lane, lo);
     vm += LD::NLOADS;
     mk.set(slot, vm);
     if (++lkt == lnkt) {
       lit = sched_item(sched, ++lr, g, G, BH);
       lkt = 0;
       if (lit < nitems) {
-        lnkt = item_nkt(lit);
+        item_chunk(lit, lkb, lnkt, lpart);
         lrows = key_rows(lit);
         kbase = head_off<STR, D>(lay.k, lit % BH, H, Sk);
         vbase = head_off<STR, D>(lay.v, lit % BH, H, Sk);
@@ -137,7 +169,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
 
   // Consumer state: item cit (round cr), its tile kt of nkt.  (Taken before
   // the first issues, which may move the loader cursor past the first item.)
-  int cr = 0, cit = lit, kt = 0, nkt = lnkt;
+  int cr = 0, cit = lit, kt = 0, nkt = lnkt, ckb = lkb;
+  bool cpart = lpart;
   load_q(lit);
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue_next(s);
@@ -156,32 +189,34 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   // partial's factor exp2(m_p - max m) is formed once.
   auto merge = [&](char* buf, bool active) __attribute__((always_inline)) {
     if constexpr (NSPLIT > 1) {
+      // Values go through LDS four at a time (group q of lane l at float
+      // (q * 64 + l) * 4: 1 KiB per wave access, no bank conflicts); the
+      // first pass leads with one group (m, l, -, -).
       constexpr int HELP = RB * (NSPLIT - 1);
       constexpr int PERDB = HELP * 16 * 64 * 4;
-      constexpr int MLB = HELP * 2 * 64 * 4;
+      constexpr int MLB = HELP * 4 * 64 * 4;
       constexpr int DB0 = (STAGE - MLB) / PERDB < NDB ? (STAGE - MLB) / PERDB : NDB;
       constexpr int DBN = STAGE / PERDB < NDB ? STAGE / PERDB : NDB;
       static_assert(DBN >= 1, "a d-block of partials fits one stage");
       constexpr int NPASS = 1 + (NDB - DB0 + DBN - 1) / DBN;
-      float* cb = reinterpret_cast<float*>(buf);
+      f32x4* cb = reinterpret_cast<f32x4*>(buf);
       float a0 = 1.f, ap[NSPLIT - 1];
 #pragma unroll
       for (int pass = 0; pass < NPASS; ++pass) {
         const int dlo = pass == 0 ? 0 : DB0 + (pass - 1) * DBN;
         const int dhi = pass == 0 ? DB0 : (dlo + DBN < NDB ? dlo + DBN : NDB);
-        const int nv = (pass == 0 ? 2 : 0) + 16 * (dhi - dlo);  // floats per lane per helper
-        const int ov = pass == 0 ? 2 : 0;
+        const int ov = pass == 0 ? 1 : 0;          // leading (m, l) group
+        const int ng = ov + 4 * (dhi - dlo);       // groups per lane per helper
         lds_barrier();  // every wave is done reading the stage (or the previous pass)
         if (sp != 0 && active) {
-          float* dst = cb + ((qb * (NSPLIT - 1) + sp - 1) * nv) * 64 + lane;
-          if (pass == 0) {
-            dst[0] = m;
-            dst[64] = l;
-          }
+          f32x4* dst = cb + ((qb * (NSPLIT - 1) + sp - 1) * ng) * 64 + lane;
+          if (pass == 0) dst[0] = f32x4{m, l, 0.f, 0.f};
 #pragma unroll
           for (int db = dlo; db < dhi; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) dst[(ov + (db - dlo) * 16 + r) * 64] = oacc[db][r];
+            for (int j = 0; j < 4; ++j)
+              dst[(ov + (db - dlo) * 4 + j) * 64] =
+                  f32x4{oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2], oacc[db][4 * j + 3]};
         }
         lds_barrier();
         if (sp == 0 && active) {
@@ -193,9 +228,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
             float mx = m;
 #pragma unroll
             for (int p = 0; p < NSPLIT - 1; ++p) {
-              const float* src = cb + ((qb * (NSPLIT - 1) + p) * nv) * 64 + lane;
-              mp[p] = src[0];
-              lp[p] = src[64];
+              const f32x4 ml = cb[((qb * (NSPLIT - 1) + p) * ng) * 64 + lane];
+              mp[p] = ml[0];
+              lp[p] = ml[1];
               mx = fmaxf(mx, mp[p]);
             }
             const float mxs = (CROSS && mx == -INFINITY) ? 0.f : mx;
@@ -211,12 +246,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
 #pragma unroll
           for (int db = dlo; db < dhi; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              float o = oacc[db][r] * a0;
+            for (int j = 0; j < 4; ++j) {
+              f32x4 o = f32x4{oacc[db][4 * j], oacc[db][4 * j + 1], oacc[db][4 * j + 2],
+                              oacc[db][4 * j + 3]} * a0;
 #pragma unroll
               for (int p = 0; p < NSPLIT - 1; ++p)
-                o += cb[((qb * (NSPLIT - 1) + p) * nv + ov + (db - dlo) * 16 + r) * 64 + lane] * ap[p];
-              oacc[db][r] = o;
+                o += cb[((qb * (NSPLIT - 1) + p) * ng + ov + (db - dlo) * 4 + j) * 64 + lane] * ap[p];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) oacc[db][4 * j + e] = o[e];
             }
         }
       }
@@ -260,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
 #pragma unroll
       for (int j = 0; j < KPW; ++j) {
         const int kb = sp + NSPLIT * j;
-        const int kk0 = kt * BK + kb * 32;
+        const int kk0 = (ckb + kt) * BK + kb * 32;
         if (!(kk0 < cL && (!CAUSAL || kk0 <= q0 + 31 + coff))) continue;  // wave-uniform
         f32x16 sacc = dot_tile<E, D>(Kt, kb * 32 + pi32(n), h, qf, zero16());
         if (kk0 + 32 > cL || (CAUSAL && kk0 + 31 > q0 + coff)) {
@@ -318,7 +355,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     // (the tiles in flight are the next NST-1), then store O and the LSE.
     l += xhalf(l);
     merge(smem + si * STAGE, wave_active);
-    if (sp == 0 && wave_active) {
+    if (KS && cpart && sp == 0 && wave_active) {
+      // one chunk of a split query tile: O unnormalised (relative to m), and
+      // (m, l), for the merge kernel
+      if (qi < Sq) {
+        const size_t row = ((size_t)(cit / BH % nch) * BH + bh) * Sp + qi;
+        float* prow = part + row * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            store4<float>(prow + db * 32 + 8 * j + 4 * h, oacc[db][4 * j], oacc[db][4 * j + 1],
+                          oacc[db][4 * j + 2], oacc[db][4 * j + 3]);
+        if (h == 0)
+          *reinterpret_cast<float2*>(part + (size_t)nch * BH * Sp * D + row * 2) =
+              make_float2(m, l);
+      }
+      if (q0 + 31 < Sq) vm += 4 * NDB;
+    } else if (sp == 0 && wave_active) {
       // (CROSS: a row with no visible key has l = 0: O = 0, LSE = -inf)
       const float inv = (CROSS && !(l > 0.f)) ? 0.f : 1.f / l;
       if (qi < Sq) {
@@ -344,7 +398,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     cit = sched_item(sched, ++cr, g, G, BH);
     kt = 0;
     if (cit < nitems) {
-      nkt = item_nkt(cit);
+      item_chunk(cit, ckb, nkt, cpart);
       bh = cit % BH;
       q0 = item_qt(cit) * BR + qb * 32;
       head_keys<CROSS>(kvlen, bh, H, Sq, Sk, cL, coff);
@@ -369,29 +423,92 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   }
 }
 
-template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
+// The chunks of split query tiles merged in chunk order (deterministic):
+// with m* the largest chunk reference, O = sum_c 2^(m_c - m*) O_c / l and
+// l = sum_c 2^(m_c - m*) l_c, LSE = (m* + log2 l) ln 2.  One thread per four
+// columns of a query row; rows of query tiles with one chunk were written by
+// the forward kernel and are skipped.
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict__ part,
+                                                        T* __restrict__ O, float* __restrict__ LSE,
+                                                        int BH, int Sq, int Sp, int nch, int kc,
+                                                        int BR, int BK) {
+  constexpr int NG = D / 4;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long row = i / NG;
+  const int gcol = (int)(i % NG) * 4;
+  if (row >= (long long)BH * Sq) return;
+  const int bh = (int)(row / Sq), q = (int)(row % Sq);
+  const int qt = q / BR;
+  const int kend = CAUSAL ? min(Sq, qt * BR + BR) : Sq;
+  const int full = (kend + BK - 1) / BK;
+  const int nq = (full + kc - 1) / kc;
+  if (nq <= 1) return;
+  const float2* ml = reinterpret_cast<const float2*>(part + (size_t)nch * BH * Sp * D);
+  float mx = -INFINITY;
+  for (int ch = 0; ch < nq; ++ch) mx = fmaxf(mx, ml[((size_t)ch * BH + bh) * Sp + q].x);
+  float l = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int ch = 0; ch < nq; ++ch) {
+    const size_t r = ((size_t)ch * BH + bh) * Sp + q;
+    const float2 mlc = ml[r];
+    const float wgt = fast_exp2(mlc.x - mx);
+    l += mlc.y * wgt;
+    const f32x4 oc = *reinterpret_cast<const f32x4*>(part + r * D + gcol);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] += oc[e] * wgt;
+  }
+  const float inv = 1.f / l;
+  store4<T>(O + (size_t)row * D + gcol, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  if (gcol == 0 && LSE != nullptr) LSE[row] = (mx + __log2f(l)) * kLn2;
+}
+
+template <class E, int D, bool CAUSAL, bool CROSS, bool STR, bool KS>
 static hipError_t launch(const FwdArgs& a) {
   constexpr LShape SH = fwd_shape(is_bf16<E>(), D);
   constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
   using T = typename E::T;
-  constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR>;
+  constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR, KS>;
   constexpr int BR = 32 * (NW / NSPLIT);
-  const int nqt = (a.Sq + BR - 1) / BR;
-  const int nitems = a.BH * nqt;
-  const int grid = std::min(nitems, resident_workgroups<kern>(NW * 64));
-  // work of a query tile: its key tiles (with every key valid: the per-batch
-  // counts live on the device)
   constexpr int BK = 32 * NSPLIT * KPW;
-  std::vector<int> works(nqt);
-  for (int c = 0; c < nqt; ++c) {
-    const int qt = nqt - 1 - c;
+  static_assert(BR == fwd_query_tile(is_bf16<E>(), D) && BK == fwd_key_tile(is_bf16<E>(), D),
+                "tiles of the key-split choice");
+  const int nqt = (a.Sq + BR - 1) / BR;
+  // Key split (self-attention with a workspace): chunks of at most kc key
+  // tiles, nch chunk classes per query tile (class = query tile * nch + chunk).
+  int nch = 1, kc = 1 << 30;
+  if (KS) fwd_key_split(is_bf16<E>(), a.BH, a.Sq, D, CAUSAL, nch, kc);
+  const int nitems = a.BH * nqt * nch;
+  const int grid = std::min(nitems, resident_workgroups<kern>(NW * 64));
+  // work of each class: its key tiles (with every key valid: the per-batch
+  // counts live on the device); classes of chunks a query tile does not
+  // have get no work and no items
+  std::vector<int> works(nqt * nch);
+  for (int c = 0; c < nqt * nch; ++c) {
+    const int qt = nqt - 1 - c / nch, ch = c % nch;
     const int kend = CAUSAL ? std::min(a.Sk, qt * BR + BR + a.Sk - a.Sq) : a.Sk;
-    works[c] = std::max((kend + BK - 1) / BK, 1);
+    const int full = std::max((kend + BK - 1) / BK, 1);
+    const int nq = (full + kc - 1) / kc, csz = (full + nq - 1) / nq;
+    const int ntl = ch < nq ? std::min(csz, full - ch * csz) : 0;
+    works[c] = ntl > 0 ? 4 * ntl + (is_bf16<E>() ? ATTN_FWD_ITEM_COST_BF16 : ATTN_FWD_ITEM_COST_F32)
+                       : 0;
   }
   const Sched sched = make_sched(grid, a.BH, works);
+  // The chunk items exist only in a schedule table; when none can be built
+  // for this launch (grid or table size), run the forward unsplit.
+  if constexpr (KS) {
+    if (sched.M == 0) return launch<E, D, CAUSAL, CROSS, STR, false>(a);
+  }
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.o, a.lse, a.Sq, a.Sk, a.scale * kLog2e, a.BH, a.H,
-                     a.kvlen, nitems, sched, a.layout != nullptr ? *a.layout : Layout{});
+                     a.kvlen, nitems, sched, a.layout != nullptr ? *a.layout : Layout{}, nch, kc,
+                     a.part, nqt * BR);
+  if (KS) {
+    const long long threads = (long long)a.BH * a.Sq * (D / 4);
+    hipLaunchKernelGGL((fwd_merge_kernel<T, D, CAUSAL>), dim3((unsigned)((threads + 255) / 256)),
+                       dim3(256), 0, a.stream, a.part, (T*)a.o, a.lse, a.BH, a.Sq, nqt * BR, nch,
+                       kc, BR, BK);
+  }
   return hipGetLastError();
 }
 
@@ -400,10 +517,16 @@ static hipError_t launch(const FwdArgs& a) {
 template <class E, int D>
 static hipError_t launch_c(const FwdArgs& a) {
   if (a.layout != nullptr)
-    return a.causal ? launch<E, D, true, true, true>(a) : launch<E, D, false, true, true>(a);
+    return a.causal ? launch<E, D, true, true, true, false>(a)
+                    : launch<E, D, false, true, true, false>(a);
   if (a.cross)
-    return a.causal ? launch<E, D, true, true, false>(a) : launch<E, D, false, true, false>(a);
-  return a.causal ? launch<E, D, true, false, false>(a) : launch<E, D, false, false, false>(a);
+    return a.causal ? launch<E, D, true, true, false, false>(a)
+                    : launch<E, D, false, true, false, false>(a);
+  if (a.part != nullptr)  // (the caller checked that the shape is split)
+    return a.causal ? launch<E, D, true, false, false, true>(a)
+                    : launch<E, D, false, false, false, true>(a);
+  return a.causal ? launch<E, D, true, false, false, false>(a)
+                  : launch<E, D, false, false, false, false>(a);
 }
 
 template <class E>

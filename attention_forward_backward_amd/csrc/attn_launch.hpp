@@ -125,6 +125,32 @@
 #ifndef ATTN_PREP_UNR_BF16
 #define ATTN_PREP_UNR_BF16 1
 #endif
+// Work estimates of the static schedule, in quarter tile-steps: an item of
+// the forward costs 4 per key tile plus ATTN_FWD_ITEM_COST (merge, epilogue
+// and stores), an item of dK+dV 4 per query tile plus ATTN_DKDV_ITEM_COST
+// (its header tile, merge and stores).
+#ifndef ATTN_FWD_ITEM_COST_F32
+#define ATTN_FWD_ITEM_COST_F32 0
+#endif
+#ifndef ATTN_FWD_ITEM_COST_BF16
+#define ATTN_FWD_ITEM_COST_BF16 0
+#endif
+#ifndef ATTN_DKDV_ITEM_COST_F32
+#define ATTN_DKDV_ITEM_COST_F32 4
+#endif
+#ifndef ATTN_DKDV_ITEM_COST_BF16
+#define ATTN_DKDV_ITEM_COST_BF16 4
+#endif
+// Largest dS^T buffer the recommended backward workspace holds: 256 MiB,
+// the size of the last-level cache.  Measured on MI355X (backward, causal),
+// the dS path beat recomputing the scores at every length tried (f32 by
+// 20-30% up to S = 8192; bf16 by 5-15% up to S = 4096 at head_dim 64 and
+// 8192 at 128, and lost at S = 8192, head_dim 64); past this size the S^2
+// buffer costs more memory than the gain is worth, and the recommended
+// workspace becomes the O(S) minimum.
+#ifndef ATTN_DS_WORKSPACE_CAP
+#define ATTN_DS_WORKSPACE_CAP (256u << 20)
+#endif
 // Query-chunk split of the dK+dV pass (dkdv_query_chunks): shapes with
 // fewer (key tile, head) items than these are split.  At B1 H16 S1024 D128
 // causal (256 items, the longest walking 16 query tiles) two chunks took the
@@ -188,6 +214,7 @@ struct FwdArgs {
   float scale;
   hipStream_t stream;
   const Layout* layout = nullptr;  // strides of q, k, v, o; null: [B, H, S, D] row-major
+  float* part = nullptr;  // key-split partials (fwd_key_split), or null: no split
 };
 
 struct BwdArgs {
@@ -287,7 +314,8 @@ inline Sched build_sched(int G, int BH, const std::vector<int>& works, int cux) 
   std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return works[a] > works[b]; });
   std::vector<long> load(M, 0);
   std::vector<std::vector<uint16_t>> lists(M);
-  for (int c : order)
+  for (int c : order) {
+    if (works[c] <= 0) continue;  // a class without work has no items
     for (int u = 0; u < hx; ++u) {
       int bcu = 0;
       long bsum = -1;
@@ -302,6 +330,7 @@ inline Sched build_sched(int G, int BH, const std::vector<int>& works, int cux) 
       load[bj] += works[c];
       lists[bj].push_back((uint16_t)((c << 8) | u));
     }
+  }
   size_t R = 0;
   for (const auto& l : lists) R = std::max(R, l.size());
   if ((R - 1) * M > (size_t)kSchedEntries) return s;
@@ -368,6 +397,46 @@ constexpr LShape dqg_shape(bool bf16, int D) {  // dQ GEMM over the stored dS^T
                         : LShape{ATTN_DQG_NW_BF16, ATTN_DQG_NSPLIT_BF16, 1, ATTN_DQG_NST_BF16})
               : (D < 64 ? small_d_shape(ATTN_DQG_NST_F32)
                         : LShape{ATTN_DQG_NW_F32, ATTN_DQG_NSPLIT_F32, 1, ATTN_DQG_NST_F32});
+}
+
+// Tiles of the forward kernel: queries per item, keys per staged tile.
+constexpr int fwd_query_tile(bool bf16, int D) {
+  return 32 * (fwd_shape(bf16, D).nw / fwd_shape(bf16, D).nsplit);
+}
+constexpr int fwd_key_tile(bool bf16, int D) {
+  return 32 * fwd_shape(bf16, D).nsplit * fwd_shape(bf16, D).kpw;
+}
+
+// Key split of the forward for causal or non-causal self-attention whose
+// longest query tile walks far more key tiles than a balanced share (few
+// long heads): with W the key tiles of all items, the share of one of 256
+// CUs is kc = ceil(W / 256) tiles; when the longest query tile has more than
+// 1.5 kc key tiles, every query tile with more than kc is cut into
+// ceil(n / kc) chunks of equal size (nch = the most chunks), each its own
+// item with partial results, merged afterwards.  A function of the shape
+// alone, so that the workspace size and the launch agree; false (nch = 1):
+// no split.  The chunk items need the static schedule's table, which pins
+// heads to XCDs, so B*H must be a multiple of 8.
+inline bool fwd_key_split(bool bf16, long long BH, int S, int D, bool causal, int& nch, int& kc) {
+  nch = 1;
+  kc = 1 << 30;
+  if (BH % 8 != 0) return false;
+  const int BR = fwd_query_tile(bf16, D), BK = fwd_key_tile(bf16, D);
+  const int nqt = (S + BR - 1) / BR;
+  long long W = 0;
+  int longest = 0;
+  for (int qt = 0; qt < nqt; ++qt) {
+    const int kend = causal ? std::min(S, qt * BR + BR) : S;
+    const int n = (kend + BK - 1) / BK;
+    W += n;
+    longest = std::max(longest, n);
+  }
+  W *= BH;
+  const long long share = (W + 255) / 256;
+  if (share < 2 || 2LL * longest <= 3 * share || share >= longest) return false;
+  kc = (int)share;
+  nch = (longest + kc - 1) / kc;
+  return nch > 1;
 }
 
 // Tiles of the dK+dV kernel: keys per item, queries per staged tile.

@@ -436,7 +436,9 @@ def timed_graph(fn, per_graph=20, replays=30):
 def configs_section(args, log) -> dict:
     """fwd, bwd and fwd+bwd of every self-attention workload (tiny, small
     decoder, decoder step, long context, ragged encoder) in each of its
-    contracts, GPU time from HIP-graph replays (eager calls with --no-graph):
+    contracts (the forward with the key split where attn_fwd_workspace_size
+    gives it a workspace), GPU time from HIP-graph replays (eager calls with
+    --no-graph):
     credited TFLOP/s, its fraction of the contract's dense MFMA peak and of
     the attainable roofline min(peak, FLOP per compulsory byte x 8 TB/s), and
     the compulsory HBM bytes (every input read once, every output written
@@ -465,9 +467,12 @@ def configs_section(args, log) -> dict:
             code = afb.ATTN_BF16 if dt == "bf16" else afb.ATTN_F32
             ws = torch.empty(afb.attn_bwd_workspace_size(code, B, H, S, D, cfg.causal),
                              dtype=torch.uint8, device="cuda")
+            # the key-split forward where the shape takes it (few long heads)
+            fws_bytes = afb.attn_fwd_workspace_size(code, B, H, S, D, cfg.causal)
+            fws = torch.empty(fws_bytes, dtype=torch.uint8, device="cuda") if fws_bytes else None
 
             def fwd():
-                afb.attn_fwd(q, k, v, o, lse, cfg.causal, cfg.scale, None)
+                afb.attn_fwd_ws(q, k, v, o, lse, fws, cfg.causal, cfg.scale, None)
 
             def bwd():
                 afb.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, cfg.causal, cfg.scale, None)
@@ -498,8 +503,9 @@ def configs_section(args, log) -> dict:
                          "frac_of_attainable": round(tf / attain, 4),
                          "compulsory_bytes": nbytes[ph],
                          "gbs": round(nbytes[ph] / (ms[ph] * 1e-3) / 1e9, 1)}
+            r["forward_key_split"] = bool(fws_bytes)
             rec[dt] = r
-            del q, k, v, do, o, dq, dk, dv, lse, ws
+            del q, k, v, do, o, dq, dk, dv, lse, ws, fws
             torch.cuda.empty_cache()
         out[name] = rec
     return out

@@ -103,6 +103,30 @@ attn_status_t attn_fwd(attn_dtype_t dtype,
                        int causal, float scale, void* stream);
 
 /*
+ * Forward with a key split, for few long heads (the minimal-latency long
+ * context of the pages' Section 4.3): when the longest query tile of a head
+ * walks far more key tiles than a balanced share of the GPU, each such query
+ * tile's keys are cut into chunks processed as separate work items whose
+ * partial (O, row maximum, row sum) go to the workspace and are merged in
+ * chunk order by a second kernel (deterministic).  Self-attention, [B,H,S,D]
+ * layout, the arguments and errors of attn_fwd plus:
+ *   workspace   NULL, or DEVICE memory, 16-byte aligned, contents ignored;
+ *               the split is used iff workspace_bytes >=
+ *               attn_fwd_workspace_size(), else the call is attn_fwd.
+ * attn_fwd_workspace_size returns 0 for shapes that are not split (enough
+ * work items already) or rejected, else
+ *   chunks * B*H * ceil(S/64)*64 * (head_dim + 2) * 4 bytes (rounded up to 256).
+ * O and LSE equal attn_fwd's up to the summation order of the chunks.
+ */
+size_t attn_fwd_workspace_size(attn_dtype_t dtype, int batch, int heads, int seq,
+                               int head_dim, int causal);
+attn_status_t attn_fwd_ws(attn_dtype_t dtype,
+                          const void* q, const void* k, const void* v,
+                          void* o, float* lse, void* workspace, size_t workspace_bytes,
+                          int batch, int heads, int seq, int head_dim,
+                          int causal, float scale, void* stream);
+
+/*
  * Workspace of the backward, in bytes (pure host functions; 0 for arguments
  * attn_bwd would reject).  The pages' runtime plans its buffers statically
  * and allocates nothing while a step runs (Section 3.5, static execution and
@@ -119,12 +143,18 @@ attn_status_t attn_fwd(attn_dtype_t dtype,
  *      over chunks of the queries, [2][C][B*H][S][D] with C chunks chosen
  *      from the shape alone (each chunk is then its own work item and the
  *      chunks are added up in a fixed order, so results stay deterministic).
- *   attn_bwd_workspace_size      recommended size: 1 + 2 + 3
+ *   attn_bwd_workspace_size      recommended size: 1 + 2 + 3 while part 2
+ *                                (which grows as S^2) is at most 256 MiB,
+ *                                the last-level cache; beyond it 1 + 3, so
+ *                                the recommended size stays O(S) for long
+ *                                sequences (the dS path was measured 20-30%
+ *                                faster in f32 and 5-15% in bf16 there, so a
+ *                                caller with memory to spare may still give
+ *                                1 + 2 + 3 bytes)
  *   attn_bwd_workspace_size_min  minimum size: 1 (dQ recomputes P and dP)
  * The backward takes the dS path iff workspace_bytes >= the size of 1 + 2,
  * and the query-chunk split iff the partials fit as well (after 2 on the dS
- * path, else after 1).  The recommended size grows as S^2, so very long
- * sequences can use the minimum instead.
+ * path, else after 1).
  */
 size_t attn_bwd_workspace_size(attn_dtype_t dtype, int batch, int heads,
                                int seq, int head_dim, int causal);

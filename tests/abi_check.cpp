@@ -111,10 +111,17 @@ int main() {
   // workspace sizes: 0 for rejected shapes, monotone and overflow-free at the edges
   EXPECT(attn_bwd_workspace_size(ATTN_F32, 1, 1, 8, 48, 1), 0);
   EXPECT(attn_bwd_workspace_size_min(ATTN_F32, 0, 1, 8, 64, 1), 0);
+  // beyond the cap on the dS/dP layout the recommendation falls back to the minimum
   const size_t big = attn_bwd_workspace_size(ATTN_F32, 1, 1, 1 << 20, 128, 1);
   const size_t bigmin = attn_bwd_workspace_size_min(ATTN_F32, 1, 1, 1 << 20, 128, 1);
-  if (!(big > bigmin && bigmin == 2u * (1u << 20) * 4u)) {
+  if (!(big == bigmin && bigmin == 2u * (1u << 20) * 4u)) {
     std::printf("FAIL: workspace sizes at S = 2^20: %zu, %zu\n", big, bigmin);
+    ++fails;
+  }
+  const size_t mid = attn_bwd_workspace_size(ATTN_F32, 1, 16, 2048, 128, 1);
+  const size_t midmin = attn_bwd_workspace_size_min(ATTN_F32, 1, 16, 2048, 128, 1);
+  if (!(mid > midmin && mid - midmin <= (size_t)ATTN_DS_WORKSPACE_CAP)) {
+    std::printf("FAIL: workspace sizes at S = 2048: %zu, %zu\n", mid, midmin);
     ++fails;
   }
   if (attn_bwd_cross_workspace_size(ATTN_BF16, 2, 8, 4096, 77, 64, 0) <=

@@ -95,6 +95,7 @@ struct FwdCase {
   bool causal, cross;
   std::vector<int> kvlen;  // per batch (cross only; empty: all Sk)
   bool lse;
+  bool ks = false;  // key split (fwd_key_split), self-attention only
 };
 
 template <class E, int D>
@@ -105,15 +106,27 @@ bool model_fwd(const FwdCase& c, int G) {
   using LD = StageLoader<E, D, BK, NW>;
   using QL = TileLoader<E, D, BR, NW>;
   const int Sq = c.Sq, Sk = c.cross ? c.Sk : c.Sq, BH = c.BH, H = c.H;
-  const int nqt = (Sq + BR - 1) / BR, nitems = BH * nqt;
+  const int nqt = (Sq + BR - 1) / BR;
+  int nch = 1, kc = 1 << 30;
+  if (c.ks && !fwd_key_split(is_bf16<E>(), BH, Sq, D, c.causal, nch, kc)) return true;
+  const int nitems = BH * nqt * nch;
   G = std::min(G, nitems);
-  std::vector<int> works(nqt);
-  for (int cc = 0; cc < nqt; ++cc) {
-    const int qt = nqt - 1 - cc;
+  std::vector<int> works(nqt * nch);
+  for (int cc = 0; cc < nqt * nch; ++cc) {
+    const int qt = nqt - 1 - cc / nch, ch = cc % nch;
     const int kend = c.causal ? std::min(Sk, qt * BR + BR + Sk - Sq) : Sk;
-    works[cc] = std::max((kend + BK - 1) / BK, 1);
+    const int full = std::max((kend + BK - 1) / BK, 1);
+    const int nq = (full + kc - 1) / kc, csz = (full + nq - 1) / nq;
+    const int ntl = ch < nq ? std::min(csz, full - ch * csz) : 0;
+    works[cc] = ntl > 0 ? 4 * ntl + (is_bf16<E>() ? ATTN_FWD_ITEM_COST_BF16 : ATTN_FWD_ITEM_COST_F32)
+                        : 0;
   }
   const Sched sched = build_sched(G, BH, works, 32);
+  if (c.ks && sched.M == 0) {  // the launcher then runs the forward unsplit
+    FwdCase u = c;
+    u.ks = false;
+    return model_fwd<E, D>(u, G);
+  }
   auto keys = [&](int bh, int& L, int& off) {
     L = Sk;
     off = 0;
@@ -122,13 +135,16 @@ bool model_fwd(const FwdCase& c, int G) {
       off = L - Sq;
     }
   };
-  auto item_qt = [&](int it) { return nqt - 1 - it / BH; };
-  auto item_nkt = [&](int it) {
+  auto item_qt = [&](int it) { return nqt - 1 - it / BH / nch; };
+  auto item_nkt = [&](int it) {  // (the chunk's tiles, as the kernel's item_chunk)
     int L, off;
     keys(it % BH, L, off);
     const int kend = c.causal ? std::min(L, item_qt(it) * BR + BR + off) : L;
     const int n = (kend + BK - 1) / BK;
-    return c.cross ? std::max(n, 1) : n;
+    const int full = c.cross ? std::max(n, 1) : n;
+    const int nq = (full + kc - 1) / kc, csz = (full + nq - 1) / nq;
+    const int kb0 = (it / BH % nch) * csz;
+    return std::min(csz, full - kb0);
   };
   for (int g = 0; g < G; ++g) {
     if (sched_item(sched, 0, g, G, BH) >= nitems) continue;
@@ -252,7 +268,8 @@ bool model_dkdv(const BwdCase& c, int G) {
     const int kt = cc / nqs, qc = cc % nqs;
     const int fq = c.causal ? std::min(nqt, std::max(0, kt * BKV - offw) / BQ) : 0;
     const int lo = std::max(fq, qc * qpc), hi = std::min(nqt, (qc + 1) * qpc);
-    works[cc] = 1 + std::max(0, hi - lo);
+    works[cc] = 4 * std::max(0, hi - lo) +
+                (is_bf16<E>() ? ATTN_DKDV_ITEM_COST_BF16 : ATTN_DKDV_ITEM_COST_F32);
   }
   const Sched sched = build_sched(G, BH, works, 32);
   auto keys = [&](int bh, int& L, int& off) {
@@ -428,6 +445,25 @@ int main(int argc, char** argv) {
             }
           }
   std::printf("self-attention: %d cases ok\n", cases);
+  // key split: few long heads (every chunked shape the rule produces for
+  // these lengths), both storage types, every head_dim
+  int kcases = 0;
+  for (const bool bf16 : {false, true})
+    for (const int D : {32, 64, 128})
+      for (const int S : {1000, 1024, 1500, 2048})
+        for (const int BH : {1, 2, 8, 16})
+          for (const bool causal : {true, false})
+            for (const int G : {512, 256, 64}) {
+              FwdCase f{bf16, D, BH, BH, S, S, causal, false, {}, true, true};
+              const bool ok = bf16 ? fwd_d<EBF16>(f, G) : fwd_d<EF32>(f, G);
+              ++kcases;
+              if (!ok) {
+                std::printf("case: key split %s D%d BH%d S%d causal%d G%d\n", bf16 ? "bf16" : "f32",
+                            D, BH, S, causal, G);
+                return 1;
+              }
+            }
+  std::printf("key split: %d cases ok\n", kcases);
   // cross-attention: separate lengths, padded keys (0, short, full), causal
   // alignment at the end of the valid keys, query-chunk split
   struct X { int Sq, Sk; std::vector<int> kv; int nqs; };

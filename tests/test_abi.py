@@ -15,7 +15,8 @@ MIS = 0x10008           # 8-byte aligned only
 def test_library_loads_and_exports_header_symbols():
     L = afb.lib()
     declared = afb.declared_symbols()
-    assert set(declared) == {"attn_fwd", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_prep",
+    assert set(declared) == {"attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_size", "attn_bwd",
+                             "attn_bwd_noalloc", "attn_bwd_prep",
                              "attn_bwd_dq",
                              "attn_bwd_dkdv", "attn_bwd_workspace_size",
                              "attn_bwd_workspace_size_min", "attn_fwd_cross", "attn_bwd_cross",
@@ -63,6 +64,29 @@ def test_bwd_noalloc_validation():
     assert _bwd_noalloc(causal=3) == 1 and _bwd_noalloc(scale=math.nan) == 1
     assert _bwd_noalloc(B=1, H=256, S=(1 << 16) + 1) == 3
     assert _bwd_noalloc(B=4, H=64, S=(1 << 16) + 8, D=32) == 3
+
+
+def test_fwd_key_split_workspace():
+    """The key-split forward's workspace: used for few long heads, 0 for
+    shapes with enough work items (or rejected ones); a misaligned workspace
+    is rejected, a NULL one means the plain forward."""
+    L = afb.lib()
+    for dt in (0, 1, 2):
+        n = L.attn_fwd_workspace_size(dt, 1, 16, 1024, 128, 1)
+        # two chunks of the 16 query tiles' keys, (D + 2) floats per row
+        assert n == 2 * 16 * 1024 * (128 + 2) * 4, (dt, n)
+        assert L.attn_fwd_workspace_size(dt, 8, 12, 512, 64, 1) == 0  # decoder step: not split
+        assert L.attn_fwd_workspace_size(dt, 1, 8, 1024, 64, 0) > 0    # non-causal long heads
+        assert L.attn_fwd_workspace_size(dt, 1, 2, 2048, 64, 0) == 0   # B*H not a multiple of 8
+    assert L.attn_fwd_workspace_size(0, 1, 16, 1024, 48, 1) == 0
+    assert L.attn_fwd_workspace_size(0, 1, 16, 1, 128, 1) == 0        # one-query heads
+    ws_mis = MIS
+    assert L.attn_fwd_ws(0, FAKE, FAKE, FAKE, FAKE, FAKE, ws_mis, 1 << 30, 1, 16, 1024, 128, 1,
+                         0.1, None) == 1
+    assert L.attn_fwd_ws(0, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 1, 16, 1024, 128, 1,
+                         0.1, None) == 1
+    assert L.attn_fwd_ws(0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, 1, 16, 1024, 128, 1,
+                         -0.1, None) == 1
 
 
 def test_fwd_validation():
