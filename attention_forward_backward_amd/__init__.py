@@ -17,6 +17,7 @@ __all__ = ["AttnError", "lib", "attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_si
            "attn_bwd_dq", "attn_bwd_workspace_size", "attn_bwd_workspace_size_min",
            "attn_fwd_cross", "attn_bwd_cross", "attn_bwd_cross_workspace_size",
            "attn_bwd_cross_workspace_size_min",
+           "attn_fwd_rope", "attn_bwd_rope",
            "attn_status_string", "attn_version", "conv2d_fwd", "conv2d_bwd_data",
            "conv2d_bwd_filter", "conv2d_bwd_filter_workspace_size", "conv2d_out_size",
            "ATTN_F32", "ATTN_BF16", "ATTN_F32_BF16FWD", "STATUS", "LIB_PATH", "HEADER_PATH"]
@@ -61,6 +62,10 @@ _SIGS = {
                               ctypes.POINTER(ctypes.c_longlong), _I, _F, _P]),
     "attn_bwd_strided": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I,
                               _I, _P, ctypes.POINTER(ctypes.c_longlong), _I, _F, _P]),
+    "attn_fwd_rope": (_I, [_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                           ctypes.POINTER(ctypes.c_longlong), _P, _P, _I, _I, _I, _F, _P]),
+    "attn_bwd_rope": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I,
+                           ctypes.POINTER(ctypes.c_longlong), _P, _P, _I, _I, _I, _F, _P]),
     "attn_rope_copy": (_I, [_I, _P, ctypes.POINTER(ctypes.c_longlong), _P,
                             ctypes.POINTER(ctypes.c_longlong), _P, _P, _I, _I, _I, _I, _I, _I,
                             _I, _P]),
@@ -459,6 +464,70 @@ def attn_rope_copy(src, src_offset: int, src_strides, dst, dst_offset: int, dst_
                                 rows, int(pos_offset), B, H, S, D, int(bool(transpose)),
                                 _stream(stream))
     _raise("attn_rope_copy", code)
+
+
+def _rope_tables(cos, sin, half: int):
+    import torch
+    for name, t in (("cos", cos), ("sin", sin)):
+        if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous() \
+                or t.dim() != 2 or t.shape[1] != half:
+            raise ValueError(f"{name} must be a contiguous float32 device tensor [P, {half}]")
+    if cos.shape != sin.shape:
+        raise ValueError("cos and sin tables differ in shape")
+    return int(cos.shape[0]), cos.data_ptr(), sin.data_ptr()
+
+
+def _check_qk_rot(qk_rot, shape, dtype):
+    B, H, S, D = shape
+    if not qk_rot.is_cuda or not qk_rot.is_contiguous() or qk_rot.dtype != dtype \
+            or qk_rot.numel() != 2 * B * H * S * D:
+        raise ValueError(f"qk_rot must be a contiguous {dtype} device tensor of "
+                         f"2*B*H*S*D = {2 * B * H * S * D} elements")
+
+
+def attn_fwd_rope(q, k, v, o, lse, qk_rot, cos, sin, causal: bool, scale: float,
+                  pos_offset: int = 0, stream=None, bf16_operands: bool = False) -> None:
+    """Self-attention forward with RoPE on Q and K fused into the kernels:
+    q, k, v, o are [B,H,S,D] views of any layout with a contiguous head
+    dimension (as attn_fwd_strided); cos, sin [P, D/2] float32 tables (query
+    and key i at row pos_offset + i); qk_rot a [2, B, H, S, D] tensor of the
+    inputs' dtype that receives the turned Q and K for attn_bwd_rope."""
+    B, H, S, D = q.shape
+    st = _view_strides({"q": q, "k": k, "v": v, "o": o}, (B, H, S, D), q.dtype)
+    _check_qk_rot(qk_rot, (B, H, S, D), q.dtype)
+    if lse is not None:
+        _check_f32({"lse": lse}, (B, H, S))
+    rows, cp, sp = _rope_tables(cos, sin, D // 2)
+    code = _dtype_code(q)
+    if bf16_operands:
+        if code != ATTN_F32:
+            raise TypeError("bf16_operands applies to float32 tensors")
+        code = ATTN_F32_BF16FWD
+    code = lib().attn_fwd_rope(code, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               0 if lse is None else lse.data_ptr(), qk_rot.data_ptr(), B, H, S, D,
+                               (ctypes.c_longlong * 12)(*st), cp, sp, rows, int(pos_offset),
+                               int(causal), float(scale), _stream(stream))
+    _raise("attn_fwd_rope", code)
+
+
+def attn_bwd_rope(qk_rot, v, o, dout, lse, dq, dk, dv, workspace, cos, sin, causal: bool,
+                  scale: float, pos_offset: int = 0, stream=None) -> None:
+    """Backward of attn_fwd_rope: reads the turned Q and K from qk_rot,
+    writes dQ and dK with respect to the unturned inputs (and dV) into
+    [B,H,S,D] views of any layout with a contiguous head dimension; the
+    workspace is sized by attn_bwd_workspace_size."""
+    B, H, S, D = v.shape
+    st = _view_strides({"v": v, "o": o, "dout": dout, "dq": dq, "dk": dk, "dv": dv},
+                       (B, H, S, D), v.dtype)
+    _check_qk_rot(qk_rot, (B, H, S, D), v.dtype)
+    _check_f32({"lse": lse}, (B, H, S))
+    rows, cp, sp = _rope_tables(cos, sin, D // 2)
+    code = lib().attn_bwd_rope(_dtype_code(v), qk_rot.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                               dv.data_ptr(), workspace.data_ptr(), _nbytes(workspace), B, H, S,
+                               D, (ctypes.c_longlong * 18)(*st), cp, sp, rows, int(pos_offset),
+                               int(causal), float(scale), _stream(stream))
+    _raise("attn_bwd_rope", code)
 
 
 # ---------------------------------------------------------------- convolution (include/conv.h)

@@ -177,6 +177,15 @@ attn::Str3 str3(const long long* st) {
   return attn::Str3{(int)st[0], (int)st[1], (int)st[2]};
 }
 
+// RoPE tables: both given, 16-byte aligned, rows pos_offset .. pos_offset +
+// seq - 1 inside [0, table_rows).
+bool check_tables(const float* cos_table, const float* sin_table, int table_rows, int pos_offset,
+                  int seq) {
+  if (cos_table == nullptr || sin_table == nullptr) return false;
+  if (!aligned16(cos_table) || !aligned16(sin_table)) return false;
+  return pos_offset >= 0 && table_rows >= 0 && (int64_t)pos_offset + seq <= table_rows;
+}
+
 // Workspace of the key-split forward: unnormalised O partials [nch][B*H][Sp][D]
 // and (m, l) pairs [nch][B*H][Sp][2], float32; 0 when the shape is not split.
 size_t fwd_ws_bytes(attn_dtype_t dtype, int batch, int heads, int seq, int head_dim, int causal) {
@@ -193,7 +202,8 @@ size_t fwd_ws_bytes(attn_dtype_t dtype, int batch, int heads, int seq, int head_
 attn_status_t fwd_impl(attn_dtype_t dtype, const void* q, const void* k, const void* v, void* o,
                        float* lse, int batch, int heads, int sq, int sk, int head_dim,
                        const int* kvlen, int causal, float scale, void* stream,
-                       const attn::Layout* layout = nullptr, float* part = nullptr) {
+                       const attn::Layout* layout = nullptr, float* part = nullptr,
+                       const attn::RopeTab* rope = nullptr) {
   attn_status_t st = check_shape(dtype, batch, heads, sq, sk, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
   if ((st = check_ptrs({q, k, v, o})) != ATTN_OK) return st;
@@ -210,6 +220,7 @@ attn_status_t fwd_impl(attn_dtype_t dtype, const void* q, const void* k, const v
   a.stream = static_cast<hipStream_t>(stream);
   a.layout = layout;
   a.part = part;
+  if (rope != nullptr) a.rope = *rope;
   return from_hip(attn::launch_fwd(a));
 }
 
@@ -217,15 +228,17 @@ attn_status_t bwd_impl(attn_dtype_t dtype, const void* q, const void* k, const v
                        const void* o, const void* dout, const float* lse, void* dq, void* dk,
                        void* dv, void* workspace, size_t workspace_bytes, int batch, int heads,
                        int sq, int sk, int head_dim, const int* kvlen, int causal, float scale,
-                       void* stream, const attn::Layout* layout = nullptr) {
+                       void* stream, const attn::Layout* layout = nullptr,
+                       const attn::RopeTab* rope = nullptr) {
   attn_status_t st = check_shape(dtype, batch, heads, sq, sk, head_dim, causal, scale, true);
   if (st != ATTN_OK) return st;
   if ((st = check_ptrs({q, k, v, o, dout, lse, dq, dk, dv, workspace})) != ATTN_OK) return st;
   if (kvlen != nullptr && !aligned4(kvlen)) return ATTN_ERR_INVALID_ARG;
   if (workspace_bytes < ws_min_bytes(batch, heads, sq)) return ATTN_ERR_WORKSPACE;
-  const attn::BwdArgs a = make_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace,
-                                   workspace_bytes, batch, heads, sq, sk, head_dim, kvlen, causal,
-                                   scale, stream, layout);
+  attn::BwdArgs a = make_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace,
+                             workspace_bytes, batch, heads, sq, sk, head_dim, kvlen, causal, scale,
+                             stream, layout);
+  if (rope != nullptr) a.rope = *rope;
   if ((st = from_hip(attn::launch_bwd_prep(a))) != ATTN_OK) return st;
   if ((st = from_hip(attn::launch_bwd_dkdv(a))) != ATTN_OK) return st;
   return from_hip(attn::launch_bwd_dq(a));
@@ -420,6 +433,77 @@ attn_status_t attn_bwd_strided(attn_dtype_t dtype, const void* q, const void* k,
                   heads, seq_q, seq_k, head_dim, kv_len, causal, scale, stream, &lay);
 }
 
+attn_status_t attn_fwd_rope(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                            void* o, float* lse, void* qk_rot, int batch, int heads, int seq,
+                            int head_dim, const long long* strides, const float* cos_table,
+                            const float* sin_table, int table_rows, int pos_offset, int causal,
+                            float scale, void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, seq, seq, head_dim, causal, scale, true);
+  if (st != ATTN_OK) return st;
+  if ((st = check_ptrs({q, k, v, o, qk_rot})) != ATTN_OK) return st;
+  if (lse != nullptr && !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  if (strides == nullptr) return ATTN_ERR_INVALID_ARG;
+  for (int t = 0; t < 4; ++t)
+    if (!check_strides(strides + 3 * t, batch, heads, seq, head_dim, t == 3))
+      return ATTN_ERR_INVALID_ARG;
+  if (!check_tables(cos_table, sin_table, table_rows, pos_offset, seq)) return ATTN_ERR_INVALID_ARG;
+  const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
+  const long long sd = (long long)seq * head_dim;
+  const long long rs[3] = {heads * sd, sd, head_dim};  // [B, H, S, D] row-major
+  if (!check_strides(rs, batch, heads, seq, head_dim, true)) return ATTN_ERR_INVALID_ARG;
+  attn::Layout lay{};
+  lay.q = str3(strides);
+  lay.k = str3(strides + 3);
+  lay.v = str3(strides + 6);
+  lay.o = str3(strides + 9);
+  // Q and K are turned inside the forward kernel as their tiles arrive; it
+  // stores them turned into qk_rot for the backward
+  attn::RopeTab rt;
+  rt.cos = cos_table;
+  rt.sin = sin_table;
+  rt.pos = pos_offset;
+  rt.out = qk_rot;
+  rt.kout = static_cast<char*>(qk_rot) + (size_t)batch * heads * sd * esz;
+  return fwd_impl(dtype, q, k, v, o, lse, batch, heads, seq, seq, head_dim, nullptr, causal,
+                  scale, stream, &lay, nullptr, &rt);
+}
+
+attn_status_t attn_bwd_rope(attn_dtype_t dtype, const void* qk_rot, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, int batch, int heads, int seq,
+                            int head_dim, const long long* strides, const float* cos_table,
+                            const float* sin_table, int table_rows, int pos_offset, int causal,
+                            float scale, void* stream) {
+  attn_status_t st = check_shape(dtype, batch, heads, seq, seq, head_dim, causal, scale, true);
+  if (st != ATTN_OK) return st;
+  if (qk_rot == nullptr || !aligned16(qk_rot) || strides == nullptr) return ATTN_ERR_INVALID_ARG;
+  // v, o, dout, dq, dk, dv
+  for (int t = 0; t < 6; ++t)
+    if (!check_strides(strides + 3 * t, batch, heads, seq, head_dim, t >= 3))
+      return ATTN_ERR_INVALID_ARG;
+  if (!check_tables(cos_table, sin_table, table_rows, pos_offset, seq)) return ATTN_ERR_INVALID_ARG;
+  const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
+  const long long sd = (long long)seq * head_dim;
+  const long long rs[3] = {heads * sd, sd, head_dim};
+  if (!check_strides(rs, batch, heads, seq, head_dim, true)) return ATTN_ERR_INVALID_ARG;
+  const void* krot = static_cast<const char*>(qk_rot) + (size_t)batch * heads * sd * esz;
+  attn::Layout lay{};
+  lay.q = str3(rs);
+  lay.k = str3(rs);
+  lay.v = str3(strides);
+  lay.o = str3(strides + 3);
+  lay.dout = str3(strides + 6);
+  lay.dq = str3(strides + 9);
+  lay.dk = str3(strides + 12);
+  lay.dv = str3(strides + 15);
+  attn::RopeTab rt;
+  rt.cos = cos_table;
+  rt.sin = sin_table;
+  rt.pos = pos_offset;
+  return bwd_impl(dtype, qk_rot, krot, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+                  batch, heads, seq, seq, head_dim, nullptr, causal, scale, stream, &lay, &rt);
+}
+
 attn_status_t attn_rope_copy(attn_dtype_t dtype, const void* src, const long long* src_strides,
                              void* dst, const long long* dst_strides, const float* cos_table,
                              const float* sin_table, int table_rows, int pos_offset, int batch,
@@ -474,6 +558,6 @@ const char* attn_status_string(attn_status_t s) {
   return "unknown status";
 }
 
-const char* attn_version(void) { return "0.7.0"; }
+const char* attn_version(void) { return "0.8.0"; }
 
 }  // extern "C"

@@ -36,14 +36,14 @@
 namespace attn {
 
 template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS, bool CROSS,
-          bool QSPLIT, bool STR>
+          bool QSPLIT, bool STR, bool ROPE>
 __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_F32 : 1) void bwd_dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
     typename E::T* __restrict__ dSout, int SPq, int SPk, int Sq, int Sk_, int Lws, float c,
     float scale, int BH, int H, const int* __restrict__ kvlen, float* __restrict__ part, int nqs_,
-    int qpc_, int nitems, const Sched sched, const Layout lay) {
+    int qpc_, int nitems, const Sched sched, const Layout lay, const RopeTab rope) {
   // Queries Sq, keys Sk (one length in self-attention, CROSS = false); per
   // batch*head the first L keys exist and key j is visible from query i iff
   // j < L and, when causal, j <= i + off (head_keys).  Lws: offset of the
@@ -55,6 +55,9 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   // QSPLIT there is one chunk of every query tile and dK, dV are stored.
   // STR: Q, K, V, dO, dK, dV are laid out by `lay` (else [B, H, S, D]
   // row-major; the workspace is always packed).
+  // ROPE (STR): Q and K hold RoPE-turned rows; dK leaves turned back by the
+  // transposed rotation of key j (table row rope.pos + j) -- here, or with
+  // QSPLIT in the reduce kernel.
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-key blocks per item
@@ -235,14 +238,23 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
         T* dv = dV + head_off<STR, D>(lay.dv, bh, H, Sk);
         const int lddk = row_ld<STR, D>(lay.dk), lddv = row_ld<STR, D>(lay.dv);
         if (key < Sk) {
+          float ks = scale;
+          if constexpr (ROPE) {
+            // dK of the turned rows, scaled, then turned back in f32
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) dkacc[db] *= scale;
+            const size_t tr = (size_t)(rope.pos + key) * (D / 2);
+            rope_back_acc<D>(dkacc, rope.cos + tr, rope.sin + tr, h);
+            ks = 1.f;
+          }
 #pragma unroll
           for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int d = db * 32 + 8 * j + 4 * h;
-              store4<T>(dk + (size_t)key * lddk + d, dkacc[db][4 * j] * scale,
-                        dkacc[db][4 * j + 1] * scale, dkacc[db][4 * j + 2] * scale,
-                        dkacc[db][4 * j + 3] * scale);
+              store4<T>(dk + (size_t)key * lddk + d, dkacc[db][4 * j] * ks,
+                        dkacc[db][4 * j + 1] * ks, dkacc[db][4 * j + 2] * ks,
+                        dkacc[db][4 * j + 3] * ks);
               store4<T>(dv + (size_t)key * lddv + d, dvacc[db][4 * j], dvacc[db][4 * j + 1],
                         dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
             }
@@ -418,13 +430,50 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
 // in chunk order (deterministic); four elements per thread, 64 threads per
 // workgroup (a small tensor spread over the CUs), the loads of eight chunks
 // issued before their sums.
-template <class T, int D, bool STR>
+template <class T, int D, bool STR, bool ROPE>
 __global__ __launch_bounds__(64) void bwd_dkdv_reduce_kernel(const float* __restrict__ part,
                                                              T* __restrict__ dK,
                                                              T* __restrict__ dV, int nqs,
                                                              long long nel4, int Sk, int H,
-                                                             const Layout lay) {
+                                                             const Layout lay, const RopeTab rope) {
   // (partials are [B*H][Sk][D] packed; STR: dK, dV are laid out by `lay`)
+  // ROPE: thread i sums the four columns it would own and the four D/2 on
+  // (the pairs of the rotation), turns dK back, and stores both; the
+  // launch covers half the groups.
+  if constexpr (ROPE) {
+    const long long i = (long long)blockIdx.x * 64 + threadIdx.x;
+    if (i >= nel4 / 2) return;
+    const long long row = i / (D / 8);
+    const int col = (int)(i % (D / 8)) * 4;
+    const long long lo4 = (row * D + col) / 4, hi4 = lo4 + D / 8;
+    const f32x4* pk = reinterpret_cast<const f32x4*>(part);
+    const f32x4* pv = pk + (size_t)nqs * nel4;
+    f32x4 kl = {0.f, 0.f, 0.f, 0.f}, kh = kl, vl = kl, vh = kl;
+    for (int qc = 0; qc < nqs; ++qc) {
+      kl += pk[(size_t)qc * nel4 + lo4];
+      kh += pk[(size_t)qc * nel4 + hi4];
+      vl += pv[(size_t)qc * nel4 + lo4];
+      vh += pv[(size_t)qc * nel4 + hi4];
+    }
+    const int bh = (int)(row / Sk), r = (int)(row % Sk);
+    const size_t tr = (size_t)(rope.pos + r) * (D / 2) + col;
+    const f32x4 c = *reinterpret_cast<const f32x4*>(rope.cos + tr);
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(rope.sin + tr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float ylo, yhi;
+      rope_pair(kl[e], kh[e], c[e], -sv[e], ylo, yhi);
+      kl[e] = ylo;
+      kh[e] = yhi;
+    }
+    T* dk = dK + head_off<STR, D>(lay.dk, bh, H, Sk) + (size_t)r * row_ld<STR, D>(lay.dk) + col;
+    T* dv = dV + head_off<STR, D>(lay.dv, bh, H, Sk) + (size_t)r * row_ld<STR, D>(lay.dv) + col;
+    store4<T>(dk, kl[0], kl[1], kl[2], kl[3]);
+    store4<T>(dk + D / 2, kh[0], kh[1], kh[2], kh[3]);
+    store4<T>(dv, vl[0], vl[1], vl[2], vl[3]);
+    store4<T>(dv + D / 2, vh[0], vh[1], vh[2], vh[3]);
+    return;
+  }
   const long long i = (long long)blockIdx.x * 64 + threadIdx.x;
   if (i >= nel4) return;
   const f32x4* pk = reinterpret_cast<const f32x4*>(part) + i;
@@ -464,13 +513,13 @@ __global__ __launch_bounds__(64) void bwd_dkdv_reduce_kernel(const float* __rest
   }
 }
 
-template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool QSPLIT, bool STR>
+template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool QSPLIT, bool STR, bool ROPE>
 static hipError_t launch(const BwdArgs& a) {
   constexpr LShape SH = dkdv_shape(is_bf16<E>(), D);
   constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
   using T = typename E::T;
   constexpr auto kern =
-      bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS, QSPLIT, STR>;
+      bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS, QSPLIT, STR, ROPE>;
   const Layout lay = a.layout != nullptr ? *a.layout : Layout{};
   constexpr int BKV = 32 * (NW / NSPLIT);
   constexpr int BQ = 32 * NSPLIT * KPW;
@@ -498,25 +547,27 @@ static hipError_t launch(const BwdArgs& a) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SPq,
                      a.SPk, a.Sq, a.Sk, a.BH * a.Sq, a.scale * kLog2e, a.scale, a.BH, a.H, a.kvlen,
-                     QSPLIT ? a.part : nullptr, nqs, qpc, nitems, sched, lay);
+                     QSPLIT ? a.part : nullptr, nqs, qpc, nitems, sched, lay, a.rope);
   if (QSPLIT) {
     const long long nel4 = (long long)a.BH * a.Sk * D / 4;
-    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T, D, STR>), dim3((unsigned)((nel4 + 63) / 64)),
+    const long long nthr = ROPE ? nel4 / 2 : nel4;
+    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<T, D, STR, ROPE>), dim3((unsigned)((nthr + 63) / 64)),
                        dim3(64), 0, a.stream, a.part, (T*)a.dk, (T*)a.dv, nqs, nel4, a.Sk, a.H,
-                       lay);
+                       lay, a.rope);
   }
   return hipGetLastError();
 }
 
-template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool STR>
+template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool STR, bool ROPE = false>
 static hipError_t launch_s(const BwdArgs& a) {
-  if (a.part != nullptr && a.nqs > 1) return launch<E, D, CAUSAL, WDS, CROSS, true, STR>(a);
-  return launch<E, D, CAUSAL, WDS, CROSS, false, STR>(a);
+  if (a.part != nullptr && a.nqs > 1) return launch<E, D, CAUSAL, WDS, CROSS, true, STR, ROPE>(a);
+  return launch<E, D, CAUSAL, WDS, CROSS, false, STR, ROPE>(a);
 }
 
 // (strided layouts run the cross-attention instantiation)
 template <class E, int D, bool CAUSAL, bool WDS>
 static hipError_t launch_x(const BwdArgs& a) {
+  if (a.rope.cos != nullptr) return launch_s<E, D, CAUSAL, WDS, true, true, true>(a);
   if (a.layout != nullptr) return launch_s<E, D, CAUSAL, WDS, true, true>(a);
   return a.cross ? launch_s<E, D, CAUSAL, WDS, true, false>(a)
                  : launch_s<E, D, CAUSAL, WDS, false, false>(a);

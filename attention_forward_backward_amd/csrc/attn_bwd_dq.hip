@@ -31,13 +31,17 @@
 
 namespace attn {
 
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS, bool STR>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS, bool STR,
+          bool ROPE>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     typename E::T* __restrict__ dQ, const float* __restrict__ Dws, int Sq, int Sk_, int Lws,
-    float c, float scale, int H, const int* __restrict__ kvlen, const Layout lay) {
+    float c, float scale, int H, const int* __restrict__ kvlen, const Layout lay,
+    const RopeTab rope) {
   // STR: Q, K, V, dO, dQ are laid out by `lay` (else [B, H, S, D] row-major).
+  // ROPE (STR): Q and K hold RoPE-turned rows; dQ leaves turned back by the
+  // transposed rotation of query i (table row rope.pos + i).
   // Queries Sq, keys Sk (one length in self-attention, CROSS = false); key j
   // is visible from query i iff j < L and, when causal, j <= i + off
   // (head_keys).  Lws: offset of LSE*log2(e) in the workspace (B*H*Sq).
@@ -200,13 +204,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
   T* dq = STR ? dQ + head_off<STR, D>(lay.dq, bh, H, Sq) : dQ + base;
   const int lddq = row_ld<STR, D>(lay.dq);
   if (qvalid) {
+    float qs = scale;
+    if constexpr (ROPE) {  // dQ of the turned rows, scaled, then turned back in f32
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= scale;
+      const size_t tr = (size_t)(rope.pos + qi) * (D / 2);
+      rope_back_acc<D>(acc, rope.cos + tr, rope.sin + tr, h);
+      qs = 1.f;
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        store4<T>(dq + (size_t)qi * lddq + db * 32 + 8 * j + 4 * h, acc[db][4 * j] * scale,
-                  acc[db][4 * j + 1] * scale, acc[db][4 * j + 2] * scale,
-                  acc[db][4 * j + 3] * scale);
+        store4<T>(dq + (size_t)qi * lddq + db * 32 + 8 * j + 4 * h, acc[db][4 * j] * qs,
+                  acc[db][4 * j + 1] * qs, acc[db][4 * j + 2] * qs, acc[db][4 * j + 3] * qs);
   }
 }
 
@@ -219,12 +230,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
 // Blocks with no visible key (above the causal diagonal, or past S) are
 // skipped; the dK+dV kernel wrote exact zeros for every masked entry and
 // every key past S inside the blocks it processed.
-template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS, bool STR>
+template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS, bool STR,
+          bool ROPE>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
     const typename E::T* __restrict__ K, const typename E::T* __restrict__ dST,
     typename E::T* __restrict__ dQ, int Sq, int Sk_, int SPq, int SPk, float scale, int H,
-    const int* __restrict__ kvlen, const Layout lay) {
+    const int* __restrict__ kvlen, const Layout lay, const RopeTab rope) {
   // STR: K and dQ are laid out by `lay` (dS^T is the packed workspace).
+  // ROPE: as in bwd_dq_kernel.
   using T = typename E::T;
   constexpr int RB = NW / NSPLIT;
   constexpr int BR = 32 * RB;
@@ -255,6 +268,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   const int qw0 = qt * BR;         // first query of the workgroup
   const int q0 = qw0 + qb * 32;    // first query of this wave's block
   const bool wave_active = q0 < Sq;
+  RopeAccRow<D> rrow;  // (ROPE) angles of query q0 + n, fetched ahead of the tiles
+  if constexpr (ROPE) {
+    const size_t tr = (size_t)(rope.pos + min(q0 + n, Sq - 1)) * (D / 2);
+    rrow.load(rope.cos + tr, rope.sin + tr, h);
+  }
 
   f32x16 acc[NDB];
 #pragma unroll
@@ -335,17 +353,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
   const int lddq = row_ld<STR, D>(lay.dq);
   const int qi = q0 + n;
   if (qi < Sq) {
+    float qs = scale;
+    if constexpr (ROPE) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= scale;
+      rrow.apply(acc);
+      qs = 1.f;
+    }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        store4<T>(dq + (size_t)qi * lddq + db * 32 + 8 * j + 4 * h, acc[db][4 * j] * scale,
-                  acc[db][4 * j + 1] * scale, acc[db][4 * j + 2] * scale,
-                  acc[db][4 * j + 3] * scale);
+        store4<T>(dq + (size_t)qi * lddq + db * 32 + 8 * j + 4 * h, acc[db][4 * j] * qs,
+                  acc[db][4 * j + 1] * qs, acc[db][4 * j + 2] * qs, acc[db][4 * j + 3] * qs);
   }
 }
 
-template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
+template <class E, int D, bool CAUSAL, bool CROSS, bool STR, bool ROPE = false>
 static hipError_t launch_gemm(const BwdArgs& a) {
   constexpr LShape SH = dqg_shape(is_bf16<E>(), D);
   constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
@@ -353,14 +377,14 @@ static hipError_t launch_gemm(const BwdArgs& a) {
   constexpr int BR = 32 * (NW / NSPLIT);
   const int nqt = (a.Sq + BR - 1) / BR;
   dim3 grid(a.BH, nqt);
-  hipLaunchKernelGGL((bwd_dq_gemm_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR>), grid,
-                     dim3(NW * 64), 0, a.stream, (const T*)a.k, (const T*)a.ds, (T*)a.dq, a.Sq,
-                     a.Sk, a.SPq, a.SPk, a.scale, a.H, a.kvlen,
-                     a.layout != nullptr ? *a.layout : Layout{});
+  hipLaunchKernelGGL((bwd_dq_gemm_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR, ROPE>),
+                     grid, dim3(NW * 64), 0, a.stream, (const T*)a.k, (const T*)a.ds, (T*)a.dq,
+                     a.Sq, a.Sk, a.SPq, a.SPk, a.scale, a.H, a.kvlen,
+                     a.layout != nullptr ? *a.layout : Layout{}, a.rope);
   return hipGetLastError();
 }
 
-template <class E, int D, bool CAUSAL, bool CROSS, bool STR>
+template <class E, int D, bool CAUSAL, bool CROSS, bool STR, bool ROPE = false>
 static hipError_t launch(const BwdArgs& a) {
   constexpr LShape SH = dq_shape(is_bf16<E>(), D);
   constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
@@ -368,17 +392,20 @@ static hipError_t launch(const BwdArgs& a) {
   constexpr int BR = 32 * (NW / NSPLIT);
   const int nqt = (a.Sq + BR - 1) / BR;
   dim3 grid(a.BH, nqt);
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR>), grid,
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR, ROPE>), grid,
                      dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      (const T*)a.dout, (T*)a.dq, a.delta, a.Sq, a.Sk, a.BH * a.Sq,
                      a.scale * kLog2e, a.scale, a.H, a.kvlen,
-                     a.layout != nullptr ? *a.layout : Layout{});
+                     a.layout != nullptr ? *a.layout : Layout{}, a.rope);
   return hipGetLastError();
 }
 
 // (strided layouts run the cross-attention instantiation)
 template <class E, int D, bool CAUSAL>
 static hipError_t launch_x(const BwdArgs& a) {
+  if (a.rope.cos != nullptr)
+    return a.ds != nullptr ? launch_gemm<E, D, CAUSAL, true, true, true>(a)
+                           : launch<E, D, CAUSAL, true, true, true>(a);
   if (a.ds != nullptr) {
     if (a.layout != nullptr) return launch_gemm<E, D, CAUSAL, true, true>(a);
     return a.cross ? launch_gemm<E, D, CAUSAL, true, false>(a)

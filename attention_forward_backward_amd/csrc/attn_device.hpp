@@ -198,6 +198,179 @@ __device__ inline void load_row_frag_lds(RowFrag<E, D>& rf, const char* tile, in
   }
 }
 
+// ------------------------------------------------------------------ rotary embedding
+// Rotate-half RoPE (the axial RoPE of "Meganeura", Section 5.2, applied to Q
+// and K in front of the attention; 1-D and axial positions differ only in
+// the angle tables): pair (x_i, x_{i+D/2}) of a row is turned by the angle
+// of cosine c and sine s,
+//   y_i = x_i c - x_{i+D/2} s,   y_{i+D/2} = x_{i+D/2} c + x_i s,
+// and with s negated by the transposed rotation (the map of the gradient
+// with respect to the turned row back to the row).  Every site that turns
+// rows -- the rotation pass, the forward's Q operand, the dQ and dK stores --
+// rounds the same way: each output is fma(own, c, -+(other * s)).
+__device__ inline void rope_pair(float lo, float hi, float c, float s, float& ylo, float& yhi) {
+  ylo = fmaf(lo, c, -(hi * s));
+  yhi = fmaf(hi, c, lo * s);
+}
+
+// 16-byte LDS read and write through restrict pointers: with the alias-scope
+// metadata they carry, the compiler's wait insertion does not take them for
+// accesses to LDS that a direct global->LDS load in flight may write (it
+// would put a vmcnt(0) before them, draining the ring's prefetched tiles).
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+__device__ __attribute__((always_inline)) inline u32x4 lds_read16(const lds_u32x4* __restrict__ p) {
+  return *p;
+}
+__device__ __attribute__((always_inline)) inline void lds_write16(lds_u32x4* __restrict__ p,
+                                                                  u32x4 v) {
+  *p = v;
+}
+
+// RoPE on a [BR x D] tile of rows in LDS (swizzled as Tile<E, D>) filled by
+// the direct loads of TileLoader / StageLoader over NW waves: 1 KiB slot s of
+// the tile holds rows s*RPS .. s*RPS + RPS - 1 (every chunk of them) and is
+// loaded by wave s % NW, so once a wave's own loads are complete it can turn
+// the rows of its slots in place with no barrier.  Unit u of a wave = (row,
+// chunk ch of the lower half) turns the chunk's columns i with their
+// partners i + D/2; a slot has RPS * D/2 / EPC = 32 units.  load() fetches
+// the angles of a lane's units (float32 tables [rows][D/2]; row r of the
+// tile is sequence position pos0 + r, clamped to the last valid one);
+// apply() turns the units, rounds to the storage type as a rotation pass
+// would, writes them back and, when out is not null, stores rows below
+// `rows` to out + r * D (the turned rows).
+template <class E, int D, int BR, int NW>
+struct TileRope {
+  using TL = Tile<E, D>;
+  using T = typename E::T;
+  static constexpr int NCH = TL::CPR / 2;  // 16-byte chunks per half row
+  static constexpr int EPC = TL::EPC;
+  static constexpr int RPS = 64 / TL::CPR;             // rows per slot
+  static constexpr int SPW = BR * TL::CPR / 64 / NW;   // slots per wave
+  static constexpr int UNITS = SPW * 32;               // units per wave
+  static constexpr int UPT = (UNITS + 63) / 64;        // units per lane (the last may idle)
+  static_assert(BR * TL::CPR % (64 * NW) == 0 && RPS * NCH == 32, "tile slots split over waves");
+  f32x4 c[UPT * EPC / 4], s[UPT * EPC / 4];
+
+  __device__ static inline void unit(int k, int w, int lane, int& r, int& ch) {
+    const int u = k * 64 + lane;
+    const int slot = w + (u / 32) * NW, v = u % 32;
+    r = slot * RPS + v / NCH;
+    ch = v % NCH;
+  }
+
+  __device__ inline void load(const float* __restrict__ cs, const float* __restrict__ sn, int pos0,
+                              int rows, int w, int lane) {
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      if (UNITS % 64 != 0 && k * 64 + lane >= UNITS) break;
+      int r, ch;
+      unit(k, w, lane, r, ch);
+      const size_t t = (size_t)(pos0 + min(r, rows - 1)) * (D / 2) + ch * EPC;
+#pragma unroll
+      for (int v = 0; v < EPC / 4; ++v) {
+        c[k * (EPC / 4) + v] = *reinterpret_cast<const f32x4*>(cs + t + 4 * v);
+        s[k * (EPC / 4) + v] = *reinterpret_cast<const f32x4*>(sn + t + 4 * v);
+      }
+    }
+  }
+
+  // An empty use of the angles: the compiler's wait for their loads goes
+  // here (placed where no load the ring prefetches is in flight), so that
+  // apply() later needs none.
+  __device__ inline void ready() const {
+#pragma unroll
+    for (int k = 0; k < UPT * EPC / 4; ++k) asm volatile("" ::"v"(c[k]), "v"(s[k]));
+  }
+
+  __device__ inline void apply(char* tile, T* out, int rows, int w, int lane) const {
+#pragma unroll
+    for (int k = 0; k < UPT; ++k) {
+      if (UNITS % 64 != 0 && k * 64 + lane >= UNITS) break;
+      int r, ch;
+      unit(k, w, lane, r, ch);
+      lds_u32x4* plo = (lds_u32x4*)(tile + r * TL::ROWB + ((ch ^ TL::swz(r)) << 4));
+      lds_u32x4* phi = (lds_u32x4*)(tile + r * TL::ROWB + (((ch + NCH) ^ TL::swz(r)) << 4));
+      u32x4 lo = lds_read16(plo), hi = lds_read16(phi);
+      if constexpr (sizeof(T) == 4) {
+        f32x4 a = __builtin_bit_cast(f32x4, lo), b = __builtin_bit_cast(f32x4, hi);
+        const f32x4 cc = c[k], ss = s[k];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float ylo, yhi;
+          rope_pair(a[e], b[e], cc[e], ss[e], ylo, yhi);
+          a[e] = ylo;
+          b[e] = yhi;
+        }
+        lo = __builtin_bit_cast(u32x4, a);
+        hi = __builtin_bit_cast(u32x4, b);
+      } else {
+        bf16x8 a = __builtin_bit_cast(bf16x8, lo), b = __builtin_bit_cast(bf16x8, hi);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float ylo, yhi;
+          rope_pair((float)a[e], (float)b[e], c[2 * k + e / 4][e % 4], s[2 * k + e / 4][e % 4], ylo,
+                    yhi);
+          a[e] = (__bf16)ylo;
+          b[e] = (__bf16)yhi;
+        }
+        lo = __builtin_bit_cast(u32x4, a);
+        hi = __builtin_bit_cast(u32x4, b);
+      }
+      lds_write16(plo, lo);
+      lds_write16(phi, hi);
+      if (out != nullptr && r < rows) {
+        T* o = out + (size_t)r * D + ch * EPC;
+        *reinterpret_cast<u32x4*>(o) = lo;
+        *reinterpret_cast<u32x4*>(o + D / 2) = hi;
+      }
+    }
+  }
+};
+
+// The transposed rotation applied to a row held in MFMA output
+// accumulators: element 4j+e of acc[db] is column db*32 + 8j + 4h + e of the
+// lane's row (the dK^T and dQ^T accumulators), so both columns of every
+// pair (i, i + D/2) are in the lane.  load() fetches the row's angles at the
+// lane's lower-half columns (cs, sn point at the row), apply() turns acc.
+template <int D>
+struct RopeAccRow {
+  static constexpr int NDB = D / 32;
+  static constexpr int NG = D >= 64 ? 2 * NDB : 2;  // groups of 4 lower-half columns
+  f32x4 c[NG], s[NG];
+  // group g: lower column block lb, group j in it; the partner is D/2 on
+  __device__ static constexpr int lb(int g) { return D >= 64 ? g / 4 : 0; }
+  __device__ static constexpr int jj(int g) { return D >= 64 ? g % 4 : g; }
+  __device__ inline void load(const float* __restrict__ cs, const float* __restrict__ sn, int h) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int i = lb(g) * 32 + 8 * jj(g) + 4 * h;
+      c[g] = *reinterpret_cast<const f32x4*>(cs + i);
+      s[g] = *reinterpret_cast<const f32x4*>(sn + i);
+    }
+  }
+  __device__ inline void apply(f32x16 (&acc)[NDB]) const {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int l = lb(g), j = jj(g);
+      const int hb = D >= 64 ? l + NDB / 2 : 0, hj = D >= 64 ? j : j + 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float ylo, yhi;
+        rope_pair(acc[l][4 * j + e], acc[hb][4 * hj + e], c[g][e], -s[g][e], ylo, yhi);
+        acc[l][4 * j + e] = ylo;
+        acc[hb][4 * hj + e] = yhi;
+      }
+    }
+  }
+};
+template <int D>
+__device__ inline void rope_back_acc(f32x16 (&acc)[D / 32], const float* __restrict__ cs,
+                                     const float* __restrict__ sn, int h) {
+  RopeAccRow<D> r;
+  r.load(cs, sn, h);
+  r.apply(acc);
+}
+
 // Run f(t, stage) for t = 0 .. n-1, where stage = t % NST is passed as a
 // compile-time constant (std::integral_constant): the loop is unrolled by
 // NST so that each stage's LDS base folds into the reads' 16-bit immediate
@@ -259,6 +432,18 @@ struct Str3 {
 };
 struct Layout {
   Str3 q, k, v, o, dout, dq, dk, dv;
+};
+
+// RoPE of a fused call: row p of the float32 tables cos, sin [rows][D/2]
+// holds the angles of sequence position p - pos; out, kout: where the
+// forward stores the turned Q and K rows ([B, H, S, D] row-major, the
+// storage type).
+struct RopeTab {
+  const float* cos = nullptr;
+  const float* sin = nullptr;
+  int pos = 0;
+  void* out = nullptr;
+  void* kout = nullptr;
 };
 
 // First element of head bh's rows: with STR from the strides, else in the

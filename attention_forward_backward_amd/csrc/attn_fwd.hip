@@ -35,13 +35,13 @@
 namespace attn {
 
 template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool CROSS,
-          bool STR, bool KS>
+          bool STR, bool KS, bool ROPE>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, typename E::T* __restrict__ O,
     float* __restrict__ LSE, int Sq, int Sk_, float c, int BH, int H,
     const int* __restrict__ kvlen, int nitems, const Sched sched, const Layout lay, int nch,
-    int kc, float* __restrict__ part, int Sp) {
+    int kc, float* __restrict__ part, int Sp, const RopeTab rope) {
   // LSE may be null (an inference-only forward stores no LSE).  Queries Sq,
   // keys Sk (one length in self-attention, CROSS = false); per batch*head the
   // first L keys exist and key j is visible from query i iff j < L and, when
@@ -52,6 +52,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   // it = (query tile, chunk) * BH + head, and an item of a query tile with
   // more than one chunk stores its unnormalised O (f32) and its (m, l) in
   // `part` -- [nch][BH][Sp][D] then [nch][BH][Sp][2] -- for fwd_merge_kernel.
+  // ROPE (self-attention, STR; query and key i at table row rope.pos + i):
+  // Q and K tiles are turned by RoPE in LDS (TileRope) once they arrive,
+  // each wave turning the rows it loaded, each K tile by every item that
+  // reads it; the turned rows are stored once, Q by its item and key tile t
+  // by the item of query tile t (same tile height), to rope.out and
+  // rope.kout for the backward.
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-query blocks per item
@@ -63,6 +69,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   constexpr int TILEB = BK * TL::ROWB;  // one matrix tile; V follows K in a stage
   using QL = TileLoader<E, D, BR, NW>;
   static_assert(NW % NSPLIT == 0 && NST >= 2 && NST <= 4, "launch shape");
+  // (ROPE: a tile's angles are fetched on the step before it is consumed,
+  // the one that issues it; the diagonal store needs square tiles)
+  static_assert(!ROPE || (NST == 2 && BK == BR && !KS), "RoPE launch shape");
   __shared__ __attribute__((aligned(1024))) char smem[NST * STAGE + QL::BYTES];
   char* const qtile = smem + NST * STAGE;
 
@@ -172,6 +181,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   int cr = 0, cit = lit, kt = 0, nkt = lnkt, ckb = lkb;
   bool cpart = lpart;
   load_q(lit);
+  // (ROPE) angles of this lane's share of the next Q tile and of the K tile
+  // the loader issues next
+  TileRope<E, D, BR, NW> qrope;
+  TileRope<E, D, BK, NW> krope;
+  if constexpr (ROPE) {
+    const int qrow0 = item_qt(lit) * BR;
+    qrope.load(rope.cos, rope.sin, rope.pos + qrow0, Sq - qrow0, w, lane);
+    const int krow0 = (lkb + lkt) * BK;
+    krope.load(rope.cos, rope.sin, rope.pos + krow0, Sk - krow0, w, lane);
+  }
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s) issue_next(s);
   int bh = cit % BH, q0 = item_qt(cit) * BR + qb * 32;
@@ -268,8 +287,35 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
     int mark = mk.get(si);
     if (kt == 0) mark = max(mark, qmark);  // the item's Q rows too
     wait_vmem_dyn(vm - mark);
+    if constexpr (ROPE) {
+      // This wave's own rows of the tile (and on an item's first tile of its
+      // Q tile) are in LDS: the wave turns them in place before the barrier,
+      // storing the turned Q rows, and the turned K rows on the item's
+      // diagonal tile.  The angles were fetched on the previous step; no
+      // load the ring prefetches is in flight here, so the compiler's wait
+      // for them stalls on nothing.
+      krope.ready();
+      if (kt == 0) {
+        qrope.ready();
+        const int qrow0 = item_qt(cit) * BR;
+        qrope.apply(qtile, static_cast<T*>(rope.out) + ((size_t)bh * Sq + qrow0) * D,
+                    Sq - qrow0, w, lane);
+      }
+      const int krow0 = (ckb + kt) * BK;
+      T* kout = item_qt(cit) == ckb + kt
+                    ? static_cast<T*>(rope.kout) + ((size_t)bh * Sk + krow0) * D
+                    : nullptr;
+      krope.apply(smem + si * STAGE, kout, Sk - krow0, w, lane);
+    }
     lds_barrier();  // tile pos (and on an item's first tile its Q) is in LDS;
                     // every wave is done with tile pos-1
+    if constexpr (ROPE) {  // the angles of the tile issued below
+      if (lit < nitems) {
+        const int r0 = (lkb + lkt) * BK;
+        krope.load(rope.cos, rope.sin, rope.pos + r0, Sk - r0, w, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     issue_next((si + NST - 1) % NST);
     if (kt == 0) {
       // This wave's Q rows, then the next item's Q tile (if any) once every
@@ -279,6 +325,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
       if (nit < nitems) {
         lds_barrier();
         load_q(nit);
+        if constexpr (ROPE) {  // the angles of that tile
+          const int qrow0 = item_qt(nit) * BR;
+          qrope.load(rope.cos, rope.sin, rope.pos + qrow0, Sq - qrow0, w, lane);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // the counts above assume this issue order
@@ -463,12 +513,12 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const float* __restrict_
   if (gcol == 0 && LSE != nullptr) LSE[row] = (mx + __log2f(l)) * kLn2;
 }
 
-template <class E, int D, bool CAUSAL, bool CROSS, bool STR, bool KS>
+template <class E, int D, bool CAUSAL, bool CROSS, bool STR, bool KS, bool ROPE = false>
 static hipError_t launch(const FwdArgs& a) {
   constexpr LShape SH = fwd_shape(is_bf16<E>(), D);
   constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
   using T = typename E::T;
-  constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR, KS>;
+  constexpr auto kern = fwd_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, CROSS, STR, KS, ROPE>;
   constexpr int BR = 32 * (NW / NSPLIT);
   constexpr int BK = 32 * NSPLIT * KPW;
   static_assert(BR == fwd_query_tile(is_bf16<E>(), D) && BK == fwd_key_tile(is_bf16<E>(), D),
@@ -502,7 +552,7 @@ static hipError_t launch(const FwdArgs& a) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (T*)a.o, a.lse, a.Sq, a.Sk, a.scale * kLog2e, a.BH, a.H,
                      a.kvlen, nitems, sched, a.layout != nullptr ? *a.layout : Layout{}, nch, kc,
-                     a.part, nqt * BR);
+                     a.part, nqt * BR, a.rope);
   if (KS) {
     const long long threads = (long long)a.BH * a.Sq * (D / 4);
     hipLaunchKernelGGL((fwd_merge_kernel<T, D, CAUSAL>), dim3((unsigned)((threads + 255) / 256)),
@@ -516,6 +566,9 @@ static hipError_t launch(const FwdArgs& a) {
 // lengths)
 template <class E, int D>
 static hipError_t launch_c(const FwdArgs& a) {
+  if (a.rope.cos != nullptr)  // (strided self-attention)
+    return a.causal ? launch<E, D, true, true, true, false, true>(a)
+                    : launch<E, D, false, true, true, false, true>(a);
   if (a.layout != nullptr)
     return a.causal ? launch<E, D, true, true, true, false>(a)
                     : launch<E, D, false, true, true, false>(a);
@@ -540,7 +593,7 @@ static hipError_t launch_d(const FwdArgs& a) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.Sq <= (a.bf16 ? ATTN_FWD_SMALL_MAXQ_BF16 : ATTN_FWD_SMALL_MAXQ_F32))
+  if (a.rope.cos == nullptr && a.Sq <= (a.bf16 ? ATTN_FWD_SMALL_MAXQ_BF16 : ATTN_FWD_SMALL_MAXQ_F32))
     return launch_fwd_small(a);
   if (a.bf16) return launch_d<EBF16>(a);
   return a.bf16_operands ? launch_d<EF32B>(a) : launch_d<EF32>(a);

@@ -215,6 +215,8 @@ struct FwdArgs {
   hipStream_t stream;
   const Layout* layout = nullptr;  // strides of q, k, v, o; null: [B, H, S, D] row-major
   float* part = nullptr;  // key-split partials (fwd_key_split), or null: no split
+  RopeTab rope;           // rope.cos null: no RoPE; else Q turned on load (strided
+                          // self-attention) and stored turned to rope.out
 };
 
 struct BwdArgs {
@@ -234,6 +236,8 @@ struct BwdArgs {
   bool causal;
   float scale;
   hipStream_t stream;
+  RopeTab rope;  // rope.cos null: no RoPE; else dQ and dK leave turned back
+                 // (transposed rotation, query / key i at table row rope.pos + i)
 };
 
 // Rotary embedding / layout pass: dst rows = R(src rows) (or R^T, or a plain

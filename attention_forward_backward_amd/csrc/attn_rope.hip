@@ -61,9 +61,10 @@ __global__ __launch_bounds__(256) void rope_copy_kernel(
     }
 #pragma unroll
     for (int e = 0; e < PV; ++e) {
-      const float a = (float)lo.v[e], bv = (float)hi.v[e];
-      olo.v[e] = (T)(a * c[e] - bv * sn[e]);
-      ohi.v[e] = (T)(bv * c[e] + a * sn[e]);
+      float ylo, yhi;
+      rope_pair((float)lo.v[e], (float)hi.v[e], c[e], sn[e], ylo, yhi);
+      olo.v[e] = (T)ylo;
+      ohi.v[e] = (T)yhi;
     }
   } else {
     olo = lo;

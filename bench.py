@@ -731,12 +731,14 @@ def graph_time(fn, per_graph=20, replays=30) -> float:
 
 def rope_section(cfg, dtypes, args, stream, log) -> dict:
     """The workload's step on a packed [B, S, 3, H, D] projection with 1-D
-    RoPE on Q and K, O and dO in [B, S, H, D]: attn_rope_copy writes the
-    rotated Q and K ([B, H, S, D]) and takes dQ, dK back through the
-    transposed rotation into the packed gradient; the strided entry points
-    read V and dO and write O and dV in place.  A rotation pass reads and
-    writes one [B, H, S, D] tensor (plus table rows): HBM-bound.  Timed from
-    HIP graph replays."""
+    RoPE on Q and K, O and dO in [B, S, H, D], three ways:
+    fused (attn_fwd_rope + attn_bwd_rope: Q and K tiles turned inside the
+    forward kernel, dQ and dK turned back in the kernels that store them);
+    with separate passes (attn_rope_copy turns Q and K into
+    [B, H, S, D] before the strided kernels and takes dQ, dK back through the
+    transposed rotation after them); and the packed step without RoPE.  A
+    rotation pass reads and writes one [B, H, S, D] tensor (plus table rows):
+    HBM-bound.  Timed from HIP graph replays."""
     import torch
     import attention_forward_backward_amd as afb
     from attention_forward_backward_amd import synth
@@ -791,6 +793,20 @@ def rope_section(cfg, dtypes, args, stream, log) -> dict:
         q_view, k_view = pk[:, :, 0].permute(0, 2, 1, 3), pk[:, :, 1].permute(0, 2, 1, 3)
         dq_view, dk_view = dpk[:, :, 0].permute(0, 2, 1, 3), dpk[:, :, 1].permute(0, 2, 1, 3)
 
+        qk = torch.empty((2,) + shp, dtype=tdt, device="cuda")
+        dq_view0, dk_view0 = dpk[:, :, 0].permute(0, 2, 1, 3), dpk[:, :, 1].permute(0, 2, 1, 3)
+        q_raw, k_raw = pk[:, :, 0].permute(0, 2, 1, 3), pk[:, :, 1].permute(0, 2, 1, 3)
+
+        def step_fused():
+            afb.attn_fwd_rope(q_raw, k_raw, v_view, o_view, lse, qk, ct, st, cfg.causal,
+                              cfg.scale)
+            afb.attn_bwd_rope(qk, v_view, o_view, do_view, lse, dq_view0, dk_view0, dv_view, ws,
+                              ct, st, cfg.causal, cfg.scale)
+
+        def fwd_fused():
+            afb.attn_fwd_rope(q_raw, k_raw, v_view, o_view, lse, qk, ct, st, cfg.causal,
+                              cfg.scale)
+
         def step_plain():
             afb.attn_fwd_strided(q_view, k_view, v_view, o_view, lse, None, cfg.causal, cfg.scale)
             afb.attn_bwd_strided(q_view, k_view, v_view, o_view, do_view, lse, dq_view, dk_view,
@@ -805,13 +821,17 @@ def rope_section(cfg, dtypes, args, stream, log) -> dict:
         bytes_rot = 2 * tb + 2 * S * (D // 2) * 4
         ms_pro, ms_epi, ms_step = tf(prologue), tf(epilogue), tf(step)
         ms_plain = tf(step_plain)
+        ms_fused, ms_ffwd = tf(step_fused), tf(fwd_fused)
         gbs = bytes_rot / (ms_rot * 1e-3) / 1e9
-        out[dt] = {"rotate_us": round(ms_rot * 1e3, 2), "rotate_bytes": bytes_rot,
+        out[dt] = {"fused_step_us": round(ms_fused * 1e3, 2),
+                   "fused_fwd_us": round(ms_ffwd * 1e3, 2),
+                   "packed_step_no_rope_us": round(ms_plain * 1e3, 2),
+                   "fused_overhead_frac": round(ms_fused / ms_plain - 1.0, 4),
+                   "passes_step_us": round(ms_step * 1e3, 2),
+                   "rotate_us": round(ms_rot * 1e3, 2), "rotate_bytes": bytes_rot,
                    "rotate_gbs": round(gbs, 1), "rotate_frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                   "prologue_us": round(ms_pro * 1e3, 2), "epilogue_us": round(ms_epi * 1e3, 2),
-                   "step_us": round(ms_step * 1e3, 2),
-                   "packed_step_no_rope_us": round(ms_plain * 1e3, 2)}
-        del pk, dOt, q, k, dq, dk, o_s, dpk, lse, ws
+                   "prologue_us": round(ms_pro * 1e3, 2), "epilogue_us": round(ms_epi * 1e3, 2)}
+        del pk, dOt, q, k, dq, dk, o_s, dpk, lse, ws, qk
     torch.cuda.empty_cache()
     return out
 

@@ -353,6 +353,56 @@ attn_status_t attn_rope_copy(attn_dtype_t dtype, const void* src, const long lon
                              const float* sin_table, int table_rows, int pos_offset, int batch,
                              int heads, int seq, int head_dim, int transpose, void* stream);
 
+/*
+ * Attention with RoPE on Q and K, fused into the kernels (axial RoPE in front
+ * of the attention, Section 5.2, on the packed projection forms of Section
+ * 3.2): self-attention (seq_q = seq_k = seq) on strided Q, K, V, O, with
+ * query and key i turned by the angles of table row pos_offset + i -- the
+ * result of attn_rope_copy (transpose = 0) on Q and K, then
+ * attn_fwd_strided / attn_bwd_strided on the turned rows, then the
+ * transposed rotation of dQ and dK -- with no pass of its own:
+ *   attn_fwd_rope turns the Q and K tiles inside the forward kernel as they
+ *     arrive in on-chip memory, and stores every turned Q and K row once
+ *     into qk_rot;
+ *   attn_bwd_rope reads the turned Q and K from qk_rot and applies the
+ *     transposed rotation to dQ and dK in the kernels that store them, in
+ *     float32 before the one rounding to the storage type.
+ *   strides    HOST int64 (batch, head, row) strides as for
+ *              attn_fwd_strided: attn_fwd_rope 12 values for q, k, v, o;
+ *              attn_bwd_rope 18 values for v, o, dout, dq, dk, dv.
+ *   qk_rot     DEVICE buffer of 2*batch*heads*seq*head_dim elements of the
+ *              tensors' storage type (float32, or bf16 for ATTN_BF16),
+ *              16-byte aligned, owned by the caller: turned Q at element 0,
+ *              turned K at element batch*heads*seq*head_dim, each
+ *              [B,H,S,D] row-major (heads*seq*head_dim < 2^31).  Written by
+ *              attn_fwd_rope, read by attn_bwd_rope; it must not overlap
+ *              any other argument.
+ *   cos_table, sin_table  DEVICE float32 [table_rows][head_dim/2], 16-byte
+ *              aligned (row p: the cosines and sines of the angles of
+ *              position p; 1-D and axial RoPE differ only in these tables);
+ *              pos_offset >= 0 and pos_offset + seq <= table_rows.
+ * Every other argument, the workspace (attn_bwd_workspace_size of the same
+ * shape) and the dtypes are as for attn_fwd_strided / attn_bwd_strided
+ * (ATTN_F32_BF16FWD: the forward's operands, turned in float32, are
+ * rounded to bf16 as they enter the MFMA).  Turned values are rounded
+ * exactly as attn_rope_copy rounds them, so the turned Q and K in qk_rot
+ * equal attn_rope_copy's output.  Errors as for the strided entry points,
+ * and ATTN_ERR_INVALID_ARG for missing or misaligned tables, a table too
+ * short, or a null or misaligned qk_rot.  Calls that overlap on one stream
+ * order as usual; nothing is allocated.
+ */
+attn_status_t attn_fwd_rope(attn_dtype_t dtype, const void* q, const void* k, const void* v,
+                            void* o, float* lse, void* qk_rot, int batch, int heads, int seq,
+                            int head_dim, const long long* strides, const float* cos_table,
+                            const float* sin_table, int table_rows, int pos_offset, int causal,
+                            float scale, void* stream);
+attn_status_t attn_bwd_rope(attn_dtype_t dtype, const void* qk_rot, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes, int batch, int heads, int seq,
+                            int head_dim, const long long* strides, const float* cos_table,
+                            const float* sin_table, int table_rows, int pos_offset, int causal,
+                            float scale, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* attn_status_string(attn_status_t status);
 

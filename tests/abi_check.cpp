@@ -108,6 +108,25 @@ int main() {
   EXPECT(attn_rope_copy(ATTN_F32, P, rs, P, rs, L, L, 8, 1, 1, 1, 8, 64, 0, nullptr), INV);
   EXPECT(attn_rope_copy(ATTN_F32, P, rs, P, rs, nullptr, nullptr, 0, 0, 1, 1, 8, 64, 2, nullptr),
          INV);
+  // fused RoPE entry points: tables, qk_rot and the internal [B,H,S,D] strides
+  const float* const T = L;
+  for (int i = 0; i < 24; ++i) st[i] = (i % 3 == 0) ? 8 * 64 : 64;  // B = H = 1, rows of 64
+  EXPECT(attn_fwd_rope(ATTN_F32, P, P, P, P, L, nullptr, 1, 1, 8, 64, st, T, T, 8, 0, 1, s,
+                       nullptr), INV);
+  EXPECT(attn_fwd_rope(ATTN_F32, P, P, P, P, L, P, 1, 1, 8, 64, st, T, nullptr, 8, 0, 1, s,
+                       nullptr), INV);
+  EXPECT(attn_fwd_rope(ATTN_F32, P, P, P, P, L, P, 1, 1, 8, 64, st, T, T, 8, 1, 1, s, nullptr),
+         INV);
+  EXPECT(attn_fwd_rope(ATTN_F32, P, P, P, P, L, P, 1, 1, 8, 64, st, static_cast<const float*>(M),
+                       T, 8, 0, 1, s, nullptr), INV);
+  EXPECT(attn_bwd_rope(ATTN_F32, P, P, P, P, L, P, P, P, P, 1 << 20, 1, 1, 8, 64, st, T, T, 7, 0,
+                       1, s, nullptr), INV);
+  EXPECT(attn_bwd_rope(ATTN_F32, M, P, P, P, L, P, P, P, P, 1 << 20, 1, 1, 8, 64, st, T, T, 8, 0,
+                       1, s, nullptr), INV);
+  EXPECT(attn_bwd_rope(ATTN_F32, P, P, P, P, L, P, P, P, P, 16, 1, 1, 8, 64, st, T, T, 8, 0, 1, s,
+                       nullptr), WS);
+  EXPECT(attn_bwd_rope(ATTN_BF16, P, P, P, P, L, P, P, P, P, 1 << 20, 1, 1, 8, 96, st, T, T, 8, 0,
+                       1, s, nullptr), UNS);
   // workspace sizes: 0 for rejected shapes, monotone and overflow-free at the edges
   EXPECT(attn_bwd_workspace_size(ATTN_F32, 1, 1, 8, 48, 1), 0);
   EXPECT(attn_bwd_workspace_size_min(ATTN_F32, 0, 1, 8, 64, 1), 0);

@@ -22,12 +22,13 @@ def test_library_loads_and_exports_header_symbols():
                              "attn_bwd_workspace_size_min", "attn_fwd_cross", "attn_bwd_cross",
                              "attn_bwd_cross_workspace_size", "attn_bwd_cross_workspace_size_min",
                              "attn_rope_copy", "attn_fwd_strided", "attn_bwd_strided",
+                             "attn_fwd_rope", "attn_bwd_rope",
                              "attn_status_string", "attn_version", "conv2d_fwd",
                              "conv2d_bwd_data", "conv2d_bwd_filter",
                              "conv2d_bwd_filter_workspace_size"}
     for name in declared:
         assert hasattr(L, name), name
-    assert afb.attn_version() == "0.7.0"
+    assert afb.attn_version() == "0.8.0"
     for code in range(5):
         assert afb.attn_status_string(code) not in ("", "unknown status")
     assert afb.attn_status_string(99) == "unknown status"
@@ -249,6 +250,44 @@ def test_strided_validation():
     mq = bhsd + [S * D, 0, D] * 2
     assert _bwds(mq + bhsd * 2 + bshd + [S * D, 0, D] * 2) == 1
     assert _bwds(mq + bhsd * 5, wsb=16) == 3                       # workspace still checked
+
+
+def _fwd_rope(strides=None, qk=FAKE, cos=FAKE, sin=FAKE, rows=8, pos=0, B=2, H=3, S=8, D=64,
+              dtype=0, lse=FAKE):
+    if strides is None:
+        strides = [H * S * D, S * D, D] * 4
+    LL = ctypes.c_longlong * 12
+    return afb.lib().attn_fwd_rope(dtype, FAKE, FAKE, FAKE, FAKE, lse, qk, B, H, S, D,
+                                   LL(*strides), cos, sin, rows, pos, 1, 0.125, None)
+
+
+def _bwd_rope(strides=None, qk=FAKE, cos=FAKE, sin=FAKE, rows=8, pos=0, B=2, H=3, S=8, D=64,
+              wsb=1 << 20):
+    if strides is None:
+        strides = [H * S * D, S * D, D] * 6
+    LL = ctypes.c_longlong * 18
+    return afb.lib().attn_bwd_rope(0, qk, *([FAKE] * 7), FAKE, wsb, B, H, S, D, LL(*strides),
+                                   cos, sin, rows, pos, 1, 0.125, None)
+
+
+def test_rope_fused_validation():
+    """attn_fwd_rope / attn_bwd_rope reject bad tables, qk_rot and strides
+    before the rotation pass or any kernel is enqueued."""
+    B, H, S, D = 2, 3, 8, 64
+    bhsd = [H * S * D, S * D, D]
+    for fn in (_fwd_rope, _bwd_rope):
+        assert fn(qk=None) == 1 and fn(qk=MIS) == 1
+        assert fn(cos=None) == 1 and fn(sin=None) == 1 and fn(cos=MIS) == 1
+        assert fn(rows=7) == 1 and fn(pos=1) == 1 and fn(pos=-1, rows=100) == 1
+        assert fn(D=48) == 2
+        # heads*seq*head_dim of qk_rot at 2^31 elements (the given strides pass)
+        n = 4 if fn is _fwd_rope else 6
+        assert fn(B=1, H=256, S=1 << 17, D=64, rows=1 << 17,
+                  strides=[0, (1 << 17) * 64, 64] * n) == 1
+    assert _fwd_rope(lse=MIS) == 1
+    assert _fwd_rope(strides=bhsd * 3 + [H * S * D, S * D, 32]) == 1   # output rows overlap
+    assert _bwd_rope(strides=bhsd * 3 + [H * S * D, 0, D] + bhsd * 2) == 1  # dq heads overlap
+    assert _bwd_rope(wsb=16) == 3
 
 
 def _conv(fn, dtype=0, a=FAKE, b=FAKE, out=FAKE, dims=(2, 8, 8, 4, 6, 3, 3, 1, 1, 1, 1)):
