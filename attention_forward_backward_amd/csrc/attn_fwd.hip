@@ -133,7 +133,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   // tile in the ring and of the prefetched Q rows.  Waiting until at most
   // vm - mark operations are pending completes everything up to that mark
   // (vmcnt counts loads and stores, and they retire in issue order);
-  // counting fewer stores than issued only makes a wait stricter.
+  // counting fewer operations than issued (the stores of partial waves, and
+  // with ROPE the angle loads and turned-row stores) only makes a wait
+  // stricter.
   int vm = 0, qmark = 0;
   RingMarks<NST> mk;
 

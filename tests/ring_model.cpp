@@ -87,6 +87,7 @@ struct Queue {
 
 constexpr long kStore = -1;          // tag of store instructions
 constexpr long kQBase = 1L << 40;    // forward Q tiles: kQBase + round
+constexpr long kAngle = -2;          // tag of the RoPE angle loads (counted by no wait)
 
 // ---------------------------------------------------------------- forward
 struct FwdCase {
@@ -96,6 +97,7 @@ struct FwdCase {
   std::vector<int> kvlen;  // per batch (cross only; empty: all Sk)
   bool lse;
   bool ks = false;  // key split (fwd_key_split), self-attention only
+  bool rope = false;  // RoPE turned in the kernel (attn_fwd_rope), self-attention only
 };
 
 template <class E, int D>
@@ -105,6 +107,11 @@ bool model_fwd(const FwdCase& c, int G) {
   constexpr int RB = NW / NSPLIT, BR = 32 * RB, BK = 32 * NSPLIT * KPW, NDB = D / 32;
   using LD = StageLoader<E, D, BK, NW>;
   using QL = TileLoader<E, D, BR, NW>;
+  // RoPE: the kernel's per-wave angle loads of one Q or K tile and its
+  // turned-row stores, none of them in its count
+  constexpr int NANG = 2 * TileRope<E, D, BK, NW>::UPT * (TileRope<E, D, BK, NW>::EPC / 4);
+  constexpr int NTST = 2 * TileRope<E, D, BK, NW>::UPT;
+  static_assert(BR == BK, "the RoPE forward turns square tiles");
   const int Sq = c.Sq, Sk = c.cross ? c.Sk : c.Sq, BH = c.BH, H = c.H;
   const int nqt = (Sq + BR - 1) / BR;
   int nch = 1, kc = 1 << 30;
@@ -185,6 +192,8 @@ bool model_fwd(const FwdCase& c, int G) {
       };
       int cr = 0, cit = lit, kt = 0, nkt = lnkt;
       load_q(0);
+      if (c.rope)  // angles of the first Q tile and of the first K tile
+        for (int i = 0; i < 2 * NANG; ++i) Q.issue(kAngle);
       for (int s = 0; s < NST - 1; ++s)
         if (!issue_next(s)) return false;
       if (plant == 1) {
@@ -211,11 +220,28 @@ bool model_fwd(const FwdCase& c, int G) {
               "fwd g%d w%d pos %d: loader issued (item %d, tile %d), consumer expects (%d, %d)", g,
               w, pos, stream[pos].first, stream[pos].second, cit, kt);
         consumed[si] = true;
+        if (c.rope) {
+          // the wave turns its rows of the K tile (and on an item's first
+          // tile of its Q tile) before the barrier; the compiler's wait for
+          // the angles (taken as vmcnt(0)); turned-row stores; then the
+          // angles of the tile issued next
+          if (kt == 0)
+            CHECK(qtile == cr && !Q.pending(kQBase + cr),
+                  "fwd g%d w%d: item round %d turned its Q tile before it arrived", g, w, cr);
+          Q.wait(0);
+          for (int i = 0; i < (kt == 0 ? 2 : 1) * NTST; ++i) Q.issue(kStore);
+          if (lit < nitems)
+            for (int i = 0; i < NANG; ++i) Q.issue(kAngle);
+        }
         if (!issue_next((si + NST - 1) % NST)) return false;
         if (kt == 0) {
           CHECK(qtile == cr && !Q.pending(kQBase + cr),
                 "fwd g%d w%d: item round %d read its Q tile before it arrived", g, w, cr);
-          if (sched_item(sched, cr + 1, g, G, BH) < nitems) load_q(cr + 1);
+          if (sched_item(sched, cr + 1, g, G, BH) < nitems) {
+            load_q(cr + 1);
+            if (c.rope)
+              for (int i = 0; i < NANG; ++i) Q.issue(kAngle);
+          }
         }
         if (++kt < nkt) continue;
         // item done: O stores (and the LSE store) of the waves that own the block
@@ -464,6 +490,25 @@ int main(int argc, char** argv) {
               }
             }
   std::printf("key split: %d cases ok\n", kcases);
+  // RoPE turned in the forward: angle loads and turned-row stores that no
+  // wait counts, in every self-attention shape above
+  int rcases = 0;
+  for (const bool bf16 : {false, true})
+    for (const int D : {32, 64, 128})
+      for (const int S : {1, 5, 17, 33, 64, 65, 130, 197, 512})
+        for (const bool causal : {true, false})
+          for (const int G : grids) {
+            const int BH = S >= 512 ? 16 : 24;
+            FwdCase f{bf16, D, BH, 4, S, S, causal, false, {}, true, false, true};
+            const bool ok = bf16 ? fwd_d<EBF16>(f, G) : fwd_d<EF32>(f, G);
+            ++rcases;
+            if (!ok) {
+              std::printf("case: rope %s D%d S%d causal%d G%d\n", bf16 ? "bf16" : "f32", D, S,
+                          causal, G);
+              return 1;
+            }
+          }
+  std::printf("rope forward: %d cases ok\n", rcases);
   // cross-attention: separate lengths, padded keys (0, short, full), causal
   // alignment at the end of the valid keys, query-chunk split
   struct X { int Sq, Sk; std::vector<int> kv; int nqs; };
