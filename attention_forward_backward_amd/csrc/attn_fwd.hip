@@ -351,7 +351,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
         const int kb = sp + NSPLIT * j;
         const int kk0 = (ckb + kt) * BK + kb * 32;
         if (!(kk0 < cL && (!CAUSAL || kk0 <= q0 + 31 + coff))) continue;  // wave-uniform
+        // The products run at raised wave priority, so that while one wave
+        // of a SIMD works through its softmax the other's MFMAs issue first
+        // (f32: forward 40.2 -> 39.3 us at B8 H12 S512 D64; bf16 unchanged).
+        __builtin_amdgcn_s_setprio(1);
         f32x16 sacc = dot_tile<E, D>(Kt, kb * 32 + pi32(n), h, qf, zero16());
+        __builtin_amdgcn_s_setprio(0);
         if (kk0 + 32 > cL || (CAUSAL && kk0 + 31 > q0 + coff)) {
           // key(r) = kk0 + 8h + (16*(r/8) + r%8); visible iff key < L and key <= qi + off
           const int lim = min(cL - 1, CAUSAL ? qi + coff : cL - 1) - kk0 - 8 * h;
@@ -396,9 +401,11 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
         l += rs;
         RegOperand<E> P;
         P.set(sacc);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
           oacc[db] = second_tile<E, D, false>(P, Vt, kb * 32, db * 32, lane, oacc[db]);
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     if (++kt < nkt) return;
