@@ -165,3 +165,73 @@ def test_fused_rope_repeatable():
         outs.append([to_host(t) for t in (o_s, lse, dpk, qk)])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_fused_rope_separate_bshd_tensors(dt):
+    """Q, K, V, O, dO and the gradients as separate [B, S, H, D] tensors
+    (row stride H*D), a sequence that is not a multiple of the tile, and a
+    table offset: the fused step against the oracle."""
+    import torch
+    B, H, S, D, causal, pos = 2, 3, 150, 64, True, 7
+    note(f"[gpu case] fused RoPE [B,S,H,D] tensors B{B} H{H} S{S} D{D} pos={pos} dtype={dt}")
+    rng = np.random.default_rng(11)
+    x = {n: _exact(rng.standard_normal((B, S, H, D)), dt) for n in ("q", "k", "v", "do")}
+    c, s, ct, st = _tables(S + pos, D, None)
+    scale = 1.0 / np.sqrt(D)
+    dev = {n: _dev(v, dt) for n, v in x.items()}
+    view = lambda t: t.permute(0, 2, 1, 3)
+    tdt = dev["q"].dtype
+    nan = float("nan")
+    o_s, dq_s, dk_s, dv_s = (torch.full((B, S, H, D), nan, dtype=tdt, device="cuda")
+                             for _ in range(4))
+    qk = torch.full((2, B, H, S, D), nan, dtype=tdt, device="cuda")
+    lse = torch.full((B, H, S), nan, device="cuda")
+    code = afb.ATTN_BF16 if dt == "bf16" else afb.ATTN_F32
+    ws = torch.empty(afb.attn_bwd_workspace_size(code, B, H, S, D, causal), dtype=torch.uint8,
+                     device="cuda")
+    afb.attn_fwd_rope(view(dev["q"]), view(dev["k"]), view(dev["v"]), view(o_s), lse, qk, ct, st,
+                      causal, scale, pos_offset=pos)
+    afb.attn_bwd_rope(qk, view(dev["v"]), view(o_s), view(dev["do"]), lse, view(dq_s),
+                      view(dk_s), view(dv_s), ws, ct, st, causal, scale, pos_offset=pos)
+    torch.cuda.synchronize()
+    t = {n: x[n].transpose(0, 2, 1, 3).astype(np.float64) for n in x}
+    rq, rk = oracle.rope(t["q"], c, s, pos), oracle.rope(t["k"], c, s, pos)
+    ro, rl = oracle.attention_forward(rq, rk, t["v"], causal, scale)
+    rdq, rdk, rdv, _ = oracle.attention_backward(rq, rk, t["v"], t["do"], causal, scale)
+    got = {n: to_host(v).transpose(0, 2, 1, 3) for n, v in (("o", o_s), ("dq", dq_s),
+                                                           ("dk", dk_s), ("dv", dv_s))}
+    errs = {"o": max_rel_err(got["o"], ro), "lse": max_rel_err(to_host(lse), rl),
+            "dq": max_rel_err(got["dq"], oracle.rope_transpose(rdq, c, s, pos)),
+            "dk": max_rel_err(got["dk"], oracle.rope_transpose(rdk, c, s, pos)),
+            "dv": max_rel_err(got["dv"], rdv)}
+    note("  errors " + ", ".join(f"{k_}={v_:.2e}" for k_, v_ in errs.items()))
+    for k_, v_ in errs.items():
+        assert v_ <= TOL[dt], (k_, v_)
+
+
+def test_fused_rope_forward_shared_kv_head():
+    """Multi-query attention in the fused forward: one K, V head (head stride
+    0) read by every query head; each head's turned K copy is stored for it."""
+    import torch
+    B, H, S, D, causal = 1, 4, 96, 64, True
+    note(f"[gpu case] fused RoPE forward, shared K/V head B{B} H{H} S{S} D{D}")
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((B, H, S, D)).astype(np.float32)
+    k1 = rng.standard_normal((B, 1, S, D)).astype(np.float32)
+    v1 = rng.standard_normal((B, 1, S, D)).astype(np.float32)
+    c, s, ct, st = _tables(S, D, None)
+    qd = _dev(q, "f32")
+    kd, vd = _dev(k1, "f32").expand(B, H, S, D), _dev(v1, "f32").expand(B, H, S, D)
+    o = torch.full((B, H, S, D), float("nan"), device="cuda")
+    lse = torch.full((B, H, S), float("nan"), device="cuda")
+    qk = torch.full((2, B, H, S, D), float("nan"), device="cuda")
+    afb.attn_fwd_rope(qd, kd, vd, o, lse, qk, ct, st, causal, 0.125)
+    torch.cuda.synchronize()
+    kx = np.broadcast_to(k1, (B, H, S, D)).astype(np.float64)
+    vx = np.broadcast_to(v1, (B, H, S, D)).astype(np.float64)
+    rq, rk = oracle.rope(q.astype(np.float64), c, s), oracle.rope(kx, c, s)
+    ro, rl = oracle.attention_forward(rq, rk, vx, causal, 0.125)
+    assert max_rel_err(to_host(o), ro) <= TOL["f32"]
+    assert max_rel_err(to_host(lse), rl) <= TOL["f32"]
+    assert max_rel_err(to_host(qk[1]), rk) <= 1e-6
