@@ -138,7 +138,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
                      CROSS ? max(lL, 1) : Sk, w, lane);
       } else {
         LD::issue(st, K + lhk * D, V + lhk * D, lkt * BKV, CROSS ? max(lL, 1) : Sk, w, lane,
-                  lane_off);
+                  lane_off, lane_off);
       }
     } else {
       if constexpr (STR) {
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
         LD::issue_ld(st, Q + head_off<STR, D>(lay.q, bhl, H, Sq), ldq,
                      dO + head_off<STR, D>(lay.dout, bhl, H, Sq), lddo, lqt * BQ, Sq, w, lane);
       } else {
-        LD::issue(st, Q + lhq * D, dO + lhq * D, lqt * BQ, Sq, w, lane, lane_off);
+        LD::issue(st, Q + lhq * D, dO + lhq * D, lqt * BQ, Sq, w, lane, lane_off, lane_off);
       }
     }
     issue_stats<BQ, NW>(stats0 + (nissued % NST) * (2 * BQ), Dws + Lws + lhq, Dws + lhq,

@@ -107,7 +107,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(
     if constexpr (STR)
       LD::issue_ld(st, k, ldk, v, ldv, row0, krows, w, lane);
     else
-      LD::issue(st, k, v, row0, krows, w, lane, lo);
+      LD::issue(st, k, v, row0, krows, w, lane, lo, lo);
   };
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)

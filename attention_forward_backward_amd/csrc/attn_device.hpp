@@ -160,7 +160,13 @@ __device__ inline void load_row_frag(RowFrag<E, D>& rf, const typename E::T* p, 
 // Every swizzle depends on row % 16 only, so offsets of 16-row aligned blocks
 // are additive.  (f32 with D = 32 keeps a 2-way conflict on pattern B: the
 // two rows 8 apart share a bank half whatever the swizzle.)
-template <class E, int D>
+// KS selects a second f32 layout for tiles read only by pattern B: chunk c of
+// row r sits at c ^ (8 * bit 3 of r), which is all pattern B needs (its two
+// half waves read rows 8 apart and land in opposite bank halves), and which
+// leaves the 16 rows of one read sequence a fixed distance apart, so a lane
+// forms their addresses from one base with immediate offsets instead of one
+// XOR per read.  bf16 storage ignores KS.
+template <class E, int D, bool KS = false>
 struct Tile {
   using T = typename E::T;
   static constexpr int ROWB = D * (int)sizeof(T);  // bytes per row
@@ -171,6 +177,8 @@ struct Tile {
       if constexpr (CPR == 4) return (row >> 2) & 3;
       else if constexpr (CPR == 8) return ((row >> 1) & 7) ^ (((row >> 1) & 1) << 2);
       else return ((row & 3) << 2) | ((row >> 2) & 3);
+    } else if constexpr (KS) {
+      return CPR >= 16 ? ((row >> 3) & 1) << 3 : 0;
     } else {
       if constexpr (CPR == 8) return (row >> 1) & 7;
       else return row & 15;
@@ -583,55 +591,70 @@ __device__ inline const void* lane_addr(const void* base, unsigned lane_bytes) {
 
 // The direct loads of one staged tile: rows row0 .. row0+BT-1 of two
 // row-major [S x D] matrices (src0, src1) into two consecutive swizzled
-// tiles at `stage`.  Rows past S read row S-1 (finite; the caller masks
-// them).  Each wave issues NLOADS instructions, each filling 1 KiB of LDS.
+// tiles at `stage`, the second in the KS1 layout of Tile.  Rows past S read
+// row S-1 (finite; the caller masks them).  Each wave issues NLOADS
+// instructions, each filling 1 KiB of LDS.
 //
 // A wave's consecutive loads are RS rows apart.  The swizzle repeats every
-// 16 rows, so when RS and BT are multiples of 16 every load of a wave has the
-// same lane offset from its (wave-uniform) first row: lane_offset() is then
-// computed once per kernel and a whole tile costs one address add per load.
-// The clamped per-lane form remains for tiles that cross S.
-template <class E, int D, int BT, int NW>
+// 16 rows, so when RS and BT are multiples of 16 every load of a wave into
+// one matrix has the same lane offset from its (wave-uniform) first row:
+// lane_offset() is then computed once per kernel per matrix and a whole tile
+// costs one address add per load.  The clamped per-lane form remains for
+// tiles that cross S.
+template <class E, int D, int BT, int NW, bool KS1 = false>
 struct StageLoader {
   using T = typename E::T;
   using TL = Tile<E, D>;
+  using TL1 = Tile<E, D, KS1>;
   static constexpr int CH_PER = BT * TL::CPR;            // chunks per matrix
   static constexpr int NLOADS = 2 * CH_PER / (NW * 64);  // per wave
   static constexpr int BYTES = 2 * BT * TL::ROWB;
   static constexpr int RPS = 64 / TL::CPR;               // rows per 1 KiB slot
   static constexpr int RS = NW * RPS;                    // rows between a wave's loads
+  static constexpr int SPM = CH_PER / 64;                // 1 KiB slots per matrix
   static constexpr bool FAST = RS % 16 == 0 && BT % 16 == 0;
   static_assert((2 * CH_PER) % (NW * 64) == 0, "tile must split into whole wave loads");
   static_assert(CH_PER % 64 == 0, "a 1 KiB slot lies in one matrix");
-  // Byte offset of this lane's chunk from the first row of the wave's first
-  // load (valid for every load of the wave when FAST).
-  __device__ static inline unsigned lane_offset(int w, int lane) {
+  // The matrix of load i of wave w (wave-uniform; a compile-time constant
+  // when a matrix holds whole rounds of the NW waves' loads).
+  __device__ static inline int mat_of(int i, int w) {
+    return SPM % NW == 0 ? i * NW / SPM : (i * NW + w) / SPM;
+  }
+  __host__ __device__ static constexpr int swz(int mat, int row) {
+    return mat == 0 ? TL::swz(row) : TL1::swz(row);
+  }
+  // Byte offset of this lane's chunk of matrix `mat` from the first row of
+  // the wave's first load (valid for every load of the wave into that
+  // matrix when FAST).
+  __device__ static inline unsigned lane_offset(int w, int lane, int mat = 0) {
     const int row = w * RPS + lane / TL::CPR;
-    return (unsigned)((row * D + ((lane % TL::CPR) ^ TL::swz(row)) * TL::EPC) * sizeof(T));
+    return (unsigned)((row * D + ((lane % TL::CPR) ^ swz(mat, row)) * TL::EPC) * sizeof(T));
   }
   __device__ static inline void issue(char* stage, const T* src0, const T* src1, int row0, int S,
-                                      int w, int lane, unsigned lo) {
+                                      int w, int lane, unsigned lo, unsigned lo1) {
     if constexpr (FAST) {
       if (row0 + BT <= S) {
 #pragma unroll
         for (int i = 0; i < NLOADS; ++i) {
-          const int slot = i * NW + w;         // 1 KiB slot of the stage (wave-uniform)
-          const int mat = slot * 64 / CH_PER;  // wave-uniform
+          const int slot = i * NW + w;  // 1 KiB slot of the stage (wave-uniform)
+          const int mat = mat_of(i, w);
           const T* base = (mat == 0 ? src0 : src1) + (size_t)(row0 + i * RS - mat * BT) * D;
-          __builtin_amdgcn_global_load_lds(lane_addr(base, lo), stage + slot * 1024, 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(lane_addr(base, mat == 0 ? lo : lo1),
+                                           stage + slot * 1024, 16, 0, 0);
         }
         return;
       }
       // The tile crosses S: the same lane pattern with the global row clamped.
       const int lrow = lo / (D * (int)sizeof(T));  // tile row of the lane in the first load
       const unsigned col = lo - lrow * D * (int)sizeof(T);
+      const unsigned col1 = lo1 - lrow * D * (int)sizeof(T);
 #pragma unroll
       for (int i = 0; i < NLOADS; ++i) {
         const int slot = i * NW + w;
-        const int mat = slot * 64 / CH_PER;
+        const int mat = mat_of(i, w);
         const int grow = min(row0 + i * RS - mat * BT + lrow, S - 1);
         const char* src = reinterpret_cast<const char*>(mat == 0 ? src0 : src1) +
-                          (size_t)grow * D * sizeof(T) + col;
+                          (size_t)grow * D * sizeof(T) + (mat == 0 ? col : col1);
         __builtin_amdgcn_global_load_lds(src, stage + slot * 1024, 16, 0, 0);
       }
       return;
@@ -643,7 +666,7 @@ struct StageLoader {
       const int mat = chunk / CH_PER;
       const int pc = chunk - mat * CH_PER;
       const int row = pc / TL::CPR;
-      const int logical = (pc % TL::CPR) ^ TL::swz(row);
+      const int logical = (pc % TL::CPR) ^ swz(mat, row);
       const T* src = (mat == 0 ? src0 : src1) + (size_t)min(row0 + row, S - 1) * D + logical * TL::EPC;
       __builtin_amdgcn_global_load_lds(src, stage + slot * 1024, 16, 0, 0);
     }
@@ -657,17 +680,19 @@ struct StageLoader {
                                          int ld1, int row0, int S, int w, int lane) {
     if constexpr (FAST) {
       const int lrow = w * RPS + lane / TL::CPR;
-      const int lcolb = ((lane % TL::CPR) ^ TL::swz(lrow)) * TL::EPC * (int)sizeof(T);
+      const int lcolb0 = ((lane % TL::CPR) ^ swz(0, lrow)) * TL::EPC * (int)sizeof(T);
+      const int lcolb1 = ((lane % TL::CPR) ^ swz(1, lrow)) * TL::EPC * (int)sizeof(T);
       const int lim = row0 + BT <= S ? 0x7fffffff : S - 1;
 #pragma unroll
       for (int i = 0; i < NLOADS; ++i) {
         const int slot = i * NW + w;
-        const int mat = slot * 64 / CH_PER;  // wave-uniform
+        const int mat = mat_of(i, w);
         const size_t grow = (size_t)min(row0 + i * RS - mat * BT + lrow, lim);
         const char* src = mat == 0
                               ? reinterpret_cast<const char*>(src0) + grow * ld0 * sizeof(T)
                               : reinterpret_cast<const char*>(src1) + grow * ld1 * sizeof(T);
-        __builtin_amdgcn_global_load_lds(src + lcolb, stage + slot * 1024, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src + (mat == 0 ? lcolb0 : lcolb1), stage + slot * 1024,
+                                         16, 0, 0);
       }
       return;
     }
@@ -678,7 +703,7 @@ struct StageLoader {
       const int mat = chunk / CH_PER;
       const int pc = chunk - mat * CH_PER;
       const int row = pc / TL::CPR;
-      const int logical = (pc % TL::CPR) ^ TL::swz(row);
+      const int logical = (pc % TL::CPR) ^ swz(mat, row);
       const size_t r = (size_t)min(row0 + row, S - 1);
       const T* src = mat == 0 ? src0 + r * ld0 : src1 + r * ld1;
       __builtin_amdgcn_global_load_lds(src + logical * TL::EPC, stage + slot * 1024, 16, 0, 0);
@@ -846,14 +871,33 @@ __device__ __attribute__((always_inline)) inline s16x4 ds_read_tr(
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4*>(p));
 }
 
-template <class E, int COLS>
+template <class E, int COLS, bool KS = false>
 __device__ inline void read_kslot_operand(RegOperand<E>& X, const char* tile, int row0, int col0,
                                           int lane) {
   // X in the k-slot layout of RegOperand: for this lane's column col0 + n,
   // the k-slot rows row0 + rho(w, h) (f32) or row0 + 16u + 8h + t (bf16).
-  using TL = Tile<E, COLS>;
+  using TL = Tile<E, COLS, KS>;
   const int h = lane >> 5, n = lane & 31;
-  if constexpr (is_bf16<E>()) {
+  if constexpr (KS && !is_bf16<E>()) {
+    // k-slot layout (row0 and col0 multiples of 16 and 32): every k-slot row
+    // of the lane is row0 + 8h plus a constant, all with the lane's chunk
+    // XOR 8h, so one base address serves all 16 reads.
+    static_assert(TL::EPC == 4, "f32 tile");
+    const int sw = TL::CPR >= 16 ? 8 * h : 0;
+    const char* p = tile + (row0 + 8 * h) * TL::ROWB + ((((col0 >> 2) ^ sw) + (n >> 2)) << 4) +
+                    (n & 3) * 4;
+    if constexpr (mma_bf16<E>()) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          X.v[u][t] = (__bf16)*reinterpret_cast<const float*>(p + (16 * u + t) * TL::ROWB);
+    } else {
+#pragma unroll
+      for (int w = 0; w < 16; ++w)
+        X.v[w] = *reinterpret_cast<const float*>(p + (rho(w, 0)) * TL::ROWB);
+    }
+  } else if constexpr (is_bf16<E>()) {
     const int g = lane >> 4, r = lane & 15;
     const int col = col0 + 16 * (g & 1) + 4 * (r & 3);
 #pragma unroll
@@ -883,11 +927,11 @@ __device__ inline void read_kslot_operand(RegOperand<E>& X, const char* tile, in
   }
 }
 
-template <class E, int D, bool REG_IS_A>
+template <class E, int D, bool REG_IS_A, bool KS = false>
 __device__ inline f32x16 second_tile(const RegOperand<E>& R, const char* tile, int row0, int col0,
                                      int lane, f32x16 acc) {
   RegOperand<E> X;
-  read_kslot_operand<E, D>(X, tile, row0, col0, lane);
+  read_kslot_operand<E, D, KS>(X, tile, row0, col0, lane);
   constexpr int NU = 16 / E::KL;
 #pragma unroll
   for (int u = 0; u < NU; ++u) acc = REG_IS_A ? E::mma(R.v[u], X.v[u], acc) : E::mma(X.v[u], R.v[u], acc);

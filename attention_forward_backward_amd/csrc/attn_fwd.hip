@@ -64,7 +64,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   constexpr int BR = 32 * RB;            // queries per item
   constexpr int BK = 32 * NSPLIT * KPW;  // keys per staged tile
   constexpr int NDB = D / 32;
-  using LD = StageLoader<E, D, BK, NW>;
+  using LD = StageLoader<E, D, BK, NW, true>;  // V in the k-slot layout (read by PV only)
   constexpr int STAGE = LD::BYTES;
   constexpr int TILEB = BK * TL::ROWB;  // one matrix tile; V follows K in a stage
   using QL = TileLoader<E, D, BR, NW>;
@@ -85,6 +85,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
   const int ldk = row_ld<STR, D>(lay.k), ldv = row_ld<STR, D>(lay.v);
   const int ldq = row_ld<STR, D>(lay.q), ldo = row_ld<STR, D>(lay.o);
   const unsigned lo = STR ? 0u : LD::lane_offset(w, lane);
+  const unsigned lo1 = STR ? 0u : LD::lane_offset(w, lane, 1);
   const unsigned qlo = QL::lane_offset(ldq, w, lane);
   auto item_qt = [&](int it) { return nqt - 1 - (KS ? it / BH / nch : it / BH); };
   // Key tiles of item it's query tile: those holding a key visible from one
@@ -155,7 +156,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
       LD::issue_ld(smem + slot * STAGE, K + kbase, ldk, V + vbase, ldv, (lkb + lkt) * BK, lrows,
                    w, lane);
     else
-      LD::issue(smem + slot * STAGE, K + kbase, V + vbase, (lkb + lkt) * BK, lrows, w, lane, lo);
+      LD::issue(smem + slot * STAGE, K + kbase, V + vbase, (lkb + lkt) * BK, lrows, w, lane, lo,
+                lo1);
     vm += LD::NLOADS;
     mk.set(slot, vm);
     if (++lkt == lnkt) {
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-          oacc[db] = second_tile<E, D, false>(P, Vt, kb * 32, db * 32, lane, oacc[db]);
+          oacc[db] = second_tile<E, D, false, true>(P, Vt, kb * 32, db * 32, lane, oacc[db]);
         __builtin_amdgcn_s_setprio(0);
       }
     }
