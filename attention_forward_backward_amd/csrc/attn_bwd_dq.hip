@@ -294,8 +294,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
     const int si = sc;  // kt % NST
     wait_tiles<NL>(min(NST - 2, nkt - 1 - kt));
     lds_barrier();
-    if (kt + NST - 1 < nkt) issue(kt + NST - 1);
-    if (!wave_active) return;
+    // The next tile's loads go out after the first product of the step is
+    // issued, and the products run at raised wave priority: together (not
+    // either alone) 23.0 -> 22.3 us for f32 at B8 H12 S512 D64 causal.
+    bool issued = false;
+    if (!wave_active) {
+      if (kt + NST - 1 < nkt) issue(kt + NST - 1);
+      return;
+    }
     const char* St = smem + si * STAGE;
     const char* Kt = St + LDS_::BYTES;
 #pragma unroll
@@ -305,10 +311,20 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_gemm_kernel(
       if (!(kk0 < L && (!CAUSAL || kk0 <= q0 + 31 + off))) continue;  // wave-uniform
       RegOperand<E> R;  // dS[q0 + n][keys]: k-slots from the dS^T rows
       read_kslot_operand<E, BR>(R, St, kb * 32, qb * 32, lane);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db) {
         acc[db] = second_tile<E, D, false>(R, Kt, kb * 32, db * 32, lane, acc[db]);
+        if (db == 0 && !issued) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (kt + NST - 1 < nkt) issue(kt + NST - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          issued = true;
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
     }
+    if (!issued && kt + NST - 1 < nkt) issue(kt + NST - 1);
   };
   if constexpr (NST * STAGE <= 65536) {
     for_stages<NST>(nkt, step);
