@@ -348,8 +348,13 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
         if (!(qq0 < Sq && (!CAUSAL || qq0 + 31 >= k0 - coff) && (!CROSS || k0 < cL)))
           continue;  // wave-uniform
         const int arow = qbl * 32 + pi32(n);
+        // f32 runs the products at raised wave priority, so that while one
+        // wave of a SIMD is in its softmax the other's MFMAs issue first
+        // (70.4 -> 69.2 us at B8 H12 S512 D64 causal; bf16 measured slower)
+        if constexpr (!is_bf16<E>()) __builtin_amdgcn_s_setprio(1);
         f32x16 s = dot_tile<E, D>(Qt, arow, h, kf, zero16());
         f32x16 dp = dot_tile<E, D>(dOt, arow, h, vf, zero16());
+        if constexpr (!is_bf16<E>()) __builtin_amdgcn_s_setprio(0);
         if (!issued) {
           __builtin_amdgcn_sched_barrier(0);
           issue_next();
@@ -424,6 +429,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
         RegOperand<E> P, dS;
         P.set(s);
         dS.set(dp);
+        if constexpr (!is_bf16<E>()) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           // dV^T (d x keys) += dO^T P and dK^T += Q^T dS: the register
@@ -431,6 +437,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
           dvacc[db] = second_tile<E, D, false>(P, dOt, qbl * 32, db * 32, lane, dvacc[db]);
           dkacc[db] = second_tile<E, D, false>(dS, Qt, qbl * 32, db * 32, lane, dkacc[db]);
         }
+        if constexpr (!is_bf16<E>()) __builtin_amdgcn_s_setprio(0);
       }
       if (!issued) issue_next();  // (no block of the tile was visible)
     }
