@@ -8,9 +8,14 @@
 * tests/abi_check.cpp drives the C ABI's argument validation (attn_api.hip)
   with rejected arguments, the kernel launchers replaced by stubs that abort.
 * tests/sched_check.cpp checks the static schedule builder.
+* tests/tile_check.cpp checks the LDS tile layouts: each a permutation of a
+  row's chunks, bank-conflict-free column reads for the second product, the
+  single-base addresses of the k-slot layout, and that every direct load of
+  the stage loaders lands where the tile layout places its chunk.
 
-The ring model, the ABI check and the schedule check are also built with
-AddressSanitizer and UndefinedBehaviorSanitizer on their host code."""
+The ring model, the ABI check, the schedule check and the tile check are
+also built with AddressSanitizer and UndefinedBehaviorSanitizer on their
+host code."""
 import os
 import shutil
 import subprocess
@@ -56,8 +61,16 @@ def test_ring_model_and_planted_mistakes(tmp_path):
         assert r.returncode != 0 and "FAIL" in r.stdout, (plant, r.stdout[-500:])
 
 
+def test_tile_layouts(tmp_path):
+    exe = _build(tmp_path, "tile_check", ["tests/tile_check.cpp"])
+    r = _run(exe)
+    print(r.stdout)
+    assert r.returncode == 0 and r.stdout.strip().endswith("OK"), r.stdout + r.stderr
+
+
 @pytest.mark.parametrize("name,sources", [
     ("ring_model", ["tests/ring_model.cpp"]),
+    ("tile_check", ["tests/tile_check.cpp"]),
     ("abi_check", ["tests/abi_check.cpp", "attention_forward_backward_amd/csrc/attn_api.hip"]),
     ("sched_check", ["tests/sched_check.cpp"]),
 ])
