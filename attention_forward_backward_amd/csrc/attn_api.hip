@@ -239,7 +239,8 @@ attn_status_t bwd_impl(attn_dtype_t dtype, const void* q, const void* k, const v
                              workspace_bytes, batch, heads, sq, sk, head_dim, kvlen, causal, scale,
                              stream, layout);
   if (rope != nullptr) a.rope = *rope;
-  if ((st = from_hip(attn::launch_bwd_prep(a))) != ATTN_OK) return st;
+  a.dfused = attn::dkdv_dfused(a);
+  if (!a.dfused && (st = from_hip(attn::launch_bwd_prep(a))) != ATTN_OK) return st;
   if ((st = from_hip(attn::launch_bwd_dkdv(a))) != ATTN_OK) return st;
   return from_hip(attn::launch_bwd_dq(a));
 }

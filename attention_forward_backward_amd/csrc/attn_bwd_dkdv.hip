@@ -36,14 +36,15 @@
 namespace attn {
 
 template <class E, int D, int NW, int NSPLIT, int KPW, int NST, bool CAUSAL, bool WDS, bool CROSS,
-          bool QSPLIT, bool STR, bool ROPE>
+          bool QSPLIT, bool STR, bool ROPE, bool DF = false>
 __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_F32 : 1) void bwd_dkdv_kernel(
     const typename E::T* __restrict__ Q, const typename E::T* __restrict__ K,
     const typename E::T* __restrict__ V, const typename E::T* __restrict__ dO,
     const float* __restrict__ Dws, typename E::T* __restrict__ dK, typename E::T* __restrict__ dV,
     typename E::T* __restrict__ dSout, int SPq, int SPk, int Sq, int Sk_, int Lws, float c,
     float scale, int BH, int H, const int* __restrict__ kvlen, float* __restrict__ part, int nqs_,
-    int qpc_, int nitems, const Sched sched, const Layout lay, const RopeTab rope) {
+    int qpc_, int nitems, const Sched sched, const Layout lay, const RopeTab rope,
+    const typename E::T* __restrict__ Oin, const float* __restrict__ LSEin) {
   // Queries Sq, keys Sk (one length in self-attention, CROSS = false); per
   // batch*head the first L keys exist and key j is visible from query i iff
   // j < L and, when causal, j <= i + off (head_keys).  Lws: offset of the
@@ -58,6 +59,11 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   // ROPE (STR): Q and K hold RoPE-turned rows; dK leaves turned back by the
   // transposed rotation of key j (table row rope.pos + j) -- here, or with
   // QSPLIT in the reduce kernel.
+  // DF (bf16, dS stored, plain layout): no prep pass ran; D and LSE*log2(e)
+  // of each query tile are formed here from O (Oin, whose rows follow Q and
+  // dO in a stage), dO and the LSE (LSEin): the statistics of a stage hold
+  // the raw LSE (loaded twice, to keep the load count), then LSE*log2(e) and
+  // D written by the waves.
   using T = typename E::T;
   using TL = Tile<E, D>;
   constexpr int RB = NW / NSPLIT;        // 32-key blocks per item
@@ -66,12 +72,16 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   constexpr int NDB = D / 32;
   using LD = StageLoader<E, D, BQ, NW>;
   constexpr int TILEB = BQ * TL::ROWB;                            // dO follows Q in a stage
+  using OL = TileLoader<E, D, BQ, NW>;                            // DF: O follows dO
   // A ring stage holds the tiles only (its LDS addresses then fit the read
   // instructions' 16-bit offsets); the per-stage statistics (LSE*log2e, D)
   // follow all the stages.
-  constexpr int STAGE = LD::BYTES;
-  constexpr int STATS = 2 * BQ * 4;
-  constexpr int NL = LD::NLOADS + 1;                              // loads per wave per tile
+  constexpr int STAGE = LD::BYTES + (DF ? OL::BYTES : 0);
+  constexpr int SQF = (DF ? 4 : 2) * BQ;  // floats of statistics per stage
+  constexpr int STATS = SQF * 4;
+  constexpr int NL = LD::NLOADS + (DF ? OL::NLOADS : 0) + 1;      // loads per wave per tile
+  static_assert(!DF || (is_bf16<E>() && WDS && !STR && !CROSS && !QSPLIT && !ROPE),
+                "D formed in dK+dV: bf16 on the dS path, plain layout only");
   // Partials of the NSPLIT-1 helper waves of every key block, one matrix
   // (dK or dV): summed through the stage just consumed, in one pass when it
   // holds both matrices, else in two.
@@ -93,6 +103,7 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
   const int nqs = QSPLIT ? nqs_ : 1;
   const int qpc = QSPLIT ? qpc_ : nqt;
   const unsigned lane_off = STR ? 0u : LD::lane_offset(w, lane);
+  const unsigned o_off = DF ? OL::lane_offset(D, w, lane) : 0u;
   const int ldq = row_ld<STR, D>(lay.q), ldk = row_ld<STR, D>(lay.k);
   const int ldv = row_ld<STR, D>(lay.v), lddo = row_ld<STR, D>(lay.dout);
   // First query tile with a query that sees a key of key tile kt (nqt: none).
@@ -139,6 +150,8 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
       } else {
         LD::issue(st, K + lhk * D, V + lhk * D, lkt * BKV, CROSS ? max(lL, 1) : Sk, w, lane,
                   lane_off, lane_off);
+        // (DF: the head's first O rows, unused, so every tile has NL loads)
+        if constexpr (DF) OL::issue(st + LD::BYTES, Oin + lhq * D, D, 0, Sq, 0, w, lane, o_off);
       }
     } else {
       if constexpr (STR) {
@@ -147,10 +160,12 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
                      dO + head_off<STR, D>(lay.dout, bhl, H, Sq), lddo, lqt * BQ, Sq, w, lane);
       } else {
         LD::issue(st, Q + lhq * D, dO + lhq * D, lqt * BQ, Sq, w, lane, lane_off, lane_off);
+        if constexpr (DF)
+          OL::issue(st + LD::BYTES, Oin + lhq * D, D, lqt * BQ, Sq, 0, w, lane, o_off);
       }
     }
-    issue_stats<BQ, NW>(stats0 + (nissued % NST) * (2 * BQ), Dws + Lws + lhq, Dws + lhq,
-                        head ? 0 : lqt * BQ, Sq, w, lane);
+    issue_stats<BQ, NW>(stats0 + (nissued % NST) * SQF, DF ? LSEin + lhq : Dws + Lws + lhq,
+                        DF ? LSEin + lhq : Dws + lhq, head ? 0 : lqt * BQ, Sq, w, lane);
     ++nissued;
     if (head) {
       lqt = first_qt(lkt, lL, loff);
@@ -338,7 +353,8 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
       const int si = pos % NST;
       const char* Qt = smem + si * STAGE;
       const char* dOt = Qt + TILEB;
-      const float* lse2s = stats0 + si * (2 * BQ);
+      float* const stw = stats0 + si * SQF + (DF ? 2 * BQ : 0);  // LSE*log2(e), then D
+      const float* lse2s = stw;
       const float* Ds = lse2s + BQ;
 
 #pragma unroll
@@ -360,6 +376,32 @@ __global__ __launch_bounds__(NW * 64, !is_bf16<E>() && D <= 64 ? ATTN_DKDV_MINW_
           issue_next();
           __builtin_amdgcn_sched_barrier(0);
           issued = true;
+        }
+        if constexpr (DF) {
+          // D and LSE*log2(e) of the block's 32 queries: lane (h, n) dots
+          // half h of query row qbl*32 + n of dO and O, the halves add, and
+          // every lane stores its row's pair (both halves, and the other wave
+          // of this query block, store the same bits), read back below.
+          const int qr = qbl * 32 + n;
+          RowFrag<E, D> fd, fo;
+          load_row_frag_lds<E, D>(fd, dOt, qr, h, true);
+          load_row_frag_lds<E, D>(fo, dOt + TILEB, qr, h, true);
+          float dsum = 0.f;
+#pragma unroll
+          for (int c = 0; c < RowFrag<E, D>::NS; ++c) {
+            const bf16x8 x = fd.f[c], y = fo.f[c];
+            dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 0, 1),
+                                                   __builtin_shufflevector(y, y, 0, 1), dsum, false);
+            dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 2, 3),
+                                                   __builtin_shufflevector(y, y, 2, 3), dsum, false);
+            dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 4, 5),
+                                                   __builtin_shufflevector(y, y, 4, 5), dsum, false);
+            dsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(x, x, 6, 7),
+                                                   __builtin_shufflevector(y, y, 6, 7), dsum, false);
+          }
+          dsum += __shfl_xor(dsum, 32);
+          stw[qr] = stw[qr - 2 * BQ] * kLog2e;
+          stw[BQ + qr] = dsum;
         }
         if ((CAUSAL && qq0 < k0 + 31 - coff) || qq0 + 32 > Sq || k0 + 32 > (CROSS ? cL : Sk)) {
           // query(r) = qq0 + 8h + (16*(r/8) + r%8) sees key kj iff
@@ -535,13 +577,15 @@ __global__ __launch_bounds__(64) void bwd_dkdv_reduce_kernel(const float* __rest
   }
 }
 
-template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool QSPLIT, bool STR, bool ROPE>
+template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool QSPLIT, bool STR, bool ROPE,
+          bool DF = false>
 static hipError_t launch(const BwdArgs& a) {
   constexpr LShape SH = dkdv_shape(is_bf16<E>(), D);
-  constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
+  constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw;
+  constexpr int NST = DF ? ATTN_DKDV_NST_BF16_DF : SH.nst;
   using T = typename E::T;
   constexpr auto kern =
-      bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS, QSPLIT, STR, ROPE>;
+      bwd_dkdv_kernel<E, D, NW, NSPLIT, KPW, NST, CAUSAL, WDS, CROSS, QSPLIT, STR, ROPE, DF>;
   const Layout lay = a.layout != nullptr ? *a.layout : Layout{};
   constexpr int BKV = 32 * (NW / NSPLIT);
   constexpr int BQ = 32 * NSPLIT * KPW;
@@ -569,7 +613,8 @@ static hipError_t launch(const BwdArgs& a) {
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k,
                      (const T*)a.v, (const T*)a.dout, a.delta, (T*)a.dk, (T*)a.dv, (T*)a.ds, a.SPq,
                      a.SPk, a.Sq, a.Sk, a.BH * a.Sq, a.scale * kLog2e, a.scale, a.BH, a.H, a.kvlen,
-                     QSPLIT ? a.part : nullptr, nqs, qpc, nitems, sched, lay, a.rope);
+                     QSPLIT ? a.part : nullptr, nqs, qpc, nitems, sched, lay, a.rope,
+                     DF ? (const T*)a.o : nullptr, DF ? a.lse : nullptr);
   if (QSPLIT) {
     const long long nel4 = (long long)a.BH * a.Sk * D / 4;
     const long long nthr = ROPE ? nel4 / 2 : nel4;
@@ -582,6 +627,10 @@ static hipError_t launch(const BwdArgs& a) {
 
 template <class E, int D, bool CAUSAL, bool WDS, bool CROSS, bool STR, bool ROPE = false>
 static hipError_t launch_s(const BwdArgs& a) {
+  if constexpr (is_bf16<E>() && WDS && !CROSS && !STR && !ROPE) {
+    if (a.dfused) return launch<E, D, CAUSAL, WDS, CROSS, false, STR, ROPE, true>(a);
+  }
+  if (a.dfused) return hipErrorInvalidValue;  // (dkdv_dfused admits only the case above)
   if (a.part != nullptr && a.nqs > 1) return launch<E, D, CAUSAL, WDS, CROSS, true, STR, ROPE>(a);
   return launch<E, D, CAUSAL, WDS, CROSS, false, STR, ROPE>(a);
 }

@@ -88,6 +88,10 @@
 #ifndef ATTN_DKDV_NST_BF16
 #define ATTN_DKDV_NST_BF16 3
 #endif
+// the bf16 dK+dV that forms D itself (dkdv_dfused): 2 stages
+#ifndef ATTN_DKDV_NST_BF16_DF
+#define ATTN_DKDV_NST_BF16_DF 2
+#endif
 // The dQ GEMM (dS K with the stored dS^T): waves per workgroup, waves
 // sharing each 32-query block, LDS stages.  At B8 H12 S512 D64 causal the
 // f32 defaults took 23.4 us against 27.9 with 3 stages, 26.3 with 8 waves
@@ -238,7 +242,18 @@ struct BwdArgs {
   hipStream_t stream;
   RopeTab rope;  // rope.cos null: no RoPE; else dQ and dK leave turned back
                  // (transposed rotation, query / key i at table row rope.pos + i)
+  bool dfused = false;  // dK+dV forms D and LSE*log2(e) itself from O, dO and
+                        // the LSE (no prep pass; the workspace's D part unused)
 };
+
+// The bf16 backward on the dS path, plain layout and no padded keys, query
+// chunks or RoPE forms D inside dK+dV (its step is instruction-bound, so the
+// few dot products per query tile cost less than the prep pass they replace;
+// f32 keeps the pass: the O rows would not fit its register budget).
+inline bool dkdv_dfused(const BwdArgs& a) {
+  return a.bf16 && a.ds != nullptr && a.layout == nullptr && !a.cross &&
+         !(a.part != nullptr && a.nqs > 1) && a.rope.cos == nullptr;
+}
 
 // Rotary embedding / layout pass: dst rows = R(src rows) (or R^T, or a plain
 // copy without tables); element (b, h, s, d) of a tensor at

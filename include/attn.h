@@ -164,7 +164,10 @@ size_t attn_bwd_workspace_size_min(attn_dtype_t dtype, int batch, int heads,
 /*
  * Backward pass (the pages' attention derivative: dQ kernel and fused dK+dV
  * kernel, Section 3.3; profiled in Section 7.3): attn_bwd_prep, then
- * attn_bwd_dkdv, then attn_bwd_dq, enqueued on `stream`.
+ * attn_bwd_dkdv, then attn_bwd_dq, enqueued on `stream` -- except that bf16
+ * on the dS path (no padded keys, strided layout or RoPE) runs no prep: its
+ * dK+dV kernel forms D and LSE*log2(e) of each query tile from O, dO and
+ * the LSE itself (workspace part 1 is then left unused).
  *   in : q, k, v, o, dout  [B,H,S,D] dtype  (o = the forward's output)
  *        lse               [B,H,S]   float32 (the forward's LSE)
  *   out: dq, dk, dv        [B,H,S,D] dtype  gradients of the loss

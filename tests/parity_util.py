@@ -85,10 +85,16 @@ def gpu_fwd_bwd(inp: dict, shape, dtype: str, causal: bool, scale: float, guard:
     afb.attn_fwd(dev["q"], dev["k"], dev["v"], t["o"], t["lse"], causal, scale)
     afb.attn_bwd(dev["q"], dev["k"], dev["v"], t["o"], dev["do"], t["lse"],
                  t["dq"], t["dk"], t["dv"], ws, causal, scale)
+    # The prep stage on its own (attn_bwd runs it, except where dK+dV forms D
+    # itself: bf16 on the dS path), into a fresh minimum workspace: D and
+    # LSE*log2(e) of every row.
+    wsp = torch.full((workspace_bytes("min", code, shape, causal) // 4,), float("nan"),
+                     dtype=torch.float32, device="cuda")
+    afb.attn_bwd_prep(t["o"], dev["do"], t["lse"], wsp)
     torch.cuda.synchronize()
     host = {k_: to_host(v_) for k_, v_ in t.items()}
-    host["delta"] = ws[: B * H * S].cpu().numpy().reshape(B, H, S)
-    host["lse2"] = ws[B * H * S: 2 * B * H * S].cpu().numpy().reshape(B, H, S)
+    host["delta"] = wsp[: B * H * S].cpu().numpy().reshape(B, H, S)
+    host["lse2"] = wsp[B * H * S: 2 * B * H * S].cpu().numpy().reshape(B, H, S)
     if guard:
         for name, (buf, _) in bufs.items():
             tail = buf[buf.numel() - guard:].float().cpu().numpy()

@@ -272,16 +272,18 @@ struct BwdCase {
   int D, BH, H, Sq, Sk;
   bool causal, cross, wds;
   std::vector<int> kvlen;
-  int nqs;  // query chunks (1: no split)
+  int nqs;          // query chunks (1: no split)
+  bool df = false;  // bf16 with D formed in the kernel: O rows in every tile, its own ring depth
 };
 
-template <class E, int D>
+template <class E, int D, bool DF = false>
 bool model_dkdv(const BwdCase& c, int G) {
   constexpr LShape SH = dkdv_shape(is_bf16<E>(), D);
-  constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw, NST = SH.nst;
+  constexpr int NW = SH.nw, NSPLIT = SH.nsplit, KPW = SH.kpw;
+  constexpr int NST = DF ? ATTN_DKDV_NST_BF16_DF : SH.nst;
   constexpr int RB = NW / NSPLIT, BKV = 32 * RB, BQ = 32 * NSPLIT * KPW, NDB = D / 32;
   using LD = StageLoader<E, D, BQ, NW>;
-  constexpr int NL = LD::NLOADS + 1;
+  constexpr int NL = LD::NLOADS + (DF ? TileLoader<E, D, BQ, NW>::NLOADS : 0) + 1;
   constexpr int NSTORE = 16 * (int)sizeof(typename E::T) / 16;
   const int nstore = c.wds ? NSTORE : 0;
   const int Sq = c.Sq, Sk = c.cross ? c.Sk : c.Sq, BH = c.BH, H = c.H;
@@ -437,6 +439,13 @@ bool fwd_d(const FwdCase& c, int G) {
 }
 template <class E>
 bool dkdv_d(const BwdCase& c, int G) {
+  if (c.df) {
+    switch (c.D) {
+      case 32: return model_dkdv<E, 32, true>(c, G);
+      case 64: return model_dkdv<E, 64, true>(c, G);
+      default: return model_dkdv<E, 128, true>(c, G);
+    }
+  }
   switch (c.D) {
     case 32: return model_dkdv<E, 32>(c, G);
     case 64: return model_dkdv<E, 64>(c, G);
@@ -462,8 +471,14 @@ int main(int argc, char** argv) {
             BwdCase b{bf16, D, BH, 4, S, S, causal, false, true, {}, 1};
             const bool ok = (bf16 ? fwd_d<EBF16>(f, G) : fwd_d<EF32>(f, G)) &&
                             (bf16 ? dkdv_d<EBF16>(b, G) : dkdv_d<EF32>(b, G));
+            bool ok3 = true;
+            if (bf16) {  // (the D-fused bf16 dK+dV: dS stored, self-attention)
+              b.df = true;
+              ok3 = dkdv_d<EBF16>(b, G);
+              b.df = false;
+            }
             b.wds = false;
-            const bool ok2 = bf16 ? dkdv_d<EBF16>(b, G) : dkdv_d<EF32>(b, G);
+            const bool ok2 = (bf16 ? dkdv_d<EBF16>(b, G) : dkdv_d<EF32>(b, G)) && ok3;
             ++cases;
             if (!ok || !ok2) {
               std::printf("case: %s D%d S%d causal%d G%d\n", bf16 ? "bf16" : "f32", D, S, causal, G);

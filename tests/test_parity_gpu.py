@@ -27,7 +27,7 @@ def test_config_parity(name, dtype, seed, ws):
          ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= TOL[dtype], (k, v)
-    # D and LSE*log2(e) written to the workspace by the prep kernel
+    # D and LSE*log2(e) as the prep stage writes them to the workspace
     assert max_rel_err(host["delta"], ref["delta"]) <= TOL[dtype]
     assert max_rel_err(host["lse2"], ref["lse"] * np.log2(np.e)) <= TOL[dtype]
 
