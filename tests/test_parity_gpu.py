@@ -145,6 +145,34 @@ def test_split_stages_match_fused_call(ws):
     assert torch.equal(dq, outs["dq"]) and torch.equal(dk, outs["dk"]) and torch.equal(dv, outs["dv"])
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_split_stages_bf16(causal):
+    """bf16 with the recommended workspace: attn_bwd forms D inside dK+dV (no
+    prep launch), while the three stage entry points run the prep pass and
+    the dK+dV kernel that reads D from the workspace; both against the
+    oracle, and against each other to the rounding of D."""
+    import torch
+    import attention_forward_backward_amd as afb
+    from parity_util import oracle_all, to_host
+    shape = (2, 3, 197, 64)
+    inp = synth.make_inputs(shape, 5, "bf16")
+    note(f"[gpu case] bf16 split stages shape={shape} causal={causal}")
+    h, dev, outs = gpu_fwd_bwd(inp, shape, "bf16", causal, 0.125, ws_mode="full")
+    ref = oracle_all(inp, causal, 0.125)
+    dq, dk, dv = (torch.empty_like(outs[n]) for n in ("dq", "dk", "dv"))
+    wsb = torch.empty(afb.attn_bwd_workspace_size(afb.ATTN_BF16, *shape, causal),
+                      dtype=torch.uint8, device="cuda")
+    afb.attn_bwd_prep(outs["o"], dev["do"], outs["lse"], wsb)
+    afb.attn_bwd_dkdv(dev["q"], dev["k"], dev["v"], dev["do"], dk, dv, wsb, causal, 0.125)
+    afb.attn_bwd_dq(dev["q"], dev["k"], dev["v"], dev["do"], dq, wsb, causal, 0.125)
+    torch.cuda.synchronize()
+    for t, n in zip((dq, dk, dv), ("dq", "dk", "dv")):
+        staged = to_host(t)
+        assert max_rel_err(staged, ref[n]) <= TOL["bf16"], ("staged", n)
+        assert max_rel_err(h[n], ref[n]) <= TOL["bf16"], ("fused", n)
+        assert max_rel_err(staged, h[n]) <= TOL["bf16"], ("staged vs fused", n)
+
+
 def test_paths_agree():
     """The dS + GEMM path and the recompute path give the same gradients to
     within rounding (they sum the same terms in a different order)."""
