@@ -94,10 +94,14 @@ constexpr int CT = 64;  // output tile rows and columns
 #define ATTN_CONV_PREFETCH 1
 #endif
 static_assert(ATTN_CONV_PREFETCH == 1 || ATTN_CONV_PREFETCH == 2, "prefetch depth 1 or 2");
-template <class E>
-__host__ __device__ constexpr int conv_kc() {
-  return is_bf16<E>() ? ATTN_CONV_KC_BF16 : ATTN_CONV_KC_F32;
-}
+// bf16 with both operands gathered as 16-byte vectors: 64 values per chunk
+// (1x1 C1024->256 forward at 14x14, batch 32: 21.8 -> 18.0 us; 3x3 C64->64
+// data derivative 46.9 -> 45.2; 128 helped the 1x1 forward further but not
+// the 3x3 layer, and with element gathers larger chunks doubled the stem's
+// forward, so those keep 32).
+#ifndef ATTN_CONV_KC_BF16_VEC
+#define ATTN_CONV_KC_BF16_VEC 64
+#endif
 
 // A[m][kk] of the GEMM (zero outside the tensors and past KD).
 template <class T, int MODE>
@@ -152,6 +156,15 @@ __device__ inline float b_val(const T* __restrict__ b, const ConvShape& s, int k
 // every group of V is contiguous and 16-byte aligned (channel counts and
 // reduction lengths multiples of V, aligned base pointers).
 enum Gather { G_SCALAR = 0, G_ALONG_K = 1, G_ALONG_ROW = 2 };
+
+// Reduction values per chunk of a kernel with gathers GA, GB.
+template <class E, int GA, int GB>
+__host__ __device__ constexpr int conv_kc() {
+  if constexpr (is_bf16<E>())
+    return GA != G_SCALAR && GB != G_SCALAR ? ATTN_CONV_KC_BF16_VEC : ATTN_CONV_KC_BF16;
+  else
+    return ATTN_CONV_KC_F32;
+}
 
 // The V values of operand WHICH (0: A, 1: B) at output index row (the first
 // of V rows with G_ALONG_ROW) and reduction index kk (the first of V with
@@ -213,7 +226,7 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
   // (blockIdx.y, blockIdx.x); GA, GB: how A and B are gathered (Gather).
   using T = typename E::T;
   constexpr int V = 16 / (int)sizeof(T);            // elements per vector gather
-  constexpr int KC = conv_kc<E>();
+  constexpr int KC = conv_kc<E, GA, GB>();
   constexpr int PER = CT * KC / 256;                // values of one operand per thread per chunk
   constexpr int NV = CT * KC / V / 256;             // vector groups per thread per chunk
   constexpr int LDK = KC + (is_bf16<E>() ? 8 : 1);  // padded LDS row (bf16: 16-byte reads)
@@ -433,9 +446,12 @@ bool make_shape(int N, int H, int W, int C, int K, int R, int S, int sh, int sw,
 }
 
 template <class E, int MODE, int GA, int GB>
-void launch_g(const void* a, const void* b, void* out, float* part, int kspan, dim3 grid,
+void launch_g(const void* a, const void* b, void* out, float* part, int nz, dim3 grid,
               const ConvShape& s, hipStream_t st) {
   using T = typename E::T;
+  // each of the nz reduction slices a whole number of chunks
+  constexpr int KC = attn::conv_kc<E, GA, GB>();
+  const int kspan = ((s.KD + nz - 1) / nz + KC - 1) / KC * KC;
   hipLaunchKernelGGL((attn::conv_igemm_kernel<E, MODE, GA, GB>), grid, dim3(256), 0, st,
                      (const T*)a, (const T*)b, (T*)out, part, kspan, s);
 }
@@ -454,29 +470,27 @@ hipError_t launch(const void* a, const void* b, void* out, float* part, int nz, 
   } else {
     s.M = s.K; s.NC = s.R * s.S * s.C; s.KD = s.N * s.P * s.Q;
   }
-  constexpr int KC = attn::conv_kc<E>();
-  const int kspan = ((s.KD + nz - 1) / nz + KC - 1) / KC * KC;
   dim3 grid((s.NC + 63) / 64, (s.M + 63) / 64, nz);
   // Vector gathers where every group of V is contiguous and aligned.
   using namespace attn;
   if (MODE == CONV_FWD) {
     const bool va = s.C % V == 0 && aligned16(a), vb = s.KD % V == 0 && aligned16(b);
-    if (va && vb) launch_g<E, CONV_FWD, G_ALONG_K, G_ALONG_K>(a, b, out, part, kspan, grid, s, st);
-    else if (va) launch_g<E, CONV_FWD, G_ALONG_K, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
-    else if (vb) launch_g<E, CONV_FWD, G_SCALAR, G_ALONG_K>(a, b, out, part, kspan, grid, s, st);
-    else launch_g<E, CONV_FWD, G_SCALAR, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
+    if (va && vb) launch_g<E, CONV_FWD, G_ALONG_K, G_ALONG_K>(a, b, out, part, nz, grid, s, st);
+    else if (va) launch_g<E, CONV_FWD, G_ALONG_K, G_SCALAR>(a, b, out, part, nz, grid, s, st);
+    else if (vb) launch_g<E, CONV_FWD, G_SCALAR, G_ALONG_K>(a, b, out, part, nz, grid, s, st);
+    else launch_g<E, CONV_FWD, G_SCALAR, G_SCALAR>(a, b, out, part, nz, grid, s, st);
   } else if (MODE == CONV_DATA) {
     const bool va = s.K % V == 0 && aligned16(a), vb = s.C % V == 0 && aligned16(b);
-    if (va && vb) launch_g<E, CONV_DATA, G_ALONG_K, G_ALONG_ROW>(a, b, out, part, kspan, grid, s, st);
-    else if (va) launch_g<E, CONV_DATA, G_ALONG_K, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
-    else if (vb) launch_g<E, CONV_DATA, G_SCALAR, G_ALONG_ROW>(a, b, out, part, kspan, grid, s, st);
-    else launch_g<E, CONV_DATA, G_SCALAR, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
+    if (va && vb) launch_g<E, CONV_DATA, G_ALONG_K, G_ALONG_ROW>(a, b, out, part, nz, grid, s, st);
+    else if (va) launch_g<E, CONV_DATA, G_ALONG_K, G_SCALAR>(a, b, out, part, nz, grid, s, st);
+    else if (vb) launch_g<E, CONV_DATA, G_SCALAR, G_ALONG_ROW>(a, b, out, part, nz, grid, s, st);
+    else launch_g<E, CONV_DATA, G_SCALAR, G_SCALAR>(a, b, out, part, nz, grid, s, st);
   } else {
     const bool va = s.K % V == 0 && aligned16(a), vb = s.C % V == 0 && aligned16(b);
-    if (va && vb) launch_g<E, CONV_FILTER, G_ALONG_ROW, G_ALONG_ROW>(a, b, out, part, kspan, grid, s, st);
-    else if (va) launch_g<E, CONV_FILTER, G_ALONG_ROW, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
-    else if (vb) launch_g<E, CONV_FILTER, G_SCALAR, G_ALONG_ROW>(a, b, out, part, kspan, grid, s, st);
-    else launch_g<E, CONV_FILTER, G_SCALAR, G_SCALAR>(a, b, out, part, kspan, grid, s, st);
+    if (va && vb) launch_g<E, CONV_FILTER, G_ALONG_ROW, G_ALONG_ROW>(a, b, out, part, nz, grid, s, st);
+    else if (va) launch_g<E, CONV_FILTER, G_ALONG_ROW, G_SCALAR>(a, b, out, part, nz, grid, s, st);
+    else if (vb) launch_g<E, CONV_FILTER, G_SCALAR, G_ALONG_ROW>(a, b, out, part, nz, grid, s, st);
+    else launch_g<E, CONV_FILTER, G_SCALAR, G_SCALAR>(a, b, out, part, nz, grid, s, st);
   }
   if (part != nullptr) {
     const int total = s.M * s.NC;
