@@ -429,9 +429,10 @@ constexpr int fwd_key_tile(bool bf16, int D) {
 // Key split of the forward for causal or non-causal self-attention whose
 // longest query tile walks far more key tiles than a balanced share (few
 // long heads): with W the key tiles of all items, the share of one of 256
-// CUs is kc = ceil(W / 256) tiles; when the longest query tile has more than
-// 1.5 kc key tiles, every query tile with more than kc is cut into
-// ceil(n / kc) chunks of equal size (nch = the most chunks), each its own
+// CUs is ceil(W / 256) tiles; when the longest query tile has more than 1.5
+// shares, every query tile with more than kc = 3/4 of a share (at least 2)
+// key tiles is cut into ceil(n / kc) chunks of equal size (nch = the most
+// chunks), each its own
 // item with partial results, merged afterwards.  A function of the shape
 // alone, so that the workspace size and the launch agree; false (nch = 1):
 // no split.  The chunk items need the static schedule's table, which pins
@@ -451,8 +452,12 @@ inline bool fwd_key_split(bool bf16, long long BH, int S, int D, bool causal, in
     longest = std::max(longest, n);
   }
   W *= BH;
-  const long long share = (W + 255) / 256;
-  if (share < 2 || 2LL * longest <= 3 * share || share >= longest) return false;
+  const long long share0 = (W + 255) / 256;
+  if (share0 < 2 || 2LL * longest <= 3 * share0 || share0 >= longest) return false;
+  // chunks of three quarters of a share: more, shorter items than one share
+  // each (B1 H16 S1024 D128 causal, f32: forward 69.2 -> 65.2 us; half a
+  // share measured slower, 70.2)
+  const long long share = std::max<long long>(2, share0 * 3 / 4);
   kc = (int)share;
   nch = (longest + kc - 1) / kc;
   return nch > 1;
