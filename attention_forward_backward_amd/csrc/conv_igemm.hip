@@ -230,6 +230,15 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
   constexpr int PER = CT * KC / 256;                // values of one operand per thread per chunk
   constexpr int NV = CT * KC / V / 256;             // vector groups per thread per chunk
   constexpr int LDK = KC + (is_bf16<E>() ? 8 : 1);  // padded LDS row (bf16: 16-byte reads)
+  // bf16 operands gathered along the output index are held transposed: KC
+  // reduction rows of CT output values in the swizzled tile layout of the
+  // attention kernels (one 16-byte store per gathered group instead of eight
+  // 2-byte ones), read back with transposed LDS reads
+  constexpr bool TA = is_bf16<E>() && GA == G_ALONG_ROW;
+  constexpr bool TB = is_bf16<E>() && GB == G_ALONG_ROW;
+  using TT = Tile<E, CT>;
+  static_assert(!is_bf16<E>() || KC % 32 == 0, "bf16 chunks of whole MFMA pairs");
+  static_assert(KC * TT::ROWB <= CT * LDK * (int)sizeof(T), "transposed tile fits the buffer");
   __shared__ __attribute__((aligned(16))) T As[CT * LDK];
   __shared__ __attribute__((aligned(16))) T Bs[CT * LDK];
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, h = lane >> 5;
@@ -322,6 +331,10 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
         vslot(g, mode, row, kk);
         if constexpr (mode == G_ALONG_K && is_bf16<E>()) {
           *reinterpret_cast<u32x4*>(dst + row * LDK + kk) = vv[g];  // 16-byte aligned row part
+        } else if constexpr (mode == G_ALONG_ROW && is_bf16<E>()) {
+          // the group is one 16-byte chunk of reduction row kk of the
+          // transposed tile
+          *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(dst) + TT::off(kk, row)) = vv[g];
         } else {
           const T* e = reinterpret_cast<const T*>(&vv[g]);
 #pragma unroll
@@ -347,11 +360,28 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
     const T* ar = As + (wm * 32 + n) * LDK;
     const T* br = Bs + (wn * 32 + n) * LDK;
     if constexpr (is_bf16<E>()) {
+      // per 32 reduction values, two MFMAs; an operand held transposed is
+      // read in the same k-slot form (8 consecutive reduction values of the
+      // lane's row) with transposed LDS reads
 #pragma unroll
-      for (int t = 0; t < KC / 16; ++t) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ar + 16 * t + 8 * h);
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(br + 16 * t + 8 * h);
-        acc = E::mma(a, b, acc);
+      for (int t = 0; t < KC / 32; ++t) {
+        RegOperand<E> xa, xb;
+        if constexpr (TA) {
+          read_kslot_operand<E, CT>(xa, reinterpret_cast<const char*>(As), 32 * t, wm * 32, lane);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            xa.v[u] = *reinterpret_cast<const bf16x8*>(ar + 32 * t + 16 * u + 8 * h);
+        }
+        if constexpr (TB) {
+          read_kslot_operand<E, CT>(xb, reinterpret_cast<const char*>(Bs), 32 * t, wn * 32, lane);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+            xb.v[u] = *reinterpret_cast<const bf16x8*>(br + 32 * t + 16 * u + 8 * h);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) acc = E::mma(xa.v[u], xb.v[u], acc);
       }
     } else {
 #pragma unroll
