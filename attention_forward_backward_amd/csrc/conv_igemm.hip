@@ -274,6 +274,46 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
   constexpr int NS = ATTN_CONV_PREFETCH;
   float sa_[NS][GA == G_SCALAR ? PER : 1], sb_[NS][GB == G_SCALAR ? PER : 1];
   u32x4 va_[NS][GA == G_SCALAR ? 1 : NV], vb_[NS][GB == G_SCALAR ? 1 : NV];
+  // The part of a vector group's x address that its output index fixes,
+  // computed once: the forward's A (output pixel n, p, q: image row base and
+  // the window's top-left input coordinate; a pixel past M gets a row that no
+  // tap brings inside the image) and the filter derivative's B (tap r, s and
+  // channel c).  Per chunk only the reduction index is decomposed.
+  constexpr bool XA = MODE == CONV_FWD && GA == G_ALONG_K;
+  constexpr bool XB = MODE == CONV_FILTER && GB == G_ALONG_ROW;
+  constexpr bool XD = MODE == CONV_DATA && GA == G_ALONG_K;  // dy, likewise
+  constexpr bool XANY = XA || XB || XD;
+  int xh[XANY ? NV : 1], xw[XANY ? NV : 1], xc[XANY ? NV : 1];
+  if constexpr (XANY) {
+#pragma unroll
+    for (int g = 0; g < NV; ++g) {
+      int row, kk;
+      vslot(g, XB ? GB : GA, row, kk);
+      if constexpr (XD) {
+        // input pixel n, h, w: dy image base and the padded coordinates
+        const int m = m0 + row;
+        int w, h;
+        const int n = s.dH.divmod(s.dW.divmod(min(m, s.M - 1), w), h);
+        xc[g] = n * s.P;
+        xh[g] = m < s.M ? h + s.ph : -(1 << 28);
+        xw[g] = w + s.pw;
+      } else if constexpr (XA) {
+        const int m = m0 + row;
+        int q, p;
+        const int n = s.dP.divmod(s.dQ.divmod(min(m, s.M - 1), q), p);
+        xc[g] = n * s.H;                                   // image n's first row
+        xh[g] = m < s.M ? p * s.sh - s.ph : -(1 << 28);    // top input row of the window
+        xw[g] = q * s.sw - s.pw;
+      } else {
+        const int j = j0 + row;
+        int c, ss;
+        const int r = s.dS.divmod(s.dC.divmod(min(j, s.NC - 1), c), ss);
+        xh[g] = j < s.NC ? r - s.ph : -(1 << 28);          // tap offsets, padding folded in
+        xw[g] = ss - s.pw;
+        xc[g] = c;
+      }
+    }
+  }
   // (k1 and every group boundary are multiples of V on the vector paths, so
   // a group is either wholly inside the chunk range or wholly outside)
   auto gather = [&](int kc, auto setc) __attribute__((always_inline)) {
@@ -294,7 +334,31 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
       for (int g = 0; g < NV; ++g) {
         int row, kk;
         vslot(g, GA, row, kk);
-        va[g] = kc + kk < k1 ? vec_val<T, MODE, 0>(A, s, m0 + row, kc + kk) : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (XD) {
+          // dy channels k .. k+V-1 of the output pixel that tap (r, ss) of
+          // the group's input pixel comes from (none between strides)
+          const int kx = kc + kk;
+          int k, ss;
+          const int r = s.dS.divmod(s.dK.divmod(kx, k), ss);
+          const int ph = xh[g] - r, pw = xw[g] - ss;
+          int rh, rw;
+          const int p = s.dsh.divmod(max(ph, 0), rh), q = s.dsw.divmod(max(pw, 0), rw);
+          const bool in = kx < k1 && ph >= 0 && pw >= 0 && rh == 0 && rw == 0 && p < s.P &&
+                          q < s.Q;
+          va[g] = in ? *reinterpret_cast<const u32x4*>(A + ((size_t)(xc[g] + p) * s.Q + q) * s.K + k)
+                     : u32x4{0u, 0u, 0u, 0u};
+        } else if constexpr (XA) {
+          // x channels c .. c+V-1 of tap (r, ss) of the group's output pixel
+          const int k = kc + kk;
+          int c, ss;
+          const int r = s.dS.divmod(s.dC.divmod(k, c), ss);
+          const int ih = xh[g] + r, iw = xw[g] + ss;
+          const bool in = k < k1 && (unsigned)ih < (unsigned)s.H && (unsigned)iw < (unsigned)s.W;
+          va[g] = in ? *reinterpret_cast<const u32x4*>(A + ((size_t)(xc[g] + ih) * s.W + iw) * s.C + c)
+                     : u32x4{0u, 0u, 0u, 0u};
+        } else {
+          va[g] = kc + kk < k1 ? vec_val<T, MODE, 0>(A, s, m0 + row, kc + kk) : u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
     if constexpr (GB == G_SCALAR) {
@@ -309,7 +373,18 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
       for (int g = 0; g < NV; ++g) {
         int row, kk;
         vslot(g, GB, row, kk);
-        vb[g] = kc + kk < k1 ? vec_val<T, MODE, 1>(B, s, j0 + row, kc + kk) : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (XB) {
+          // x channels c .. c+V-1 of the group's tap at output pixel kc + kk
+          const int k = kc + kk;
+          int q, p;
+          const int n = s.dP.divmod(s.dQ.divmod(k, q), p);
+          const int ih = p * s.sh + xh[g], iw = q * s.sw + xw[g];
+          const bool in = k < k1 && (unsigned)ih < (unsigned)s.H && (unsigned)iw < (unsigned)s.W;
+          vb[g] = in ? *reinterpret_cast<const u32x4*>(B + (((size_t)n * s.H + ih) * s.W + iw) * s.C + xc[g])
+                     : u32x4{0u, 0u, 0u, 0u};
+        } else {
+          vb[g] = kc + kk < k1 ? vec_val<T, MODE, 1>(B, s, j0 + row, kc + kk) : u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
   };
