@@ -314,6 +314,39 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
       }
     }
   }
+  // The same for x gathered element by element (the 3-channel stem): in the
+  // forward a thread's PER elements share one reduction index (tid % KC) and
+  // have PER output pixels, decomposed once here, so a chunk decomposes its
+  // reduction index once; in the filter derivative they share one tap and
+  // channel (tid % CT).
+  constexpr bool SA = MODE == CONV_FWD && GA == G_SCALAR;
+  constexpr bool SB = MODE == CONV_FILTER && GB == G_SCALAR;
+  static_assert(256 % KC == 0 && 256 % CT == 0, "element slots keep their index across i");
+  int sxh[SA ? PER : 1], sxw[SA ? PER : 1], sxc[SA ? PER : 1];
+  int fr = 0, fs = 0, fc = 0;
+  if constexpr (SA) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int row, kk;
+      slot(i, row, kk);
+      const int m = m0 + row;
+      int q, p;
+      const int n = s.dP.divmod(s.dQ.divmod(min(m, s.M - 1), q), p);
+      sxc[i] = n * s.H;
+      sxh[i] = m < s.M ? p * s.sh - s.ph : -(1 << 28);
+      sxw[i] = q * s.sw - s.pw;
+    }
+  }
+  if constexpr (SB) {
+    int row, kk;
+    slot(0, row, kk);
+    const int j = j0 + row;
+    int c, ss;
+    const int r = s.dS.divmod(s.dC.divmod(min(j, s.NC - 1), c), ss);
+    fr = j < s.NC ? r - s.ph : -(1 << 28);
+    fs = ss - s.pw;
+    fc = c;
+  }
   // (k1 and every group boundary are multiples of V on the vector paths, so
   // a group is either wholly inside the chunk range or wholly outside)
   auto gather = [&](int kc, auto setc) __attribute__((always_inline)) {
@@ -322,7 +355,19 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
     float* sb = sb_[st];
     u32x4* va = va_[st];
     u32x4* vb = vb_[st];
-    if constexpr (GA == G_SCALAR) {
+    if constexpr (SA) {
+      int row0, kk0;
+      slot(0, row0, kk0);  // (every i has this reduction index)
+      const int k = kc + kk0;
+      int c, ss;
+      const int r = s.dS.divmod(s.dC.divmod(min(k, s.KD - 1), c), ss);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int ih = sxh[i] + r, iw = sxw[i] + ss;
+        const bool in = k < k1 && (unsigned)ih < (unsigned)s.H && (unsigned)iw < (unsigned)s.W;
+        sa[i] = in ? (float)A[((size_t)(sxc[i] + ih) * s.W + iw) * s.C + c] : 0.f;
+      }
+    } else if constexpr (GA == G_SCALAR) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         int row, kk;
@@ -361,7 +406,19 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
         }
       }
     }
-    if constexpr (GB == G_SCALAR) {
+    if constexpr (SB) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        int row, kk;
+        slot(i, row, kk);
+        const int k = kc + kk;
+        int q, p;
+        const int n = s.dP.divmod(s.dQ.divmod(min(k, s.KD - 1), q), p);
+        const int ih = p * s.sh + fr, iw = q * s.sw + fs;
+        const bool in = k < k1 && (unsigned)ih < (unsigned)s.H && (unsigned)iw < (unsigned)s.W;
+        sb[i] = in ? (float)B[(((size_t)n * s.H + ih) * s.W + iw) * s.C + fc] : 0.f;
+      }
+    } else if constexpr (GB == G_SCALAR) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         int row, kk;
