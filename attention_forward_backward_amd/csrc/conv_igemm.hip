@@ -547,26 +547,33 @@ __global__ __launch_bounds__(256) void conv_igemm_kernel(const typename E::T* __
   }
 }
 
-// out[i] = sum over the z slices of part[z][i] in a fixed order: eight
-// running sums over the slices z = u (mod 8), added pairwise at the end, so
-// that eight independent loads are in flight per thread (deterministic).
+// out[i] = sum over the z slices of part[z][i] in a fixed order: a
+// workgroup takes 64 outputs, its wave g sums the slices z = g (mod 4) of
+// each in eight running sums (z = g + 4u mod 32), added pairwise, and the
+// four wave sums are added pairwise through LDS (deterministic; four waves
+// per output keep more loads in flight than one thread per output did).
 template <class T>
 __global__ __launch_bounds__(256) void conv_split_reduce_kernel(const float* __restrict__ part,
                                                                 T* __restrict__ out, int total,
                                                                 int nz) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const float* p = part + i;
+  __shared__ float red[4][64];
+  const int g = threadIdx.x >> 6, o = threadIdx.x & 63;
+  const int i = blockIdx.x * 64 + o;
   float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  int z = 0;
-  for (; z + 8 <= nz; z += 8) {
+  if (i < total) {
+    const float* p = part + i;
+    int z = g;
+    for (; z + 28 < nz; z += 32) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a[u] += p[(size_t)(z + u) * total];
+      for (int u = 0; u < 8; ++u) a[u] += p[(size_t)(z + 4 * u) * total];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (z + 4 * u < nz) a[u] += p[(size_t)(z + 4 * u) * total];
   }
-#pragma unroll
-  for (int u = 0; u < 7; ++u)
-    if (z + u < nz) a[u] += p[(size_t)(z + u) * total];
-  out[i] = (T)(((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])));
+  red[g][o] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  __syncthreads();
+  if (g == 0 && i < total) out[i] = (T)((red[0][o] + red[1][o]) + (red[2][o] + red[3][o]));
 }
 
 }  // namespace attn
@@ -656,7 +663,7 @@ hipError_t launch(const void* a, const void* b, void* out, float* part, int nz, 
   }
   if (part != nullptr) {
     const int total = s.M * s.NC;
-    hipLaunchKernelGGL((attn::conv_split_reduce_kernel<T>), dim3((total + 255) / 256), dim3(256),
+    hipLaunchKernelGGL((attn::conv_split_reduce_kernel<T>), dim3((total + 63) / 64), dim3(256),
                        0, st, (const float*)part, (T*)out, total, nz);
   }
   return hipGetLastError();
